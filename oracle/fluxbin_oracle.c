@@ -1,0 +1,431 @@
+/*
+ * fluxbin_oracle.c -- plain, slow, fp64 CPU oracle for the FluxBin LUT GEMV.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  The GPU library never
+ * links, includes or calls it, and this file includes nothing from the GPU
+ * library: every format below is re-derived here from its written definition.
+ *
+ * What is computed (FluxBin, paperlayer.ai summary, section 3 "Methodology",
+ * bullets "Quantization", "Salient-Aware Hybrid Bases", "Virtual Columnar
+ * Mapping"; same page, appendix C.1 "Compute Complexity Analysis"):
+ *
+ *   W_hat = sum_{k<Kb} diag(r_k) B_k diag(c_k)
+ *         + sum_{s<Ks} diag(r_s) B_s diag(c_s) P_S          (P_S x = x[S])
+ *   y[b]  = W_hat x[b]
+ *
+ * B are +-1 matrices stored as packed sign bits.  The salient bases act on
+ * the salient columns only and are added on top of the global bases: a
+ * second correction of the same columns, not a replacement of them.  The LUT form of the same
+ * product (sub-vectors of g inputs, a table of all 2^g signed sums of the
+ * scale-fused inputs, indexed by the weight bit pattern) reaches the same y
+ * up to rounding order; orc_gemv_lut() evaluates it step by step in fp64 so
+ * that the two routes can be compared.
+ *
+ * Readings taken where the pages are silent (each is documented in the
+ * design notes of the repository):
+ *   - bit value 1 means +1 and 0 means -1 (LUT Tensor Core page, section
+ *     3.1.2: binary digits reinterpreted as {-1,+1});
+ *   - bits are packed along the input dimension, least significant bit first:
+ *     word w of a row holds column 32w+t at bit t; padding bits are 0;
+ *   - the row scale is one fp16 value per output row per basis;
+ *   - the salient column scale c_s is stored in compact (VCM) order;
+ *   - fp16 inputs, fp64 arithmetic, results returned in fp64.
+ *
+ * Parity status: the dense product is pinned by closed forms (popcount
+ * identity, one-hot column selection, the LUT Tensor Core page's 1x4 times
+ * 4xN worked shape with dyadic inputs), exact integer brute force on tiny
+ * problems, and agreement with the separately written LUT route.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORC_EXPORT __attribute__((visibility("default")))
+
+/* ---------------------------------------------------------------------- */
+/* IEEE 754 binary16 <-> binary64, written from the format definition.     */
+/* ---------------------------------------------------------------------- */
+
+ORC_EXPORT double orc_half_to_double(uint16_t h) {
+  int sign = (h >> 15) & 1;
+  int e = (h >> 10) & 0x1f;
+  int m = h & 0x3ff;
+  double v;
+  if (e == 0) {
+    v = ldexp((double)m, -24); /* zero or subnormal: m * 2^-24 */
+  } else if (e == 31) {
+    v = m ? NAN : INFINITY;
+  } else {
+    v = ldexp((double)(1024 + m), e - 25); /* (1 + m/1024) * 2^(e-15) */
+  }
+  return sign ? -v : v;
+}
+
+/* Round to nearest, ties to even (the default rounding mode of rint()). */
+ORC_EXPORT uint16_t orc_double_to_half(double v) {
+  uint16_t sign = signbit(v) ? 0x8000 : 0;
+  double a = fabs(v);
+  if (isnan(v)) return 0x7e00;
+  if (a >= 65520.0) return sign | 0x7c00; /* halfway above 65504 rounds to inf */
+  if (a < ldexp(1.0, -14)) {
+    /* subnormal range: quantum 2^-24; rounding may reach 1024 = min normal */
+    double q = rint(ldexp(a, 24));
+    return sign | (uint16_t)q;
+  }
+  int E;
+  frexp(a, &E);                   /* a in [2^(E-1), 2^E) */
+  int e = E - 1;                  /* unbiased exponent */
+  double q = rint(ldexp(a, 10 - e)); /* significand in units of 2^(e-10) */
+  if (q == 2048.0) {
+    q = 1024.0;
+    e += 1;
+  }
+  return sign | (uint16_t)(((e + 15) << 10) | ((int)q - 1024));
+}
+
+ORC_EXPORT void orc_half_array_to_double(const uint16_t *h, int64_t count, double *out) {
+  for (int64_t i = 0; i < count; ++i) out[i] = orc_half_to_double(h[i]);
+}
+
+ORC_EXPORT void orc_double_array_to_half(const double *v, int64_t count, uint16_t *out) {
+  for (int64_t i = 0; i < count; ++i) out[i] = orc_double_to_half(v[i]);
+}
+
+/* ---------------------------------------------------------------------- */
+/* Sign bits                                                                */
+/* ---------------------------------------------------------------------- */
+
+static inline int64_t words_per_row(int64_t cols) { return (cols + 31) / 32; }
+
+/* Sign of column `col` of a canonical row: +1 when the bit is set, else -1. */
+static inline double sign_at(const uint32_t *row_words, int64_t col) {
+  uint32_t w = row_words[col >> 5];
+  return ((w >> (col & 31)) & 1u) ? 1.0 : -1.0;
+}
+
+/* Pack int8 signs [rows][ld] (first `cols` used) into canonical words
+ * [rows][ceil(cols/32)].  +1 sets the bit, -1 clears it; any other value is
+ * counted as invalid and stored as a cleared bit.  Returns the invalid count. */
+ORC_EXPORT int64_t orc_pack_rowmajor(const int8_t *signs, int64_t rows, int64_t cols, int64_t ld,
+                                     uint32_t *out) {
+  int64_t wpr = words_per_row(cols);
+  int64_t bad = 0;
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int64_t w = 0; w < wpr; ++w) {
+      uint32_t word = 0;
+      for (int t = 0; t < 32; ++t) {
+        int64_t col = 32 * w + t;
+        if (col >= cols) break;
+        int8_t s = signs[r * ld + col];
+        if (s == 1) {
+          word |= (1u << t);
+        } else if (s != -1) {
+          ++bad;
+        }
+      }
+      out[r * wpr + w] = word;
+    }
+  }
+  return bad;
+}
+
+/* Inverse of orc_pack_rowmajor for valid words: +1 / -1 as int8. */
+ORC_EXPORT void orc_unpack_rowmajor(const uint32_t *words, int64_t rows, int64_t cols, int8_t *signs) {
+  int64_t wpr = words_per_row(cols);
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t col = 0; col < cols; ++col)
+      signs[r * cols + col] = (int8_t)sign_at(words + r * wpr, col);
+}
+
+/* Tiled device layout.  Rows are padded to a multiple of 64 and columns to a
+ * multiple of 128 (4 words).  The word holding canonical (row r, word w) is
+ * stored at index ((floor(r/64) * NC + floor(w/4)) * 64 + r mod 64) * 4 + w mod 4,
+ * NC = ceil(cols/128).  Padding words are zero.  The bits inside a word are
+ * not permuted. */
+ORC_EXPORT int64_t orc_tiled_words(int64_t rows, int64_t cols) {
+  int64_t rt = (rows + 63) / 64;
+  int64_t nc = (cols + 127) / 128;
+  return rt * nc * 64 * 4;
+}
+
+ORC_EXPORT void orc_tile_words(const uint32_t *canon, int64_t rows, int64_t cols, uint32_t *tiled) {
+  int64_t wpr = words_per_row(cols);
+  int64_t nc = (cols + 127) / 128;
+  memset(tiled, 0, (size_t)orc_tiled_words(rows, cols) * sizeof(uint32_t));
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int64_t w = 0; w < wpr; ++w) {
+      int64_t dst = (((r / 64) * nc + w / 4) * 64 + (r % 64)) * 4 + (w % 4);
+      tiled[dst] = canon[r * wpr + w];
+    }
+  }
+}
+
+/* VCM on sign bits: compact column c of the destination is source column
+ * idx[c].  src canonical [rows][ceil(k/32)], dst canonical [rows][ceil(s/32)]. */
+ORC_EXPORT void orc_vcm_gather_bits(const uint32_t *src, int64_t rows, int64_t k, const int32_t *idx,
+                                    int64_t s, uint32_t *dst) {
+  int64_t wk = words_per_row(k), ws = words_per_row(s);
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int64_t w = 0; w < ws; ++w) dst[r * ws + w] = 0;
+    for (int64_t c = 0; c < s; ++c) {
+      if (sign_at(src + r * wk, idx[c]) > 0) dst[r * ws + c / 32] |= (1u << (c % 32));
+    }
+  }
+}
+
+/* ---------------------------------------------------------------------- */
+/* Dense reconstruction and product                                         */
+/* ---------------------------------------------------------------------- */
+
+typedef struct {
+  int64_t n, k, s;
+  int32_t kb, ks;
+  const uint32_t *bits_g; /* [kb][n][ceil(k/32)] */
+  const uint16_t *r_g;    /* [kb][n] */
+  const uint16_t *c_g;    /* [kb][k] */
+  const uint32_t *bits_s; /* [ks][n][ceil(s/32)] */
+  const uint16_t *r_s;    /* [ks][n] */
+  const uint16_t *c_s;    /* [ks][s], compact order */
+  const int32_t *idx;     /* [s], salient column of compact column c */
+} orc_layer;
+
+static double *halves(const uint16_t *h, int64_t count) {
+  double *d = (double *)malloc((size_t)(count > 0 ? count : 1) * sizeof(double));
+  orc_half_array_to_double(h, count, d);
+  return d;
+}
+
+/* Row i of W_hat in fp64, written out from its definition. */
+static void reconstruct_row(const orc_layer *L, const double *cg, const double *cs, int64_t i,
+                            double *wrow) {
+  int64_t wk = words_per_row(L->k), ws = words_per_row(L->s);
+  for (int64_t j = 0; j < L->k; ++j) wrow[j] = 0.0;
+  for (int32_t b = 0; b < L->kb; ++b) {
+    const uint32_t *row = L->bits_g + ((int64_t)b * L->n + i) * wk;
+    double r = orc_half_to_double(L->r_g[(int64_t)b * L->n + i]);
+    for (int64_t j = 0; j < L->k; ++j) wrow[j] += r * sign_at(row, j) * cg[(int64_t)b * L->k + j];
+  }
+  for (int32_t b = 0; b < L->ks; ++b) {
+    const uint32_t *row = L->bits_s + ((int64_t)b * L->n + i) * ws;
+    double r = orc_half_to_double(L->r_s[(int64_t)b * L->n + i]);
+    for (int64_t c = 0; c < L->s; ++c)
+      wrow[L->idx[c]] += r * sign_at(row, c) * cs[(int64_t)b * L->s + c];
+  }
+}
+
+/* y[b][t] = sum_j W_hat[rows[t]][j] * x[b][j] and mag[b][t] = sum_j |W_hat x|
+ * for each listed row t (all n rows when rows == NULL; then nrows must be n).
+ * y and mag are [batch][nrows].  nthreads <= 0 uses the OpenMP default. */
+ORC_EXPORT int orc_gemv_dense(int64_t n, int64_t k, int64_t s, int32_t kb, int32_t ks,
+                              const uint32_t *bits_g, const uint16_t *r_g, const uint16_t *c_g,
+                              const uint32_t *bits_s, const uint16_t *r_s, const uint16_t *c_s,
+                              const int32_t *idx, const uint16_t *x, int64_t batch,
+                              const int64_t *rows, int64_t nrows, double *y, double *mag,
+                              int32_t nthreads) {
+  orc_layer L = {n, k, s, kb, ks, bits_g, r_g, c_g, bits_s, r_s, c_s, idx};
+  double *cg = halves(c_g, (int64_t)kb * k);
+  double *cs = halves(c_s, (int64_t)ks * s);
+  double *xd = halves(x, batch * k);
+  int err = 0;
+#ifdef _OPENMP
+  int nt = nthreads > 0 ? nthreads : omp_get_max_threads();
+#pragma omp parallel num_threads(nt)
+#endif
+  {
+    double *wrow = (double *)malloc((size_t)(k > 0 ? k : 1) * sizeof(double));
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 16)
+#endif
+    for (int64_t t = 0; t < nrows; ++t) {
+      int64_t i = rows ? rows[t] : t;
+      if (i < 0 || i >= n) {
+        err = 1;
+        continue;
+      }
+      reconstruct_row(&L, cg, cs, i, wrow);
+      for (int64_t b = 0; b < batch; ++b) {
+        double acc = 0.0, am = 0.0;
+        const double *xb = xd + b * k;
+        for (int64_t j = 0; j < k; ++j) {
+          double p = wrow[j] * xb[j];
+          acc += p;
+          am += fabs(p);
+        }
+        y[b * nrows + t] = acc;
+        if (mag) mag[b * nrows + t] = am;
+      }
+    }
+    free(wrow);
+  }
+  free(cg);
+  free(cs);
+  free(xd);
+  return err;
+}
+
+/* ---------------------------------------------------------------------- */
+/* LUT route, step by step (scale-fused table, pattern lookup, row scale)   */
+/* ---------------------------------------------------------------------- */
+
+/* Full table of one sub-vector: LUT[p] = sum_t (2*bit_t(p) - 1) * v_t for all
+ * p < 2^g, each entry enumerated directly (LUT Tensor Core page, section 2.2
+ * Figure 3: one entry per sign pattern of a g-element activation group). */
+ORC_EXPORT void orc_lut_explicit(int32_t g, const double *v, double *lut) {
+  for (int64_t p = 0; p < ((int64_t)1 << g); ++p) {
+    double acc = 0.0;
+    for (int32_t t = 0; t < g; ++t) acc += (((p >> t) & 1) ? 1.0 : -1.0) * v[t];
+    lut[p] = acc;
+  }
+}
+
+/* Scale-fused inputs of sub-vector j of one segment: v_t = c[jg+t] * x[jg+t]
+ * (global) or c[jg+t] * x[idx[jg+t]] (salient, VCM gather); zero past L. */
+static void fused_inputs(int32_t g, int64_t j, int64_t len, const double *c, const double *xb,
+                         const int32_t *gather, double *v) {
+  for (int32_t t = 0; t < g; ++t) {
+    int64_t col = j * g + t;
+    if (col >= len) {
+      v[t] = 0.0;
+    } else {
+      double xv = gather ? xb[gather[col]] : xb[col];
+      v[t] = c[col] * xv;
+    }
+  }
+}
+
+/* Sign pattern of sub-vector j of a canonical row (g divides 32). */
+static inline uint32_t pattern_at(const uint32_t *row_words, int32_t g, int64_t j) {
+  int64_t bit = j * g;
+  return (row_words[bit >> 5] >> (bit & 31)) & ((1u << g) - 1u);
+}
+
+/* y via the LUT route in fp64: per segment and batch row, build every
+ * sub-vector's 2^g table from the scale-fused inputs, look each row's bit
+ * pattern up, accumulate, then apply the row scale after accumulation.
+ * y is [batch][nrows] like orc_gemv_dense. */
+ORC_EXPORT int orc_gemv_lut(int64_t n, int64_t k, int64_t s, int32_t kb, int32_t ks, int32_t g,
+                            const uint32_t *bits_g, const uint16_t *r_g, const uint16_t *c_g,
+                            const uint32_t *bits_s, const uint16_t *r_s, const uint16_t *c_s,
+                            const int32_t *idx, const uint16_t *x, int64_t batch,
+                            const int64_t *rows, int64_t nrows, double *y) {
+  if (g <= 0 || g > 16 || 32 % g) return 1;
+  double *cg = halves(c_g, (int64_t)kb * k);
+  double *cs = halves(c_s, (int64_t)ks * s);
+  double *xd = halves(x, batch * k);
+  int64_t tsize = (int64_t)1 << g;
+  double v[16];
+  for (int64_t i = 0; i < batch * nrows; ++i) y[i] = 0.0;
+  for (int32_t seg = 0; seg < kb + ks; ++seg) {
+    int salient = seg >= kb;
+    int32_t sb = salient ? seg - kb : seg;
+    int64_t len = salient ? s : k;
+    int64_t nsub = (len + g - 1) / g;
+    int64_t wpr = words_per_row(len);
+    const double *c = salient ? cs + (int64_t)sb * s : cg + (int64_t)sb * k;
+    const uint32_t *bits = salient ? bits_s + (int64_t)sb * n * wpr : bits_g + (int64_t)sb * n * wpr;
+    const uint16_t *r = salient ? r_s + (int64_t)sb * n : r_g + (int64_t)sb * n;
+    double *tables = (double *)malloc((size_t)(nsub > 0 ? nsub : 1) * tsize * sizeof(double));
+    double *acc = (double *)calloc((size_t)(nrows > 0 ? nrows : 1), sizeof(double));
+    for (int64_t b = 0; b < batch; ++b) {
+      const double *xb = xd + b * k;
+      for (int64_t j = 0; j < nsub; ++j) {
+        fused_inputs(g, j, len, c, xb, salient ? idx : NULL, v);
+        orc_lut_explicit(g, v, tables + j * tsize);
+      }
+      for (int64_t t = 0; t < nrows; ++t) {
+        int64_t i = rows ? rows[t] : t;
+        const uint32_t *row = bits + i * wpr;
+        double a = 0.0;
+        for (int64_t j = 0; j < nsub; ++j) a += tables[j * tsize + pattern_at(row, g, j)];
+        acc[t] = a;
+      }
+      for (int64_t t = 0; t < nrows; ++t) {
+        int64_t i = rows ? rows[t] : t;
+        y[b * nrows + t] += orc_half_to_double(r[i]) * acc[t];
+      }
+    }
+    free(tables);
+    free(acc);
+  }
+  free(cg);
+  free(cs);
+  free(xd);
+  return 0;
+}
+
+/* Half tables as exported by the GPU library's table builder:
+ * out[b][seg][j][q] = LUT[q | 2^(g-1)] of sub-vector j (the half whose top
+ * input carries sign +1; the other half follows from LUT[~p] = -LUT[p],
+ * LUT Tensor Core page, section 3.1.2).  Segments are the kb global bases
+ * then the ks salient bases; sub-vector counts are ceil(len/g).
+ * absv[b][seg][j] = sum_t |v_t| (scale of the rounding bound). */
+ORC_EXPORT int orc_half_luts(int64_t k, int64_t s, int32_t kb, int32_t ks, int32_t g,
+                             const uint16_t *c_g, const uint16_t *c_s, const int32_t *idx,
+                             const uint16_t *x, int64_t batch, double *out, double *absv) {
+  if (g <= 0 || g > 16 || 32 % g) return 1;
+  double *cg = halves(c_g, (int64_t)kb * k);
+  double *cs = halves(c_s, (int64_t)ks * s);
+  double *xd = halves(x, batch * k);
+  int64_t tsize = (int64_t)1 << g, half = tsize / 2;
+  double v[16];
+  double *full = (double *)malloc((size_t)tsize * sizeof(double));
+  int64_t o = 0, oa = 0;
+  for (int64_t b = 0; b < batch; ++b) {
+    for (int32_t seg = 0; seg < kb + ks; ++seg) {
+      int salient = seg >= kb;
+      int32_t sb = salient ? seg - kb : seg;
+      int64_t len = salient ? s : k;
+      int64_t nsub = (len + g - 1) / g;
+      const double *c = salient ? cs + (int64_t)sb * s : cg + (int64_t)sb * k;
+      for (int64_t j = 0; j < nsub; ++j) {
+        fused_inputs(g, j, len, c, xd + b * k, salient ? idx : NULL, v);
+        orc_lut_explicit(g, v, full);
+        for (int64_t q = 0; q < half; ++q) out[o++] = full[q | half];
+        double a = 0.0;
+        for (int32_t t = 0; t < g; ++t) a += fabs(v[t]);
+        absv[oa++] = a;
+      }
+    }
+  }
+  free(full);
+  free(cg);
+  free(cs);
+  free(xd);
+  return 0;
+}
+
+/* Dense fp16 matrix-vector product in fp64 (context kernel's reference):
+ * y[b][i] = sum_j w[i][j] * x[b][j], w fp16 [n][k] row-major, x fp16 [batch][k]. */
+ORC_EXPORT void orc_dense_f16_gemv(const uint16_t *w, int64_t n, int64_t k, const uint16_t *x,
+                                   int64_t batch, double *y, double *mag) {
+  double *xd = halves(x, batch * k);
+#ifdef _OPENMP
+#pragma omp parallel for schedule(static)
+#endif
+  for (int64_t i = 0; i < n; ++i) {
+    for (int64_t b = 0; b < batch; ++b) {
+      double acc = 0.0, am = 0.0;
+      for (int64_t j = 0; j < k; ++j) {
+        double p = orc_half_to_double(w[i * k + j]) * xd[b * k + j];
+        acc += p;
+        am += fabs(p);
+      }
+      y[b * n + i] = acc;
+      if (mag) mag[b * n + i] = am;
+    }
+  }
+  free(xd);
+}
+
+ORC_EXPORT int orc_max_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}

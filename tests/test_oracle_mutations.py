@@ -1,0 +1,112 @@
+"""Plant plausible mistakes in copies of the oracle and check that the pins catch each one.
+
+Each mutant is the oracle source with one textual change (a flipped sign
+convention, a reversed bit order, a dropped term, a wrong index, a transposed
+operand), compiled with gcc into a temporary directory.  The checks below are
+the same closed forms, brute force and special cases as the pin tests, written
+as predicates so that a mutant's failure can be observed instead of raised.
+"""
+import importlib.util
+import os
+import subprocess
+
+import numpy as np
+import pytest
+
+from binary_basis_lut_amd import inputs as I
+
+from .test_oracle_pins import bits_of, exact_y, f16, layer_from
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "fluxbin_oracle.c")
+PY = os.path.join(ROOT, "oracle", "oracle.py")
+
+MUTANTS = {
+    "sign_convention_flipped": ("return ((w >> (col & 31)) & 1u) ? 1.0 : -1.0;",
+                                "return ((w >> (col & 31)) & 1u) ? -1.0 : 1.0;"),
+    "msb_first_bit_order": ("return ((w >> (col & 31)) & 1u) ? 1.0 : -1.0;",
+                            "return ((w >> (31 - (col & 31))) & 1u) ? 1.0 : -1.0;"),
+    "salient_term_dropped": ("wrow[L->idx[c]] += r * sign_at(row, c) * cs[(int64_t)b * L->s + c];",
+                             "(void)row; (void)r;"),
+    "salient_ungathered_column": ("wrow[L->idx[c]] += r * sign_at(row, c) * cs[(int64_t)b * L->s + c];",
+                                  "wrow[c] += r * sign_at(row, c) * cs[(int64_t)b * L->s + c];"),
+    "salient_scale_indexed_by_column": ("wrow[L->idx[c]] += r * sign_at(row, c) * cs[(int64_t)b * L->s + c];",
+                                        "wrow[L->idx[c]] += r * sign_at(row, c) * cs[(int64_t)b * L->s + L->idx[c] % L->s];"),
+    "last_basis_dropped": ("for (int32_t b = 0; b < L->kb; ++b) {", "for (int32_t b = 0; b + 1 < L->kb; ++b) {"),
+    "row_scale_transposed": ("double r = orc_half_to_double(L->r_g[(int64_t)b * L->n + i]);",
+                             "double r = orc_half_to_double(L->r_g[(int64_t)b * L->n + (i * 7 + 1) % L->n]);"),
+    "column_scale_wrong_basis": ("wrow[j] += r * sign_at(row, j) * cg[(int64_t)b * L->k + j];",
+                                 "wrow[j] += r * sign_at(row, j) * cg[j];"),
+    "product_not_accumulated": ("acc += p;\n          am += fabs(p);", "acc = p;\n          am += fabs(p);"),
+    "half_rounding_truncates": ("double q = rint(ldexp(a, 10 - e));", "double q = floor(ldexp(a, 10 - e));"),
+}
+
+
+def build_mutant(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation site for {name} not found exactly once"
+    mpath = tmp_path / f"{name}.c"
+    mpath.write_text(src.replace(old, new))
+    so = tmp_path / f"lib_{name}.so"
+    subprocess.run(["gcc", "-O1", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off", "-o", str(so),
+                    str(mpath), "-lm"], check=True)
+    spec = importlib.util.spec_from_file_location(f"oracle_{name}", PY)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    import ctypes
+    mod._lib = ctypes.CDLL(str(so))
+    mod._declare(mod._lib)
+    return mod
+
+
+# ----------------------------------------------------------------- predicates
+
+def chk_popcount(O):
+    n, k = 9, 77
+    words = I.sign_words(I.stream(11, n, k), n, k)
+    lay = layer_from(n, k, 1, 0, 0, words[None], f16(np.ones((1, n))), f16(np.ones((1, k))))
+    y, _ = O.gemv_dense(lay, f16(np.ones((1, k))))
+    pc = np.array([sum(bin(int(w)).count("1") for w in row) for row in words])
+    return np.array_equal(y[0], 2.0 * pc - k)
+
+
+def chk_one_hot(O):
+    n, k, j = 17, 64, 45
+    rng = I.stream(13, j)
+    words = I.sign_words(rng, n, k)
+    r = f16(rng.uniform(0.5, 2.0, (1, n)))
+    c = np.zeros((1, k))
+    c[0, j] = 1.0
+    lay = layer_from(n, k, 1, 0, 0, words[None], r, f16(c))
+    y, _ = O.gemv_dense(lay, f16(np.full((1, k), 3.0)))
+    signs = 2 * bits_of(words, k)[:, j] - 1
+    return np.array_equal(y[0], r[0].view(np.float16).astype(np.float64) * signs * 3.0)
+
+
+def chk_bruteforce(O):
+    for (n, k, kb, ks, s) in [(6, 40, 2, 1, 9), (4, 64, 3, 2, 17)]:
+        lay = I.dyadic_layer(n, k, kb, ks, 4, s, seed=n * 100 + k)
+        x = I.dyadic_x(k, 2, seed=k)
+        if not np.array_equal(O.gemv_dense(lay, x)[0], exact_y(lay, x)):
+            return False
+    return True
+
+
+def chk_half_numpy(O):
+    v = np.random.default_rng(1).normal(0, 1, 5000)
+    return np.array_equal(O.double_to_half(v), v.astype(np.float16).view(np.uint16))
+
+
+CHECKS = [chk_popcount, chk_one_hot, chk_bruteforce, chk_half_numpy]
+
+
+def test_unmutated_oracle_passes_every_check(orc):
+    assert all(chk(orc) for chk in CHECKS)
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_every_planted_mistake_is_caught(name, tmp_path):
+    O = build_mutant(name, tmp_path)
+    failed = [chk.__name__ for chk in CHECKS if not chk(O)]
+    assert failed, f"mutant {name} passed every pin"
