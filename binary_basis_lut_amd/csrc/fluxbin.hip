@@ -1,0 +1,491 @@
+// fluxbin.hip -- C ABI of libfluxbin.so (declared in include/fluxbin.h).
+//
+// Host side: argument validation (pure host work, before any HIP call),
+// work planning, kernel launches.  The kernels live in kernels.hpp.
+#include "fluxbin.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "kernels.hpp"
+
+using namespace fluxbin;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+fluxbin_status fail(fluxbin_status st, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+fluxbin_status hip_fail(hipError_t e, const char *what) {
+  return fail(FLUXBIN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+fluxbin_status ok() {
+  g_err[0] = '\0';
+  return FLUXBIN_OK;
+}
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+constexpr int kWaves = 4;          // waves per workgroup of the GEMV kernel
+constexpr int kTargetBlocks = 512; // enough workgroups for two per CU on 256 CUs
+
+struct Plan {
+  int32_t nb;          // compiled batch width (power of two >= max_batch)
+  int32_t cpb;         // chunks per workgroup
+  int32_t row_tiles;
+  int32_t row_blocks;
+  int32_t total_chunks;
+  int32_t splits;
+  int64_t n_pad;
+  size_t partial_bytes;
+  size_t counter_bytes;
+};
+
+int32_t pow2_at_least(int64_t v) {
+  int32_t p = 1;
+  while (p < v) p <<= 1;
+  return p;
+}
+
+// Largest chunks-per-workgroup whose tables fit the LDS budget of one workgroup.
+int32_t max_cpb(int32_t g, int32_t nb) {
+  const int32_t limit = g == 4 ? 32 : 4;  // CPB * NB: 64 KiB of tables either way
+  int32_t c = 8;
+  while (c > 1 && c * nb > limit) c >>= 1;
+  return c;
+}
+
+int32_t lds_bytes(int32_t g, int32_t nb, int32_t cpb) {
+  const int32_t tab = cpb * nb * (kChunkCols / g) * (1 << g) * 4;
+  const int32_t v = cpb * nb * kChunkCols * 4;
+  return tab + v + 16;
+}
+
+fluxbin_status validate_shape(const fluxbin_layer_desc *d) {
+  if (!d) return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "desc is NULL");
+  if (d->abi_version != FLUXBIN_ABI_VERSION)
+    return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "abi_version %d, library %d", d->abi_version, FLUXBIN_ABI_VERSION);
+  if (d->g != 4 && d->g != 8) return fail(FLUXBIN_ERR_UNSUPPORTED, "g = %d (supported: 4, 8)", d->g);
+  if (d->kb < 1 || d->kb > 4) return fail(FLUXBIN_ERR_UNSUPPORTED, "kb = %d (supported: 1..4)", d->kb);
+  if (d->ks < 0 || d->ks > 2) return fail(FLUXBIN_ERR_UNSUPPORTED, "ks = %d (supported: 0..2)", d->ks);
+  if (d->n < 1 || d->k < 1) return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "n = %lld, k = %lld (must be >= 1)",
+                                        (long long)d->n, (long long)d->k);
+  if (d->n > (int64_t)1 << 30 || d->k > (int64_t)1 << 30)
+    return fail(FLUXBIN_ERR_UNSUPPORTED, "n or k above 2^30");
+  if (d->ks == 0 && d->s != 0) return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "s = %lld with ks = 0", (long long)d->s);
+  if (d->ks > 0 && (d->s < 1 || d->s > d->k))
+    return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "s = %lld must be in [1, k] when ks > 0", (long long)d->s);
+  const int64_t maxb = d->g == 4 ? 16 : 4;
+  if (d->max_batch < 1 || d->max_batch > maxb)
+    return fail(FLUXBIN_ERR_UNSUPPORTED, "max_batch = %lld (supported for g = %d: 1..%lld)",
+                (long long)d->max_batch, d->g, (long long)maxb);
+  if (d->chunks_per_block != 0 && d->chunks_per_block != 1 && d->chunks_per_block != 2 &&
+      d->chunks_per_block != 4 && d->chunks_per_block != 8)
+    return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "chunks_per_block = %d (0, 1, 2, 4 or 8)", d->chunks_per_block);
+  if (d->reserved != 0) return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "reserved field must be 0");
+  return FLUXBIN_OK;
+}
+
+fluxbin_status make_plan(const fluxbin_layer_desc *d, Plan *p) {
+  p->nb = pow2_at_least(d->max_batch);
+  const int32_t cmax = max_cpb(d->g, p->nb);
+  p->row_tiles = (int32_t)cdiv(d->n, kTileRows);
+  p->row_blocks = (int32_t)cdiv(p->row_tiles, kWaves);
+  p->n_pad = (int64_t)p->row_tiles * kTileRows;
+  p->total_chunks = (int32_t)(d->kb * cdiv(d->k, kChunkCols) + d->ks * cdiv(d->s, kChunkCols));
+  if (d->chunks_per_block) {
+    if (d->chunks_per_block > cmax)
+      return fail(FLUXBIN_ERR_UNSUPPORTED, "chunks_per_block = %d exceeds %d for g = %d, max_batch = %lld",
+                  d->chunks_per_block, cmax, d->g, (long long)d->max_batch);
+    p->cpb = d->chunks_per_block;
+  } else {
+    p->cpb = cmax;
+    while (p->cpb > 1 && (int64_t)p->row_blocks * cdiv(p->total_chunks, p->cpb) < kTargetBlocks) p->cpb >>= 1;
+  }
+  p->splits = (int32_t)cdiv(p->total_chunks, p->cpb);
+  p->partial_bytes = p->splits > 1 ? (size_t)p->splits * d->max_batch * p->n_pad * sizeof(float) : 0;
+  p->partial_bytes = (p->partial_bytes + 255) / 256 * 256;
+  p->counter_bytes = p->splits > 1 ? (size_t)p->row_blocks * kCounterStride * sizeof(uint32_t) : 0;
+  return FLUXBIN_OK;
+}
+
+}  // namespace
+
+struct fluxbin_layer {
+  fluxbin_layer_desc d;
+  Plan plan;
+  bool fault_launch;
+};
+
+// ---------------------------------------------------------------------------
+// launch table for the GEMV kernel
+// ---------------------------------------------------------------------------
+namespace {
+
+typedef void (*gemv_fn)(const GemvArgs);
+
+// Instances whose tables exceed the LDS budget (CPB * NB * table bytes > 64 KiB) are not built.
+template <int G, int NB, int CPB>
+gemv_fn instance() {
+  if constexpr (CPB * NB <= (G == 4 ? 32 : 4)) {
+    return lut_gemv_kernel<G, NB, CPB, kWaves>;
+  } else {
+    return nullptr;
+  }
+}
+
+template <int G, int NB>
+gemv_fn pick_cpb(int cpb) {
+  switch (cpb) {
+    case 1: return instance<G, NB, 1>();
+    case 2: return instance<G, NB, 2>();
+    case 4: return instance<G, NB, 4>();
+    case 8: return instance<G, NB, 8>();
+  }
+  return nullptr;
+}
+
+gemv_fn pick_gemv(int g, int nb, int cpb) {
+  if (g == 4) {
+    switch (nb) {
+      case 1: return pick_cpb<4, 1>(cpb);
+      case 2: return pick_cpb<4, 2>(cpb);
+      case 4: return pick_cpb<4, 4>(cpb);
+      case 8: return pick_cpb<4, 8>(cpb);
+      case 16: return pick_cpb<4, 16>(cpb);
+    }
+  } else if (g == 8) {
+    switch (nb) {
+      case 1: return pick_cpb<8, 1>(cpb);
+      case 2: return pick_cpb<8, 2>(cpb);
+      case 4: return pick_cpb<8, 4>(cpb);
+    }
+  }
+  return nullptr;
+}
+
+void fill_segments(const fluxbin_layer_desc &d, Seg *seg, int32_t *nseg) {
+  int32_t chunk0 = 0, ns = 0;
+  const int64_t tw_g = fluxbin_tiled_words(d.n, d.k);
+  for (int b = 0; b < d.kb; ++b, ++ns) {
+    Seg &s = seg[ns];
+    s.bits = reinterpret_cast<const u32x4 *>(d.bits_global + (int64_t)b * tw_g);
+    s.c = d.c_global + (int64_t)b * d.k;
+    s.r = d.r_global + (int64_t)b * d.n;
+    s.len = (int32_t)d.k;
+    s.nchunks = (int32_t)cdiv(d.k, kChunkCols);
+    s.chunk0 = chunk0;
+    s.salient = 0;
+    chunk0 += s.nchunks;
+  }
+  if (d.ks > 0) {
+    const int64_t tw_s = fluxbin_tiled_words(d.n, d.s);
+    for (int b = 0; b < d.ks; ++b, ++ns) {
+      Seg &s = seg[ns];
+      s.bits = reinterpret_cast<const u32x4 *>(d.bits_sal + (int64_t)b * tw_s);
+      s.c = d.c_sal + (int64_t)b * d.s;
+      s.r = d.r_sal + (int64_t)b * d.n;
+      s.len = (int32_t)d.s;
+      s.nchunks = (int32_t)cdiv(d.s, kChunkCols);
+      s.chunk0 = chunk0;
+      s.salient = 1;
+      chunk0 += s.nchunks;
+    }
+  }
+  for (int i = ns; i < kMaxSeg; ++i) seg[i] = Seg{nullptr, nullptr, nullptr, 0, 0, 1 << 30, 0};
+  *nseg = ns;
+}
+
+int grid_for(int64_t items, int per_thread_block = 256) {
+  int64_t g = cdiv(items, per_thread_block);
+  if (g < 1) g = 1;
+  if (g > 65536) g = 65536;
+  return (int)g;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// C ABI
+// ---------------------------------------------------------------------------
+extern "C" {
+
+int32_t fluxbin_abi_version(void) { return FLUXBIN_ABI_VERSION; }
+
+const char *fluxbin_status_string(fluxbin_status s) {
+  switch (s) {
+    case FLUXBIN_OK: return "ok";
+    case FLUXBIN_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case FLUXBIN_ERR_UNSUPPORTED: return "unsupported";
+    case FLUXBIN_ERR_WORKSPACE: return "workspace missing or too small";
+    case FLUXBIN_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char *fluxbin_last_error(void) { return g_err; }
+
+int64_t fluxbin_tiled_words(int64_t rows, int64_t cols) {
+  if (rows <= 0 || cols <= 0) return 0;
+  return cdiv(rows, kTileRows) * cdiv(cols, kChunkCols) * kTileRows * 4;
+}
+
+fluxbin_status fluxbin_pack(const int8_t *signs, int64_t rows, int64_t cols, int64_t ld, int32_t layout,
+                            uint32_t *packed, uint32_t *invalid_count, void *stream) {
+  if (rows < 0 || cols < 0) return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "negative size");
+  if (layout != FLUXBIN_LAYOUT_ROWMAJOR && layout != FLUXBIN_LAYOUT_TILED)
+    return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "layout = %d", layout);
+  if (rows == 0 || cols == 0) return ok();
+  if (!signs || !packed) return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "NULL pointer");
+  if (ld < cols) return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "ld = %lld < cols = %lld", (long long)ld, (long long)cols);
+  const int64_t words = layout == FLUXBIN_LAYOUT_ROWMAJOR ? rows * cdiv(cols, 32) : fluxbin_tiled_words(rows, cols);
+  hipLaunchKernelGGL(pack_kernel, dim3(grid_for(words)), dim3(256), 0, (hipStream_t)stream, signs, rows, cols, ld,
+                     layout, packed, invalid_count, words);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "pack launch");
+  return ok();
+}
+
+fluxbin_status fluxbin_relayout(const uint32_t *src, int64_t rows, int64_t cols, int32_t src_layout,
+                                int32_t dst_layout, uint32_t *dst, void *stream) {
+  if (rows < 0 || cols < 0) return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "negative size");
+  for (int32_t l : {src_layout, dst_layout})
+    if (l != FLUXBIN_LAYOUT_ROWMAJOR && l != FLUXBIN_LAYOUT_TILED)
+      return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "layout = %d", l);
+  if (rows == 0 || cols == 0) return ok();
+  if (!src || !dst) return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "NULL pointer");
+  if (src == dst) return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "src and dst must not overlap");
+  const int64_t words =
+      dst_layout == FLUXBIN_LAYOUT_ROWMAJOR ? rows * cdiv(cols, 32) : fluxbin_tiled_words(rows, cols);
+  hipLaunchKernelGGL(relayout_kernel, dim3(grid_for(words)), dim3(256), 0, (hipStream_t)stream, src, rows, cols,
+                     src_layout, dst_layout, dst, words);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "relayout launch");
+  return ok();
+}
+
+fluxbin_status fluxbin_vcm_gather(const int32_t *idx, int64_t s, const void *src, int64_t rows, int64_t cols,
+                                  int32_t dtype, void *dst, void *stream) {
+  if (s < 0 || rows < 0 || cols < 0) return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "negative size");
+  if (dtype != FLUXBIN_DT_I8 && dtype != FLUXBIN_DT_F16 && dtype != FLUXBIN_DT_BITS)
+    return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "dtype = %d", dtype);
+  if (s == 0 || rows == 0) return ok();
+  if (!idx || !src || !dst) return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "NULL pointer");
+  if (cols < 1) return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "cols = 0 with s > 0");
+  hipStream_t st = (hipStream_t)stream;
+  if (dtype == FLUXBIN_DT_I8) {
+    hipLaunchKernelGGL(vcm_gather_values_kernel<int8_t>, dim3(grid_for(rows * s)), dim3(256), 0, st, idx, s,
+                       (const int8_t *)src, rows, cols, (int8_t *)dst, (int8_t)-1);
+  } else if (dtype == FLUXBIN_DT_F16) {
+    hipLaunchKernelGGL(vcm_gather_values_kernel<uint16_t>, dim3(grid_for(rows * s)), dim3(256), 0, st, idx, s,
+                       (const uint16_t *)src, rows, cols, (uint16_t *)dst, (uint16_t)0);
+  } else {
+    hipLaunchKernelGGL(vcm_gather_bits_kernel, dim3(grid_for(rows * cdiv(s, 32))), dim3(256), 0, st, idx, s,
+                       (const uint32_t *)src, rows, cols, (uint32_t *)dst);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "vcm gather launch");
+  return ok();
+}
+
+fluxbin_status fluxbin_workspace_size(const fluxbin_layer_desc *d, size_t *bytes) {
+  fluxbin_status st = validate_shape(d);
+  if (st) return st;
+  if (!bytes) return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  Plan p;
+  st = make_plan(d, &p);
+  if (st) return st;
+  *bytes = p.partial_bytes + p.counter_bytes;
+  return ok();
+}
+
+fluxbin_status fluxbin_create(const fluxbin_layer_desc *d, fluxbin_handle *out) {
+  fluxbin_status st = validate_shape(d);
+  if (st) return st;
+  if (!out) return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "out is NULL");
+  if (!d->bits_global || !d->r_global || !d->c_global)
+    return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "global basis pointers must be non-NULL");
+  if (!aligned(d->bits_global, 16)) return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "bits_global not 16-byte aligned");
+  if (d->ks > 0) {
+    if (!d->bits_sal || !d->r_sal || !d->c_sal || !d->sal_idx)
+      return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "salient pointers must be non-NULL when ks > 0");
+    if (!aligned(d->bits_sal, 16)) return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "bits_sal not 16-byte aligned");
+  }
+  Plan p;
+  st = make_plan(d, &p);
+  if (st) return st;
+  const size_t need = p.partial_bytes + p.counter_bytes;
+  if (need > 0) {
+    if (!d->workspace || d->workspace_bytes < need)
+      return fail(FLUXBIN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                  d->workspace ? d->workspace_bytes : (size_t)0);
+    if (!aligned(d->workspace, 256)) return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "workspace not 256-byte aligned");
+  }
+  // salient index: strictly ascending, in [0, k)
+  if (d->ks > 0) {
+    std::vector<int32_t> idx((size_t)d->s);
+    hipError_t e = hipMemcpy(idx.data(), d->sal_idx, (size_t)d->s * sizeof(int32_t), hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(e, "reading sal_idx");
+    for (int64_t i = 0; i < d->s; ++i) {
+      if (idx[i] < 0 || idx[i] >= d->k)
+        return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "sal_idx[%lld] = %d outside [0, %lld)", (long long)i, idx[i],
+                    (long long)d->k);
+      if (i > 0 && idx[i] <= idx[i - 1])
+        return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "sal_idx not strictly ascending at %lld", (long long)i);
+    }
+  }
+  if (p.counter_bytes) {
+    hipError_t e = hipMemset((char *)d->workspace + p.partial_bytes, 0, p.counter_bytes);
+    if (e != hipSuccess) return hip_fail(e, "zeroing reduction counters");
+    e = hipDeviceSynchronize();
+    if (e != hipSuccess) return hip_fail(e, "synchronising after create");
+  }
+  fluxbin_layer *h = new (std::nothrow) fluxbin_layer;
+  if (!h) return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "out of host memory");
+  h->d = *d;
+  h->plan = p;
+  const char *f = getenv("FLUXBIN_FAULT");
+  h->fault_launch = f && strcmp(f, "launch") == 0;
+  *out = h;
+  return ok();
+}
+
+fluxbin_status fluxbin_destroy(fluxbin_handle h) {
+  if (!h) return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "handle is NULL");
+  delete h;
+  return ok();
+}
+
+fluxbin_status fluxbin_get_plan(fluxbin_handle h, fluxbin_plan *plan) {
+  if (!h || !plan) return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "NULL argument");
+  const Plan &p = h->plan;
+  plan->rows_per_block = kWaves * kTileRows;
+  plan->chunks_per_block = p.cpb;
+  plan->row_blocks = p.row_blocks;
+  plan->splits = p.splits;
+  plan->total_chunks = p.total_chunks;
+  plan->lds_bytes = lds_bytes(h->d.g, p.nb, p.cpb);
+  plan->grid = (int64_t)p.row_blocks * p.splits;
+  return ok();
+}
+
+fluxbin_status fluxbin_lut_size(fluxbin_handle h, int64_t batch, size_t *floats) {
+  if (!h || !floats) return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "NULL argument");
+  if (batch < 0) return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "negative batch");
+  const fluxbin_layer_desc &d = h->d;
+  const int64_t subs = d.kb * cdiv(d.k, d.g) + d.ks * cdiv(d.s, d.g);
+  *floats = (size_t)(batch * subs * ((int64_t)1 << (d.g - 1)));
+  return ok();
+}
+
+fluxbin_status fluxbin_build_lut(fluxbin_handle h, const uint16_t *x, int64_t batch, float *lut, void *stream) {
+  if (!h) return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "handle is NULL");
+  if (batch < 0 || batch > h->d.max_batch)
+    return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "batch = %lld outside [0, %lld]", (long long)batch,
+                (long long)h->d.max_batch);
+  if (batch == 0) return ok();
+  if (!x || !lut) return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "NULL pointer");
+  if (h->fault_launch) return fail(FLUXBIN_ERR_HIP, "injected launch fault (FLUXBIN_FAULT=launch)");
+  const fluxbin_layer_desc &d = h->d;
+  LutArgs a;
+  int32_t nseg;
+  fill_segments(d, a.seg, &nseg);
+  a.nseg = nseg;
+  a.g = d.g;
+  int64_t sub = 0;
+  for (int i = 0; i < kMaxSeg; ++i) {
+    a.sub0[i] = i < nseg ? sub : ((int64_t)1 << 62);
+    if (i < nseg) sub += cdiv(a.seg[i].len, d.g);
+  }
+  a.subs_per_batch = sub;
+  a.k = d.k;
+  a.batch = (int32_t)batch;
+  a.sal_idx = d.sal_idx;
+  a.x = x;
+  a.lut = lut;
+  const int64_t total = batch * sub * ((int64_t)1 << (d.g - 1));
+  if (d.g == 4)
+    hipLaunchKernelGGL(build_lut_kernel<4>, dim3(grid_for(total)), dim3(256), 0, (hipStream_t)stream, a);
+  else
+    hipLaunchKernelGGL(build_lut_kernel<8>, dim3(grid_for(total)), dim3(256), 0, (hipStream_t)stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "build_lut launch");
+  return ok();
+}
+
+fluxbin_status fluxbin_gemv(fluxbin_handle h, const uint16_t *x, uint16_t *y, int64_t batch, void *stream) {
+  if (!h) return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "handle is NULL");
+  if (batch < 0 || batch > h->d.max_batch)
+    return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "batch = %lld outside [0, %lld]", (long long)batch,
+                (long long)h->d.max_batch);
+  if (batch == 0) return ok();
+  if (!x || !y) return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "NULL pointer");
+  if (h->fault_launch) return fail(FLUXBIN_ERR_HIP, "injected launch fault (FLUXBIN_FAULT=launch)");
+  const fluxbin_layer_desc &d = h->d;
+  const Plan &p = h->plan;
+  gemv_fn fn = pick_gemv(d.g, p.nb, p.cpb);
+  if (!fn) return fail(FLUXBIN_ERR_UNSUPPORTED, "no kernel for g = %d, nb = %d, cpb = %d", d.g, p.nb, p.cpb);
+  GemvArgs a;
+  int32_t nseg;
+  fill_segments(d, a.seg, &nseg);
+  a.nseg = nseg;
+  a.total_chunks = p.total_chunks;
+  a.row_tiles = p.row_tiles;
+  a.row_blocks = p.row_blocks;
+  a.splits = p.splits;
+  a.batch = (int32_t)batch;
+  a.n = d.n;
+  a.k = d.k;
+  a.n_pad = p.n_pad;
+  a.sal_idx = d.sal_idx;
+  a.x = x;
+  a.y = y;
+  a.partials = p.splits > 1 ? reinterpret_cast<float *>(d.workspace) : nullptr;
+  a.counters = p.splits > 1 ? reinterpret_cast<uint32_t *>((char *)d.workspace + p.partial_bytes) : nullptr;
+  const int64_t grid = (int64_t)p.row_blocks * p.splits;
+  hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(kWaves * 64), 0, (hipStream_t)stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "gemv launch");
+  return ok();
+}
+
+fluxbin_status fluxbin_dense_gemv_f16(const uint16_t *w, int64_t n, int64_t k, const uint16_t *x, uint16_t *y,
+                                      int64_t batch, void *stream) {
+  if (n < 1 || k < 1) return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "n, k must be >= 1");
+  if (k % 8) return fail(FLUXBIN_ERR_UNSUPPORTED, "k = %lld not a multiple of 8", (long long)k);
+  if (batch < 1 || batch > 16) return fail(FLUXBIN_ERR_UNSUPPORTED, "batch = %lld (1..16)", (long long)batch);
+  if (!w || !x || !y) return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "NULL pointer");
+  if (!aligned(w, 16) || !aligned(x, 16)) return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "w and x must be 16-B aligned");
+  const int nb = pow2_at_least(batch);
+  const dim3 grid((unsigned)cdiv(n, 4)), block(256);
+  hipStream_t st = (hipStream_t)stream;
+  switch (nb) {
+    case 1: hipLaunchKernelGGL(dense_f16_gemv_kernel<1>, grid, block, 0, st, w, n, k, x, y, (int)batch); break;
+    case 2: hipLaunchKernelGGL(dense_f16_gemv_kernel<2>, grid, block, 0, st, w, n, k, x, y, (int)batch); break;
+    case 4: hipLaunchKernelGGL(dense_f16_gemv_kernel<4>, grid, block, 0, st, w, n, k, x, y, (int)batch); break;
+    case 8: hipLaunchKernelGGL(dense_f16_gemv_kernel<8>, grid, block, 0, st, w, n, k, x, y, (int)batch); break;
+    default: hipLaunchKernelGGL(dense_f16_gemv_kernel<16>, grid, block, 0, st, w, n, k, x, y, (int)batch); break;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "dense gemv launch");
+  return ok();
+}
+
+}  // extern "C"

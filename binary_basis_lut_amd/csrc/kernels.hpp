@@ -1,0 +1,471 @@
+// kernels.hpp -- gfx950 (CDNA4) kernels of the FluxBin LUT GEMV.
+//
+// Method (FluxBin: Flexible LUT-based Ultra-low-bit LLM Inference by
+// Algorithm-Kernel Synergy, paperlayer.ai summary, section 3 bullets
+// "LUT-Based GEMV Kernel" and "Virtual Columnar Mapping", appendix C.1; the
+// ainews.surl.tw article on FluxBin, paragraph on the execution layer):
+//   * scale-fused tables: for every g-column sub-vector the 2^g signed sums of
+//     v_t = c_t * x_t are tabulated, so the column scale never reaches the
+//     main loop; only 2^(g-1) sums are computed, the other half is their
+//     negation (LUT[~p] = -LUT[p], LUT Tensor Core notes, section 3.1.2);
+//   * the packed sign bits of a row are used directly as table indices;
+//   * lookups accumulate in fp32 registers; the row scale is applied once per
+//     segment after accumulation;
+//   * salient bases run through the same code on their compact columns, with
+//     x gathered through the salient index while the tables are built (VCM).
+//
+// Mapping onto CDNA4 (not the pages' A100 tiling):
+//   * one wave = 64 output rows, lane l = row l of its tile; all 64 lanes read
+//     the SAME 2^g-entry table at each step, so table reads are broadcasts
+//     within 16 (g=4) or 256 (g=8) consecutive dwords;
+//   * weights are streamed from the TILED layout: a wave's 16-byte-per-lane
+//     load of one 128-column chunk is 1 KiB of contiguous memory, loaded with
+//     non-temporal 128-bit loads (streamed once, kept out of L2);
+//   * a workgroup of WAVES waves shares the tables of CPB consecutive chunks of
+//     the concatenated column space of all segments; a grid of
+//     row_blocks x splits workgroups covers the layer;
+//   * splits > 1: each workgroup writes fp32 partial sums; the last workgroup
+//     of a row block to finish (agent-scope atomic counter) adds them in split
+//     order, writes fp16 y and re-arms the counter, so one launch does the
+//     whole GEMV and the result is bitwise deterministic.
+#pragma once
+
+#include <hip/hip_fp16.h>
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fluxbin {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kChunkCols = 128;  // columns per chunk = 4 sign words per row
+constexpr int kTileRows = 64;    // rows per tile = one wave, one row per lane
+constexpr int kMaxSeg = 6;       // kb <= 4 global + ks <= 2 salient bases
+constexpr int kCounterStride = 32;  // uint32 per reduction counter (128-byte spacing)
+
+struct Seg {
+  const u32x4 *bits;    // tiled words; element ((tile * nchunks + chunk) * 64 + lane)
+  const uint16_t *c;    // fp16 column scales [len]
+  const uint16_t *r;    // fp16 row scales [n]
+  int32_t len;          // columns of this segment (k or s)
+  int32_t nchunks;      // ceil(len / 128)
+  int32_t chunk0;       // first chunk of the segment in the concatenated chunk space
+  int32_t salient;      // 1: activation of compact column c is x[sal_idx[c]]
+};
+
+struct GemvArgs {
+  Seg seg[kMaxSeg];
+  int32_t nseg;
+  int32_t total_chunks;
+  int32_t row_tiles;
+  int32_t row_blocks;
+  int32_t splits;
+  int32_t batch;
+  int64_t n;
+  int64_t k;
+  int64_t n_pad;          // row_tiles * 64
+  const int32_t *sal_idx;
+  const uint16_t *x;      // fp16 [batch][k]
+  uint16_t *y;            // fp16 [batch][n]
+  float *partials;        // [splits][batch][n_pad]
+  uint32_t *counters;     // [row_blocks * kCounterStride]
+};
+
+__device__ __forceinline__ float h2f(uint16_t h) { return __half2float(__ushort_as_half(h)); }
+__device__ __forceinline__ uint16_t f2h(float f) { return __half_as_ushort(__float2half_rn(f)); }
+
+// Segment owning global chunk gc (uniform across the workgroup).
+__device__ __forceinline__ int seg_of(const GemvArgs &a, int gc) {
+  int s = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxSeg; ++i)
+    if (i < a.nseg && gc >= a.seg[i].chunk0) s = i;
+  return s;
+}
+
+// Value number s of six scalars (s uniform).  Plain SSA values, never an
+// aggregate: an array or struct indexed by a runtime segment number would be
+// placed in LDS or scratch memory by the compiler.
+__device__ __forceinline__ float pick6(int s, float v0, float v1, float v2, float v3, float v4, float v5) {
+  float r = v0;
+  r = s == 1 ? v1 : r;
+  r = s == 2 ? v2 : r;
+  r = s == 3 ? v3 : r;
+  r = s == 4 ? v4 : r;
+  r = s == 5 ? v5 : r;
+  return r;
+}
+
+// Byte `kk` of v, zero-extended (v_perm_b32: opaque to the optimiser, one VALU op).
+template <int kk>
+__device__ __forceinline__ uint32_t byte_of(uint32_t v) {
+  return __builtin_amdgcn_perm(0u, v, 0x0c0c0c00u | kk);
+}
+
+template <int G, int NB>
+__device__ __forceinline__ void lookup_word(uint32_t w, const char *tb, float (&acc)[NB], int j0) {
+  constexpr int SUB = kChunkCols / G;
+  constexpr int TAB = 1 << G;
+  if constexpr (G == 4) {
+    // nibble m of w at bits [4m, 4m+4); A holds nibbles 0,2,4,6 and B nibbles
+    // 1,3,5,7 as byte offsets (index * 4) of a 16-entry fp32 table.
+    const uint32_t A = (w << 2) & 0x3c3c3c3cu;
+    const uint32_t B = (w >> 2) & 0x3c3c3c3cu;
+    const uint32_t ia[4] = {byte_of<0>(A), byte_of<1>(A), byte_of<2>(A), byte_of<3>(A)};
+    const uint32_t ib[4] = {byte_of<0>(B), byte_of<1>(B), byte_of<2>(B), byte_of<3>(B)};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const char *t0 = tb + ((b * SUB + j0 + 2 * kk) * TAB) * 4;
+        acc[b] += *reinterpret_cast<const float *>(t0 + ia[kk]);
+        acc[b] += *reinterpret_cast<const float *>(t0 + TAB * 4 + ib[kk]);
+      }
+    }
+  } else {
+    // byte kk of w is the 8-bit pattern of sub-vector j0 + kk
+    const uint32_t W = w;
+    uint32_t ix[4];
+    ix[0] = (W << 2) & 0x3fcu;
+    ix[1] = (W >> 6) & 0x3fcu;
+    ix[2] = (W >> 14) & 0x3fcu;
+    ix[3] = (W >> 22) & 0x3fcu;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const char *t0 = tb + ((b * SUB + j0 + kk) * TAB) * 4;
+        acc[b] += *reinterpret_cast<const float *>(t0 + ix[kk]);
+      }
+    }
+  }
+}
+
+template <int G, int NB, int CPB, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void lut_gemv_kernel(const GemvArgs a) {
+  constexpr int NT = WAVES * 64;
+  constexpr int SUB = kChunkCols / G;  // sub-vectors per chunk
+  constexpr int TAB = 1 << G;          // full table entries
+  constexpr int HALF = TAB / 2;
+  constexpr int WPL = kChunkCols / 32;  // words per lane per chunk (4)
+  __shared__ float s_tab[CPB * NB * SUB * TAB];  // [chunk][batch][sub-vector][pattern]
+  __shared__ float s_v[CPB * NB * kChunkCols];   // [chunk][batch][column] scale-fused inputs
+  __shared__ int s_last;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int rb = blockIdx.x % a.row_blocks;
+  const int sp = blockIdx.x / a.row_blocks;
+  const int tile = rb * WAVES + wave;
+  const bool tile_ok = tile < a.row_tiles;
+  const int64_t row = (int64_t)tile * kTileRows + lane;
+  const bool row_ok = tile_ok && row < a.n;
+  const int c0 = sp * CPB;
+  const int nch = min(CPB, a.total_chunks - c0);
+
+  // 1. stream this lane's 16 bytes of every chunk (issued first: longest latency)
+  u32x4 w[CPB];
+#pragma unroll
+  for (int ch = 0; ch < CPB; ++ch) {
+    w[ch] = u32x4{0u, 0u, 0u, 0u};
+    if (ch < nch && tile_ok) {
+      const int gc = c0 + ch;
+      const Seg &sg = a.seg[seg_of(a, gc)];
+      const int cis = gc - sg.chunk0;
+      w[ch] = __builtin_nontemporal_load(sg.bits + ((int64_t)tile * sg.nchunks + cis) * kTileRows + lane);
+    }
+  }
+  // row scales of the segments this workgroup touches
+  const int s_first = seg_of(a, c0);
+  const int s_lastseg = seg_of(a, c0 + nch - 1);
+  auto rload = [&](int s) -> float {
+    return (row_ok && s >= s_first && s <= s_lastseg) ? h2f(a.seg[s].r[row]) : 0.0f;
+  };
+  const float rv0 = rload(0), rv1 = rload(1), rv2 = rload(2), rv3 = rload(3), rv4 = rload(4), rv5 = rload(5);
+
+  // 2. scale-fused inputs v = c * x (exact in fp32: product of two fp16 values)
+  for (int e = tid; e < nch * NB * kChunkCols; e += NT) {
+    const int ch = e / (NB * kChunkCols);
+    const int rem = e - ch * (NB * kChunkCols);
+    const int b = rem / kChunkCols;
+    const int col = rem - b * kChunkCols;
+    const int gc = c0 + ch;
+    const Seg &sg = a.seg[seg_of(a, gc)];
+    const int64_t cc = (int64_t)(gc - sg.chunk0) * kChunkCols + col;
+    float v = 0.0f;
+    if (b < a.batch && cc < sg.len) {
+      const int64_t xi = sg.salient ? (int64_t)a.sal_idx[cc] : cc;
+      v = h2f(sg.c[cc]) * h2f(a.x[(int64_t)b * a.k + xi]);
+    }
+    s_v[(ch * NB + b) * kChunkCols + col] = v;
+  }
+  __syncthreads();
+
+  // 3. tables: the half with the top input at +1 is summed, the rest negated
+  for (int e = tid; e < nch * NB * SUB * HALF; e += NT) {
+    const int q = e % HALF;
+    const int j = (e / HALF) % SUB;
+    const int cb = e / (HALF * SUB);  // chunk * NB + batch row
+    const float *v = &s_v[cb * kChunkCols + j * G];
+    float t = v[G - 1];
+#pragma unroll
+    for (int i = 0; i < G - 1; ++i) t = ((q >> i) & 1) ? t + v[i] : t - v[i];
+    float *tb = &s_tab[(cb * SUB + j) * TAB];
+    tb[q | HALF] = t;
+    tb[(HALF - 1) ^ q] = -t;
+  }
+  __syncthreads();
+
+  // 4. lookups: sign patterns index the tables; fp32 accumulation per segment
+  float part[NB], acc[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) part[b] = acc[b] = 0.0f;
+  int cur = s_first;
+#pragma unroll
+  for (int ch = 0; ch < CPB; ++ch) {
+    if (ch < nch) {
+      const int s = seg_of(a, c0 + ch);
+      if (s != cur) {
+        const float rc = pick6(cur, rv0, rv1, rv2, rv3, rv4, rv5);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          part[b] += rc * acc[b];
+          acc[b] = 0.0f;
+        }
+        cur = s;
+      }
+      const char *tb = reinterpret_cast<const char *>(&s_tab[ch * NB * SUB * TAB]);
+#pragma unroll
+      for (int q = 0; q < WPL; ++q) lookup_word<G, NB>(w[ch][q], tb, acc, q * (32 / G));
+    }
+  }
+  {
+    const float rc = pick6(cur, rv0, rv1, rv2, rv3, rv4, rv5);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) part[b] += rc * acc[b];
+  }
+
+  // 5. output
+  if (a.splits == 1) {
+    if (row_ok) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+        if (b < a.batch) a.y[(int64_t)b * a.n + row] = f2h(part[b]);
+    }
+    return;
+  }
+  if (tile_ok) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+      if (b < a.batch)
+        __hip_atomic_store(&a.partials[((int64_t)sp * a.batch + b) * a.n_pad + row], part[b], __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t prev =
+        __hip_atomic_fetch_add(&a.counters[rb * kCounterStride], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = (prev == (uint32_t)(a.splits - 1));
+  }
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  if (row_ok) {
+    for (int b = 0; b < a.batch; ++b) {
+      float sum = 0.0f;
+      for (int p = 0; p < a.splits; ++p)
+        sum += __hip_atomic_load(&a.partials[((int64_t)p * a.batch + b) * a.n_pad + row], __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+      a.y[(int64_t)b * a.n + row] = f2h(sum);
+    }
+  }
+  if (tid == 0) __hip_atomic_store(&a.counters[rb * kCounterStride], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// --------------------------------------------------------------------------
+// Half tables to global memory (the exported table builder)
+// --------------------------------------------------------------------------
+struct LutArgs {
+  Seg seg[kMaxSeg];
+  int32_t nseg;
+  int32_t g;
+  int64_t subs_per_batch;   // sum over segments of ceil(len/g)
+  int64_t sub0[kMaxSeg];    // first sub-vector of each segment within a batch row
+  int64_t k;
+  int32_t batch;
+  const int32_t *sal_idx;
+  const uint16_t *x;
+  float *lut;               // [batch][subs_per_batch][2^(g-1)]
+};
+
+template <int G>
+__global__ __launch_bounds__(256) void build_lut_kernel(const LutArgs a) {
+  constexpr int HALF = 1 << (G - 1);
+  const int64_t total = (int64_t)a.batch * a.subs_per_batch * HALF;
+  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total;
+       e += (int64_t)gridDim.x * blockDim.x) {
+    const int q = (int)(e % HALF);
+    const int64_t sub = (e / HALF) % a.subs_per_batch;
+    const int b = (int)(e / (HALF * a.subs_per_batch));
+    int s = 0;
+#pragma unroll
+    for (int i = 1; i < kMaxSeg; ++i)
+      if (i < a.nseg && sub >= a.sub0[i]) s = i;
+    const Seg &sg = a.seg[s];
+    const int64_t j = sub - a.sub0[s];
+    float v[G];
+#pragma unroll
+    for (int t = 0; t < G; ++t) {
+      const int64_t cc = j * G + t;
+      float val = 0.0f;
+      if (cc < sg.len) {
+        const int64_t xi = sg.salient ? (int64_t)a.sal_idx[cc] : cc;
+        val = h2f(sg.c[cc]) * h2f(a.x[(int64_t)b * a.k + xi]);
+      }
+      v[t] = val;
+    }
+    float t = v[G - 1];
+#pragma unroll
+    for (int i = 0; i < G - 1; ++i) t = ((q >> i) & 1) ? t + v[i] : t - v[i];
+    a.lut[e] = t;
+  }
+}
+
+// --------------------------------------------------------------------------
+// Packing, relayout and VCM gather (offline helpers, bit-exact)
+// --------------------------------------------------------------------------
+
+// One thread per output word.  layout 0 = row-major canonical, 1 = tiled.
+__global__ __launch_bounds__(256) void pack_kernel(const int8_t *signs, int64_t rows, int64_t cols, int64_t ld,
+                                                   int32_t layout, uint32_t *packed, uint32_t *invalid,
+                                                   int64_t total_words) {
+  const int64_t wpr = (cols + 31) / 32;
+  const int64_t nc = (cols + 127) / 128;
+  for (int64_t o = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; o < total_words;
+       o += (int64_t)gridDim.x * blockDim.x) {
+    int64_t r, w;
+    if (layout == 0) {
+      r = o / wpr;
+      w = o - r * wpr;
+    } else {
+      const int64_t q = o & 3, lane = (o >> 2) & 63, tc = o >> 8;  // tc = tile * nc + chunk
+      r = (tc / nc) * 64 + lane;
+      w = (tc % nc) * 4 + q;
+    }
+    uint32_t word = 0, bad = 0;
+    if (r < rows && w < wpr) {
+      const int8_t *p = signs + r * ld + w * 32;
+      const int lim = (int)min((int64_t)32, cols - w * 32);
+      for (int t = 0; t < lim; ++t) {
+        const int8_t s = p[t];
+        word |= (s == 1 ? 1u : 0u) << t;
+        bad += (s != 1 && s != -1) ? 1u : 0u;
+      }
+    }
+    packed[o] = word;
+    if (bad && invalid) atomicAdd(invalid, bad);
+  }
+}
+
+// One thread per destination word.
+__global__ __launch_bounds__(256) void relayout_kernel(const uint32_t *src, int64_t rows, int64_t cols,
+                                                       int32_t src_layout, int32_t dst_layout, uint32_t *dst,
+                                                       int64_t total_words) {
+  const int64_t wpr = (cols + 31) / 32;
+  const int64_t nc = (cols + 127) / 128;
+  for (int64_t o = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; o < total_words;
+       o += (int64_t)gridDim.x * blockDim.x) {
+    int64_t r, w;
+    if (dst_layout == 0) {
+      r = o / wpr;
+      w = o - r * wpr;
+    } else {
+      const int64_t q = o & 3, lane = (o >> 2) & 63, tc = o >> 8;
+      r = (tc / nc) * 64 + lane;
+      w = (tc % nc) * 4 + q;
+    }
+    uint32_t word = 0;
+    if (r < rows && w < wpr) {
+      const int64_t si = src_layout == 0 ? r * wpr + w : (((r / 64) * nc + w / 4) * 64 + (r % 64)) * 4 + (w % 4);
+      word = src[si];
+    }
+    dst[o] = word;
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void vcm_gather_values_kernel(const int32_t *idx, int64_t s, const T *src,
+                                                                int64_t rows, int64_t cols, T *dst, T fill) {
+  const int64_t total = rows * s;
+  for (int64_t o = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; o < total;
+       o += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = o / s, c = o - r * s;
+    const int32_t j = idx[c];
+    dst[o] = (j >= 0 && j < cols) ? src[r * cols + j] : fill;
+  }
+}
+
+__global__ __launch_bounds__(256) void vcm_gather_bits_kernel(const int32_t *idx, int64_t s, const uint32_t *src,
+                                                              int64_t rows, int64_t cols, uint32_t *dst) {
+  const int64_t wk = (cols + 31) / 32, ws = (s + 31) / 32;
+  const int64_t total = rows * ws;
+  for (int64_t o = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; o < total;
+       o += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = o / ws, w = o - r * ws;
+    uint32_t word = 0;
+    for (int t = 0; t < 32; ++t) {
+      const int64_t c = w * 32 + t;
+      if (c >= s) break;
+      const int32_t j = idx[c];
+      if (j >= 0 && j < cols) word |= ((src[r * wk + (j >> 5)] >> (j & 31)) & 1u) << t;
+    }
+    dst[o] = word;
+  }
+}
+
+// --------------------------------------------------------------------------
+// Dense fp16 GEMV (context kernel): one wave per row, 16-byte loads
+// --------------------------------------------------------------------------
+template <int NB>
+__global__ __launch_bounds__(256) void dense_f16_gemv_kernel(const uint16_t *w, int64_t n, int64_t k,
+                                                             const uint16_t *x, uint16_t *y, int batch) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= n) return;
+  float acc[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) acc[b] = 0.0f;
+  const u32x4 *wr = reinterpret_cast<const u32x4 *>(w + row * k);
+  const int64_t k8 = k / 8;
+  for (int64_t i = lane; i < k8; i += 64) {
+    const u32x4 wv = __builtin_nontemporal_load(wr + i);
+    float wf[8];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      wf[2 * q] = h2f((uint16_t)(wv[q] & 0xffffu));
+      wf[2 * q + 1] = h2f((uint16_t)(wv[q] >> 16));
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      if (b < batch) {
+        const u32x4 xv = *reinterpret_cast<const u32x4 *>(x + (int64_t)b * k + i * 8);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          acc[b] = fmaf(wf[2 * q], h2f((uint16_t)(xv[q] & 0xffffu)), acc[b]);
+          acc[b] = fmaf(wf[2 * q + 1], h2f((uint16_t)(xv[q] >> 16)), acc[b]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    float v = acc[b];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    if (lane == 0 && b < batch) y[(int64_t)b * n + row] = f2h(v);
+  }
+}
+
+}  // namespace fluxbin

@@ -1,0 +1,270 @@
+"""ctypes binding of libfluxbin.so (include/fluxbin.h): argument marshalling only.
+
+Every function here has the name and argument order of the C entry point it
+calls.  Array arguments may be torch CUDA tensors (their data pointers are
+passed), raw integer device addresses, or None for NULL.  `stream` defaults to
+torch's current stream.  A non-zero status raises FluxbinError.
+
+The library must have been built (``python -m binary_basis_lut_amd.build`` or
+``__graft_entry__.build()``); importing this module fails loudly otherwise.
+There is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+from pathlib import Path
+
+LIB_PATH = Path(__file__).resolve().parent / "_build" / "libfluxbin.so"
+if not LIB_PATH.exists():
+    raise ImportError(f"{LIB_PATH} is missing: build the HIP library first (binary_basis_lut_amd/build.py)")
+
+_lib = ctypes.CDLL(str(LIB_PATH))
+
+ABI_VERSION = 1
+
+OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
+LAYOUT_ROWMAJOR, LAYOUT_TILED = 0, 1
+DT_I8, DT_F16, DT_BITS = 0, 1, 2
+
+P = ctypes.c_void_p
+I64 = ctypes.c_int64
+I32 = ctypes.c_int32
+
+
+class LayerDesc(ctypes.Structure):
+    _fields_ = [
+        ("abi_version", I32), ("g", I32), ("kb", I32), ("ks", I32),
+        ("n", I64), ("k", I64), ("s", I64), ("max_batch", I64),
+        ("bits_global", P), ("r_global", P), ("c_global", P),
+        ("bits_sal", P), ("r_sal", P), ("c_sal", P), ("sal_idx", P),
+        ("workspace", P), ("workspace_bytes", ctypes.c_size_t),
+        ("chunks_per_block", I32), ("reserved", I32),
+    ]
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [
+        ("rows_per_block", I32), ("chunks_per_block", I32), ("row_blocks", I32), ("splits", I32),
+        ("total_chunks", I32), ("lds_bytes", I32), ("grid", I64),
+    ]
+
+    def as_dict(self):
+        return {name: getattr(self, name) for name, _ in self._fields_}
+
+
+class FluxbinError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = _lib.fluxbin_last_error().decode(errors="replace")
+        super().__init__(f"{where}: {_lib.fluxbin_status_string(status).decode()} ({msg})")
+
+
+def _decl(name, restype, argtypes):
+    fn = getattr(_lib, name)
+    fn.restype = restype
+    fn.argtypes = argtypes
+    return fn
+
+
+_decl("fluxbin_abi_version", I32, [])
+_decl("fluxbin_status_string", ctypes.c_char_p, [ctypes.c_int])
+_decl("fluxbin_last_error", ctypes.c_char_p, [])
+_decl("fluxbin_tiled_words", I64, [I64, I64])
+_decl("fluxbin_pack", ctypes.c_int, [P, I64, I64, I64, I32, P, P, P])
+_decl("fluxbin_relayout", ctypes.c_int, [P, I64, I64, I32, I32, P, P])
+_decl("fluxbin_vcm_gather", ctypes.c_int, [P, I64, P, I64, I64, I32, P, P])
+_decl("fluxbin_workspace_size", ctypes.c_int, [ctypes.POINTER(LayerDesc), ctypes.POINTER(ctypes.c_size_t)])
+_decl("fluxbin_create", ctypes.c_int, [ctypes.POINTER(LayerDesc), ctypes.POINTER(P)])
+_decl("fluxbin_destroy", ctypes.c_int, [P])
+_decl("fluxbin_get_plan", ctypes.c_int, [P, ctypes.POINTER(PlanInfo)])
+_decl("fluxbin_lut_size", ctypes.c_int, [P, I64, ctypes.POINTER(ctypes.c_size_t)])
+_decl("fluxbin_build_lut", ctypes.c_int, [P, P, I64, P, P])
+_decl("fluxbin_gemv", ctypes.c_int, [P, P, P, I64, P])
+_decl("fluxbin_dense_gemv_f16", ctypes.c_int, [P, I64, I64, P, P, I64, P])
+
+SYMBOLS = [
+    "fluxbin_abi_version", "fluxbin_status_string", "fluxbin_last_error", "fluxbin_tiled_words", "fluxbin_pack",
+    "fluxbin_relayout", "fluxbin_vcm_gather", "fluxbin_workspace_size", "fluxbin_create", "fluxbin_destroy",
+    "fluxbin_get_plan", "fluxbin_lut_size", "fluxbin_build_lut", "fluxbin_gemv", "fluxbin_dense_gemv_f16",
+]
+
+
+def _ptr(a):
+    if a is None:
+        return None
+    if isinstance(a, int):
+        return a
+    return a.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(st, where):
+    if st != OK:
+        raise FluxbinError(st, where)
+
+
+# ------------------------------------------------------------------ entry points
+
+def fluxbin_abi_version() -> int:
+    return int(_lib.fluxbin_abi_version())
+
+
+def fluxbin_status_string(status: int) -> str:
+    return _lib.fluxbin_status_string(status).decode()
+
+
+def fluxbin_last_error() -> str:
+    return _lib.fluxbin_last_error().decode(errors="replace")
+
+
+def fluxbin_tiled_words(rows: int, cols: int) -> int:
+    return int(_lib.fluxbin_tiled_words(rows, cols))
+
+
+def fluxbin_pack(signs, rows, cols, ld, layout, packed, invalid_count=None, stream=None):
+    _check(_lib.fluxbin_pack(_ptr(signs), rows, cols, ld, layout, _ptr(packed), _ptr(invalid_count),
+                             _stream(stream)), "fluxbin_pack")
+
+
+def fluxbin_relayout(src, rows, cols, src_layout, dst_layout, dst, stream=None):
+    _check(_lib.fluxbin_relayout(_ptr(src), rows, cols, src_layout, dst_layout, _ptr(dst), _stream(stream)),
+           "fluxbin_relayout")
+
+
+def fluxbin_vcm_gather(idx, s, src, rows, cols, dtype, dst, stream=None):
+    _check(_lib.fluxbin_vcm_gather(_ptr(idx), s, _ptr(src), rows, cols, dtype, _ptr(dst), _stream(stream)),
+           "fluxbin_vcm_gather")
+
+
+def fluxbin_workspace_size(desc: LayerDesc) -> int:
+    out = ctypes.c_size_t(0)
+    _check(_lib.fluxbin_workspace_size(ctypes.byref(desc), ctypes.byref(out)), "fluxbin_workspace_size")
+    return int(out.value)
+
+
+def fluxbin_create(desc: LayerDesc) -> int:
+    h = P()
+    _check(_lib.fluxbin_create(ctypes.byref(desc), ctypes.byref(h)), "fluxbin_create")
+    return int(h.value)
+
+
+def fluxbin_destroy(handle) -> None:
+    _check(_lib.fluxbin_destroy(handle), "fluxbin_destroy")
+
+
+def fluxbin_get_plan(handle) -> dict:
+    info = PlanInfo()
+    _check(_lib.fluxbin_get_plan(handle, ctypes.byref(info)), "fluxbin_get_plan")
+    return info.as_dict()
+
+
+def fluxbin_lut_size(handle, batch) -> int:
+    out = ctypes.c_size_t(0)
+    _check(_lib.fluxbin_lut_size(handle, batch, ctypes.byref(out)), "fluxbin_lut_size")
+    return int(out.value)
+
+
+def fluxbin_build_lut(handle, x, batch, lut, stream=None):
+    _check(_lib.fluxbin_build_lut(handle, _ptr(x), batch, _ptr(lut), _stream(stream)), "fluxbin_build_lut")
+
+
+def fluxbin_gemv(handle, x, y, batch, stream=None):
+    _check(_lib.fluxbin_gemv(handle, _ptr(x), _ptr(y), batch, _stream(stream)), "fluxbin_gemv")
+
+
+def fluxbin_dense_gemv_f16(w, n, k, x, y, batch, stream=None):
+    _check(_lib.fluxbin_dense_gemv_f16(_ptr(w), n, k, _ptr(x), _ptr(y), batch, _stream(stream)),
+           "fluxbin_dense_gemv_f16")
+
+
+def raw_status(name: str, *args) -> int:
+    """Call an entry point and return its status instead of raising (error-path tests)."""
+    return int(getattr(_lib, name)(*args))
+
+
+# ------------------------------------------------------------------ device-resident layer
+
+class DeviceLayer:
+    """Upload one synthetic layer (binary_basis_lut_amd.inputs.Layer) and create its handle.
+
+    Canonical sign words are copied to the device and converted to the tiled
+    layout with fluxbin_relayout; scales, index and workspace are torch CUDA
+    tensors owned by this object, which keeps them alive for the handle.
+    """
+
+    def __init__(self, layer, max_batch: int = 1, chunks_per_block: int = 0, device="cuda"):
+        import numpy as np
+        import torch
+
+        self.layer = layer
+        self.max_batch = max_batch
+        dev = torch.device(device)
+
+        def up(a, dtype):
+            return torch.from_numpy(np.ascontiguousarray(a).view(dtype)).to(dev)
+
+        n, k, s = layer.n, layer.k, layer.s
+        tw_g = fluxbin_tiled_words(n, k)
+        self.bits_g = torch.zeros(max(layer.kb * tw_g, 4), dtype=torch.int32, device=dev)
+        canon = up(layer.bits_g, np.int32)
+        for b in range(layer.kb):
+            fluxbin_relayout(canon[b], n, k, LAYOUT_ROWMAJOR, LAYOUT_TILED, self.bits_g[b * tw_g:(b + 1) * tw_g])
+        del canon
+        self.r_g = up(layer.r_g, np.int16)
+        self.c_g = up(layer.c_g, np.int16)
+        if layer.ks:
+            tw_s = fluxbin_tiled_words(n, s)
+            self.bits_s = torch.zeros(layer.ks * tw_s, dtype=torch.int32, device=dev)
+            canon_s = up(layer.bits_s, np.int32)
+            for b in range(layer.ks):
+                fluxbin_relayout(canon_s[b], n, s, LAYOUT_ROWMAJOR, LAYOUT_TILED,
+                                 self.bits_s[b * tw_s:(b + 1) * tw_s])
+            del canon_s
+            self.r_s = up(layer.r_s, np.int16)
+            self.c_s = up(layer.c_s, np.int16)
+            self.sal_idx = up(layer.sal_idx, np.int32)
+        else:
+            self.bits_s = self.r_s = self.c_s = self.sal_idx = None
+        desc = self.make_desc(chunks_per_block)
+        ws = fluxbin_workspace_size(desc)
+        self.workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev) if ws else None
+        desc.workspace = _ptr(self.workspace)
+        desc.workspace_bytes = ws
+        self.desc = desc
+        torch.cuda.synchronize()
+        self.handle = fluxbin_create(desc)
+        self.plan = fluxbin_get_plan(self.handle)
+
+    def make_desc(self, chunks_per_block: int = 0) -> LayerDesc:
+        L = self.layer
+        d = LayerDesc()
+        d.abi_version = ABI_VERSION
+        d.g, d.kb, d.ks = L.g, L.kb, L.ks
+        d.n, d.k, d.s, d.max_batch = L.n, L.k, L.s, self.max_batch
+        d.bits_global, d.r_global, d.c_global = _ptr(self.bits_g), _ptr(self.r_g), _ptr(self.c_g)
+        d.bits_sal, d.r_sal, d.c_sal, d.sal_idx = (_ptr(self.bits_s), _ptr(self.r_s), _ptr(self.c_s),
+                                                   _ptr(self.sal_idx))
+        d.chunks_per_block = chunks_per_block
+        return d
+
+    def gemv(self, x, y, batch=None, stream=None):
+        fluxbin_gemv(self.handle, x, y, x.shape[0] if batch is None else batch, stream)
+
+    def close(self):
+        if getattr(self, "handle", None):
+            fluxbin_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

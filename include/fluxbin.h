@@ -1,0 +1,207 @@
+/*
+ * fluxbin.h -- C ABI of libfluxbin.so: the FluxBin LUT GEMV on MI355X (gfx950).
+ *
+ * The library computes, for fp16 activations x[b] (b < batch),
+ *
+ *   y[b] = sum_{k<Kb} r_k (.) (B_k (c_k (.) x[b]))
+ *        + sum_{s<Ks} r_s (.) (B_s (c_s (.) x[b][S]))
+ *
+ * where (.) is the element-wise product, every B is a +-1 matrix stored as
+ * packed sign bits, r are per-row and c per-column fp16 scales, and S is the
+ * ordered list of salient columns.  This is the inference form of the
+ * decoupled row-column binary decomposition with salient-aware hybrid bases
+ * (FluxBin: Flexible LUT-based Ultra-low-bit LLM Inference by
+ * Algorithm-Kernel Synergy, paperlayer.ai summary, section 3 "Methodology",
+ * bullets "Quantization" and "Salient-Aware Hybrid Bases").
+ *
+ * The product is evaluated without reconstructing any floating-point weight:
+ * for every g-column sub-vector (g = 4 or 8) the kernel builds a table of the
+ * 2^g signed sums of the scale-fused inputs c (.) x, with the column scale
+ * folded into the table build; the g-bit pattern of a packed weight row is
+ * the table index; lookups accumulate in fp32 registers and the row scale is
+ * applied after accumulation (same summary, section 3 bullet "LUT-Based GEMV
+ * Kernel" and appendix C.1; the ainews.surl.tw article on FluxBin, paragraph
+ * on the execution layer).  The salient bases use the same kernel on the
+ * compact columns S, with x[S] gathered at run time (Virtual Columnar
+ * Mapping, same summary, section 3 bullet "Virtual Columnar Mapping").
+ *
+ * Conventions of every entry point
+ *   - All pointers to array data are DEVICE pointers (hipMalloc or torch
+ *     CUDA tensors), unless the comment says otherwise.  The caller owns all
+ *     memory.  Nothing is freed by the library except handle metadata.
+ *   - fp16 values are IEEE binary16 passed as raw uint16_t bits.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Launching calls
+ *     are asynchronous: they enqueue work and return.
+ *   - Every call returns fluxbin_status.  On an error nothing is launched,
+ *     outputs are left untouched and fluxbin_last_error() holds a
+ *     thread-local message.  Device faults surface at the caller's next
+ *     synchronisation.  No C++ exception crosses this boundary.
+ *   - fluxbin_gemv and fluxbin_build_lut launch exactly one kernel each and
+ *     never allocate, copy, set memory or synchronise, so they may be
+ *     captured in a HIP graph.  fluxbin_create does synchronise.
+ */
+#ifndef FLUXBIN_H
+#define FLUXBIN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FLUXBIN_ABI_VERSION 1
+
+typedef enum {
+  FLUXBIN_OK = 0,
+  FLUXBIN_ERR_INVALID_ARGUMENT = 1, /* bad pointer, size, alignment or index list */
+  FLUXBIN_ERR_UNSUPPORTED = 2,      /* valid request this build does not implement */
+  FLUXBIN_ERR_WORKSPACE = 3,        /* workspace missing or too small */
+  FLUXBIN_ERR_HIP = 4               /* a HIP runtime call failed */
+} fluxbin_status;
+
+/* Sign-word layouts.
+ *
+ * FLUXBIN_LAYOUT_ROWMAJOR (canonical): a +-1 matrix of `rows` x `cols` is
+ *   stored as uint32 words [rows][ceil(cols/32)].  Word w of row r holds
+ *   column 32w+t at bit t (least significant bit first).  Bit 1 means +1 and
+ *   bit 0 means -1 (the LUT Tensor Core notes, section 3.1.2, read weight
+ *   bits as {-1,+1}).  Padding bits past `cols` are 0.
+ *
+ * FLUXBIN_LAYOUT_TILED (what fluxbin_gemv streams): rows are padded to a
+ *   multiple of 64 and columns to a multiple of 128.  The canonical word
+ *   (row r, word w) is stored at index
+ *       ((floor(r/64) * NC + floor(w/4)) * 64 + (r mod 64)) * 4 + (w mod 4),
+ *   NC = ceil(cols/128); bits inside a word keep their canonical order and
+ *   padding words are 0.  One 64-row x 128-column tile is therefore 1 KiB of
+ *   contiguous memory in which lane l of a wave finds the 16 bytes of row l.
+ *   Size in words: fluxbin_tiled_words(rows, cols). */
+typedef enum { FLUXBIN_LAYOUT_ROWMAJOR = 0, FLUXBIN_LAYOUT_TILED = 1 } fluxbin_layout;
+
+/* Element kinds for fluxbin_vcm_gather. */
+typedef enum {
+  FLUXBIN_DT_I8 = 0,  /* int8 elements, [rows][cols] */
+  FLUXBIN_DT_F16 = 1, /* fp16 elements, [rows][cols] */
+  FLUXBIN_DT_BITS = 2 /* canonical sign words [rows][ceil(cols/32)] */
+} fluxbin_dtype;
+
+typedef struct fluxbin_layer *fluxbin_handle; /* opaque, immutable after create */
+
+/* Description of one linear layer.  The handle keeps the pointers (it does
+ * not copy the tensors): they must stay valid and unchanged for the handle's
+ * lifetime.  Segments are numbered: global bases 0..kb-1, then salient bases
+ * kb..kb+ks-1. */
+typedef struct {
+  int32_t abi_version;   /* must equal FLUXBIN_ABI_VERSION */
+  int32_t g;             /* table sub-vector length: 4 or 8 */
+  int32_t kb;            /* global bases, 1..4 */
+  int32_t ks;            /* salient bases, 0..2 */
+  int64_t n;             /* output rows, >= 1 */
+  int64_t k;             /* input columns, >= 1 */
+  int64_t s;             /* salient columns |S|: 0 when ks == 0, else 1..k */
+  int64_t max_batch;     /* largest batch a call may pass: 1..16 (g = 8: 1..4) */
+  const uint32_t *bits_global; /* TILED words, kb blocks of fluxbin_tiled_words(n, k), 16-B aligned */
+  const uint16_t *r_global;    /* fp16 [kb][n] row scales */
+  const uint16_t *c_global;    /* fp16 [kb][k] column scales */
+  const uint32_t *bits_sal;    /* TILED words, ks blocks of fluxbin_tiled_words(n, s), 16-B aligned */
+  const uint16_t *r_sal;       /* fp16 [ks][n] */
+  const uint16_t *c_sal;       /* fp16 [ks][s], compact order (entry c belongs to column sal_idx[c]) */
+  const int32_t *sal_idx;      /* [s] salient columns, strictly ascending, in [0, k) */
+  void *workspace;             /* >= fluxbin_workspace_size() bytes, 256-B aligned; may be NULL if that size is 0 */
+  size_t workspace_bytes;
+  int32_t chunks_per_block;    /* tuning: 0 = automatic, else 1, 2, 4 or 8 (128-column chunks per workgroup) */
+  int32_t reserved;            /* must be 0 */
+} fluxbin_layer_desc;
+
+/* How a handle splits the work (read-only introspection). */
+typedef struct {
+  int32_t rows_per_block;   /* output rows per workgroup (64 per wave) */
+  int32_t chunks_per_block; /* 128-column chunks per workgroup */
+  int32_t row_blocks;       /* workgroups along the rows */
+  int32_t splits;           /* workgroups along the concatenated columns of all segments */
+  int32_t total_chunks;     /* sum over segments of ceil(len/128) */
+  int32_t lds_bytes;        /* static LDS per workgroup at max_batch */
+  int64_t grid;             /* workgroups per fluxbin_gemv launch */
+} fluxbin_plan;
+
+int32_t fluxbin_abi_version(void);
+const char *fluxbin_status_string(fluxbin_status s);
+/* Thread-local description of the last error returned on this thread. */
+const char *fluxbin_last_error(void);
+
+/* Words of the TILED layout for a rows x cols sign matrix (host-side arithmetic). */
+int64_t fluxbin_tiled_words(int64_t rows, int64_t cols);
+
+/* Pack int8 signs [rows][ld] (first `cols` of each row used) into sign words
+ * in `layout`.  +1 sets a bit, -1 clears it.  Any other value is packed as a
+ * cleared bit and, when `invalid_count` (device uint32, caller-zeroed) is not
+ * NULL, adds 1 to it per such value.  `packed` must hold
+ * rows*ceil(cols/32) words (ROWMAJOR) or fluxbin_tiled_words(rows, cols)
+ * words (TILED); every word, padding included, is written.
+ * Bit order and sign meaning: see fluxbin_layout (the ainews.surl.tw article
+ * on FluxBin: weights streamed as compressed 32-bit words). */
+fluxbin_status fluxbin_pack(const int8_t *signs, int64_t rows, int64_t cols, int64_t ld, int32_t layout,
+                            uint32_t *packed, uint32_t *invalid_count, void *stream);
+
+/* Convert sign words of a rows x cols matrix between layouts (ROWMAJOR <->
+ * TILED, or a copy when they are equal).  src and dst must not overlap. */
+fluxbin_status fluxbin_relayout(const uint32_t *src, int64_t rows, int64_t cols, int32_t src_layout,
+                                int32_t dst_layout, uint32_t *dst, void *stream);
+
+/* Virtual Columnar Mapping gather (FluxBin summary, section 3 bullet "Virtual
+ * Columnar Mapping"): dst column c = src column idx[c], for c < s, of a
+ * [rows][cols] source.  DT_I8 / DT_F16: element matrices, dst [rows][s].
+ * DT_BITS: canonical sign words, src [rows][ceil(cols/32)], dst
+ * [rows][ceil(s/32)] with zero padding bits.  idx entries must lie in
+ * [0, cols) (checked on the device: out-of-range entries gather 0 / -1).
+ * Used offline to build the compact salient bases and scales; fluxbin_gemv
+ * gathers x[S] itself. */
+fluxbin_status fluxbin_vcm_gather(const int32_t *idx, int64_t s, const void *src, int64_t rows, int64_t cols,
+                                  int32_t dtype, void *dst, void *stream);
+
+/* Workspace bytes a layer needs (host-side arithmetic, no device access). */
+fluxbin_status fluxbin_workspace_size(const fluxbin_layer_desc *d, size_t *bytes);
+
+/* Validate the description (copies sal_idx to the host to check it), zero the
+ * workspace's reduction counters, and return a handle.  Synchronises the
+ * device; not capturable.  The environment variable FLUXBIN_FAULT=launch,
+ * read here, makes every launching call of this handle fail with
+ * FLUXBIN_ERR_HIP before launching (error-path testing). */
+fluxbin_status fluxbin_create(const fluxbin_layer_desc *d, fluxbin_handle *out);
+fluxbin_status fluxbin_destroy(fluxbin_handle h);
+fluxbin_status fluxbin_get_plan(fluxbin_handle h, fluxbin_plan *plan);
+
+/* Floats fluxbin_build_lut writes for `batch` rows:
+ * batch * (kb*ceil(k/g) + ks*ceil(s/g)) * 2^(g-1). */
+fluxbin_status fluxbin_lut_size(fluxbin_handle h, int64_t batch, size_t *floats);
+
+/* Scale-fused half tables (FluxBin summary, section 3 bullet "LUT-Based GEMV
+ * Kernel" and appendix C.1; halving by the symmetry LUT[~p] = -LUT[p] of the
+ * LUT Tensor Core notes, section 3.1.2).  x: fp16 [batch][k].  lut: float
+ * [batch][segment][ceil(L/g)][2^(g-1)] with segments in handle order and L
+ * the segment's width (k or s).  Entry q of sub-vector j is the table value
+ * for pattern q | 2^(g-1):  v_{g-1} + sum_{t<g-1} (2*bit_t(q) - 1) * v_t,
+ * v_t = c[jg+t] * x[jg+t] (global) or c_s[jg+t] * x[S[jg+t]] (salient),
+ * v_t = 0 past L.  fluxbin_gemv builds the same tables itself, in LDS; this
+ * call exposes them. */
+fluxbin_status fluxbin_build_lut(fluxbin_handle h, const uint16_t *x, int64_t batch, float *lut, void *stream);
+
+/* y = the layer applied to x.  x: fp16 [batch][k], y: fp16 [batch][n]
+ * (round to nearest even), 0 <= batch <= max_batch (0 launches nothing).
+ * Uses the handle's workspace: at most one call per handle may be in flight
+ * at a time (use one handle per concurrent stream).  For a given handle the
+ * result of row b does not depend on the other rows of the batch, and
+ * repeated calls give bitwise identical y. */
+fluxbin_status fluxbin_gemv(fluxbin_handle h, const uint16_t *x, uint16_t *y, int64_t batch, void *stream);
+
+/* Context kernel, not part of the method: dense fp16 y = W x with fp32
+ * accumulation.  w: fp16 [n][k] row-major (16-B aligned, k a multiple of 8),
+ * x: fp16 [batch][k], y: fp16 [batch][n], 1 <= batch <= 16. */
+fluxbin_status fluxbin_dense_gemv_f16(const uint16_t *w, int64_t n, int64_t k, const uint16_t *x, uint16_t *y,
+                                      int64_t batch, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLUXBIN_H */

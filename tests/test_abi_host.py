@@ -1,0 +1,141 @@
+"""The C-ABI library loads, exports what include/fluxbin.h declares, and validates on the host.
+
+No test here launches a kernel or needs a GPU: every call below is rejected
+by host-side validation before any HIP runtime call, or is pure host
+arithmetic.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fluxbin.h")
+
+
+@pytest.fixture(scope="module")
+def fb():
+    from binary_basis_lut_amd import build as B
+    if B.is_stale():
+        B.build()
+    from binary_basis_lut_amd import fluxbin
+    return fluxbin
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fluxbin_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(fb):
+    names = declared_functions()
+    assert len(names) >= 15
+    lib = ctypes.CDLL(str(fb.LIB_PATH))
+    for name in names:
+        assert hasattr(lib, name), name
+    assert sorted(fb.SYMBOLS) == names
+
+
+def test_abi_version_and_strings(fb):
+    assert fb.fluxbin_abi_version() == fb.ABI_VERSION == 1
+    assert fb.fluxbin_status_string(fb.OK) == "ok"
+    assert "invalid" in fb.fluxbin_status_string(fb.ERR_INVALID_ARGUMENT)
+    assert fb.fluxbin_status_string(99) == "unknown status"
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 1), (64, 128), (65, 129), (4096, 4096), (57344, 8192), (0, 5)])
+def test_tiled_words(fb, rows, cols):
+    expect = 0 if rows == 0 else -(-rows // 64) * -(-cols // 128) * 256
+    assert fb.fluxbin_tiled_words(rows, cols) == expect
+
+
+def good_desc(fb, **kw):
+    d = fb.LayerDesc()
+    d.abi_version = fb.ABI_VERSION
+    d.g, d.kb, d.ks = 4, 2, 1
+    d.n, d.k, d.s, d.max_batch = 4096, 4096, 256, 1
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+def ws_status(fb, d):
+    out = ctypes.c_size_t(0)
+    return fb.raw_status("fluxbin_workspace_size", ctypes.byref(d), ctypes.byref(out)), out.value
+
+
+def test_workspace_size_matches_plan_arithmetic(fb):
+    st, ws = ws_status(fb, good_desc(fb))
+    assert st == fb.OK
+    # 66 chunks of 128 columns (2 x 32 global + 2 salient), 64 row tiles in 16 row blocks of 4 waves
+    row_blocks, total_chunks = 16, 66
+    cpb = 8
+    while cpb > 1 and row_blocks * -(-total_chunks // cpb) < 512:
+        cpb //= 2
+    splits = -(-total_chunks // cpb)
+    partial = -(-(splits * 1 * 4096 * 4) // 256) * 256
+    assert ws == partial + row_blocks * 128
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("abi_version", 2, 1), ("g", 3, 2), ("g", 16, 2), ("kb", 0, 2), ("kb", 5, 2), ("ks", 3, 2), ("ks", -1, 2),
+    ("n", 0, 1), ("k", 0, 1), ("s", 0, 1), ("s", 5000, 1), ("max_batch", 0, 2), ("max_batch", 17, 2),
+    ("chunks_per_block", 3, 1), ("reserved", 1, 1),
+])
+def test_workspace_size_rejects(fb, field, value, status):
+    st, _ = ws_status(fb, good_desc(fb, **{field: value}))
+    assert st == status, fb.fluxbin_last_error()
+    assert fb.fluxbin_last_error()
+
+
+def test_g8_batch_limit_and_salient_flags(fb):
+    assert ws_status(fb, good_desc(fb, g=8, max_batch=4))[0] == fb.OK
+    assert ws_status(fb, good_desc(fb, g=8, max_batch=5))[0] == fb.ERR_UNSUPPORTED
+    assert ws_status(fb, good_desc(fb, ks=0, s=0))[0] == fb.OK
+    assert ws_status(fb, good_desc(fb, ks=0, s=8))[0] == fb.ERR_INVALID_ARGUMENT
+    assert ws_status(fb, good_desc(fb, chunks_per_block=8, max_batch=8))[0] == fb.ERR_UNSUPPORTED
+
+
+def test_create_rejects_before_touching_the_device(fb):
+    h = ctypes.c_void_p()
+    d = good_desc(fb)  # all pointers NULL
+    assert fb.raw_status("fluxbin_create", ctypes.byref(d), ctypes.byref(h)) == fb.ERR_INVALID_ARGUMENT
+    assert "non-NULL" in fb.fluxbin_last_error()
+    d.bits_global = d.r_global = d.c_global = 0x1000
+    d.bits_sal = d.r_sal = d.c_sal = d.sal_idx = 0x2000
+    d.bits_global = 0x1004  # misaligned
+    assert fb.raw_status("fluxbin_create", ctypes.byref(d), ctypes.byref(h)) == fb.ERR_INVALID_ARGUMENT
+    assert "aligned" in fb.fluxbin_last_error()
+    d.bits_global = 0x1000
+    d.workspace = None
+    assert fb.raw_status("fluxbin_create", ctypes.byref(d), ctypes.byref(h)) == fb.ERR_WORKSPACE
+    assert fb.raw_status("fluxbin_create", None, ctypes.byref(h)) == fb.ERR_INVALID_ARGUMENT
+    assert not h.value
+
+
+def test_launching_calls_reject_bad_arguments_on_the_host(fb):
+    s = fb.raw_status
+    assert s("fluxbin_gemv", None, 0x1000, 0x2000, 1, None) == fb.ERR_INVALID_ARGUMENT
+    assert s("fluxbin_build_lut", None, 0x1000, 1, 0x2000, None) == fb.ERR_INVALID_ARGUMENT
+    assert s("fluxbin_destroy", None) == fb.ERR_INVALID_ARGUMENT
+    assert s("fluxbin_get_plan", None, None) == fb.ERR_INVALID_ARGUMENT
+    assert s("fluxbin_pack", 0x1000, -1, 5, 5, 0, 0x2000, None, None) == fb.ERR_INVALID_ARGUMENT
+    assert s("fluxbin_pack", 0x1000, 5, 5, 5, 7, 0x2000, None, None) == fb.ERR_INVALID_ARGUMENT
+    assert s("fluxbin_pack", 0x1000, 5, 10, 5, 0, 0x2000, None, None) == fb.ERR_INVALID_ARGUMENT  # ld < cols
+    assert s("fluxbin_pack", None, 5, 5, 5, 0, 0x2000, None, None) == fb.ERR_INVALID_ARGUMENT
+    assert s("fluxbin_relayout", 0x1000, 5, 5, 0, 3, 0x2000, None) == fb.ERR_INVALID_ARGUMENT
+    assert s("fluxbin_relayout", 0x1000, 5, 5, 0, 1, 0x1000, None) == fb.ERR_INVALID_ARGUMENT  # overlap
+    assert s("fluxbin_vcm_gather", 0x1000, 4, 0x2000, 5, 5, 9, 0x3000, None) == fb.ERR_INVALID_ARGUMENT
+    assert s("fluxbin_vcm_gather", None, 4, 0x2000, 5, 5, 1, 0x3000, None) == fb.ERR_INVALID_ARGUMENT
+    assert s("fluxbin_dense_gemv_f16", 0x1000, 8, 12, 0x2000, 0x3000, 1, None) == fb.ERR_UNSUPPORTED
+    assert s("fluxbin_dense_gemv_f16", 0x1000, 8, 16, 0x2000, 0x3000, 17, None) == fb.ERR_UNSUPPORTED
+    assert s("fluxbin_dense_gemv_f16", 0x1001, 8, 16, 0x2000, 0x3000, 1, None) == fb.ERR_INVALID_ARGUMENT
+
+
+def test_empty_work_is_a_no_op(fb):
+    s = fb.raw_status
+    assert s("fluxbin_pack", None, 0, 5, 5, 0, None, None, None) == fb.OK
+    assert s("fluxbin_relayout", None, 5, 0, 0, 1, None, None) == fb.OK
+    assert s("fluxbin_vcm_gather", None, 0, None, 5, 5, 1, None, None) == fb.OK
