@@ -181,36 +181,25 @@ gemv_fn pick_gemv(int g, int nb, int cpb) {
   return nullptr;
 }
 
-void fill_segments(const fluxbin_layer_desc &d, Seg *seg, int32_t *nseg) {
-  int32_t chunk0 = 0, ns = 0;
-  const int64_t tw_g = fluxbin_tiled_words(d.n, d.k);
-  for (int b = 0; b < d.kb; ++b, ++ns) {
-    Seg &s = seg[ns];
-    s.bits = reinterpret_cast<const u32x4 *>(d.bits_global + (int64_t)b * tw_g);
-    s.c = d.c_global + (int64_t)b * d.k;
-    s.r = d.r_global + (int64_t)b * d.n;
-    s.len = (int32_t)d.k;
-    s.nchunks = (int32_t)cdiv(d.k, kChunkCols);
-    s.chunk0 = chunk0;
-    s.salient = 0;
-    chunk0 += s.nchunks;
-  }
-  if (d.ks > 0) {
-    const int64_t tw_s = fluxbin_tiled_words(d.n, d.s);
-    for (int b = 0; b < d.ks; ++b, ++ns) {
-      Seg &s = seg[ns];
-      s.bits = reinterpret_cast<const u32x4 *>(d.bits_sal + (int64_t)b * tw_s);
-      s.c = d.c_sal + (int64_t)b * d.s;
-      s.r = d.r_sal + (int64_t)b * d.n;
-      s.len = (int32_t)d.s;
-      s.nchunks = (int32_t)cdiv(d.s, kChunkCols);
-      s.chunk0 = chunk0;
-      s.salient = 1;
-      chunk0 += s.nchunks;
-    }
-  }
-  for (int i = ns; i < kMaxSeg; ++i) seg[i] = Seg{nullptr, nullptr, nullptr, 0, 0, 1 << 30, 0};
-  *nseg = ns;
+LayerArgs layer_args(const fluxbin_layer_desc &d) {
+  LayerArgs L;
+  L.bits_g = reinterpret_cast<const u32x4 *>(d.bits_global);
+  L.bits_s = reinterpret_cast<const u32x4 *>(d.ks > 0 ? d.bits_sal : d.bits_global);
+  L.c_g = d.c_global;
+  L.c_s = d.ks > 0 ? d.c_sal : d.c_global;
+  L.r_g = d.r_global;
+  L.r_s = d.ks > 0 ? d.r_sal : d.r_global;
+  L.sal_idx = d.ks > 0 ? d.sal_idx : nullptr;
+  L.tv_g = fluxbin_tiled_words(d.n, d.k) / 4;
+  L.tv_s = d.ks > 0 ? fluxbin_tiled_words(d.n, d.s) / 4 : 0;
+  L.n = d.n;
+  L.k = d.k;
+  L.s = d.s;
+  L.kb = d.kb;
+  L.ks = d.ks;
+  L.nc_g = (int32_t)cdiv(d.k, kChunkCols);
+  L.nc_s = d.ks > 0 ? (int32_t)cdiv(d.s, kChunkCols) : 1;
+  return L;
 }
 
 int grid_for(int64_t items, int per_thread_block = 256) {
@@ -405,19 +394,13 @@ fluxbin_status fluxbin_build_lut(fluxbin_handle h, const uint16_t *x, int64_t ba
   if (h->fault_launch) return fail(FLUXBIN_ERR_HIP, "injected launch fault (FLUXBIN_FAULT=launch)");
   const fluxbin_layer_desc &d = h->d;
   LutArgs a;
-  int32_t nseg;
-  fill_segments(d, a.seg, &nseg);
-  a.nseg = nseg;
+  a.L = layer_args(d);
   a.g = d.g;
-  int64_t sub = 0;
-  for (int i = 0; i < kMaxSeg; ++i) {
-    a.sub0[i] = i < nseg ? sub : ((int64_t)1 << 62);
-    if (i < nseg) sub += cdiv(a.seg[i].len, d.g);
-  }
-  a.subs_per_batch = sub;
-  a.k = d.k;
   a.batch = (int32_t)batch;
-  a.sal_idx = d.sal_idx;
+  a.sub_g = cdiv(d.k, d.g);
+  a.sub_s = d.ks > 0 ? cdiv(d.s, d.g) : 1;
+  const int64_t sub = d.kb * a.sub_g + (d.ks > 0 ? d.ks * a.sub_s : 0);
+  a.subs_per_batch = sub;
   a.x = x;
   a.lut = lut;
   const int64_t total = batch * sub * ((int64_t)1 << (d.g - 1));
@@ -443,18 +426,13 @@ fluxbin_status fluxbin_gemv(fluxbin_handle h, const uint16_t *x, uint16_t *y, in
   gemv_fn fn = pick_gemv(d.g, p.nb, p.cpb);
   if (!fn) return fail(FLUXBIN_ERR_UNSUPPORTED, "no kernel for g = %d, nb = %d, cpb = %d", d.g, p.nb, p.cpb);
   GemvArgs a;
-  int32_t nseg;
-  fill_segments(d, a.seg, &nseg);
-  a.nseg = nseg;
+  a.L = layer_args(d);
   a.total_chunks = p.total_chunks;
   a.row_tiles = p.row_tiles;
   a.row_blocks = p.row_blocks;
   a.splits = p.splits;
   a.batch = (int32_t)batch;
-  a.n = d.n;
-  a.k = d.k;
   a.n_pad = p.n_pad;
-  a.sal_idx = d.sal_idx;
   a.x = x;
   a.y = y;
   a.partials = p.splits > 1 ? reinterpret_cast<float *>(d.workspace) : nullptr;

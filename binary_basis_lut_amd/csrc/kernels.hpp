@@ -27,7 +27,8 @@
 //   * splits > 1: each workgroup writes fp32 partial sums; the last workgroup
 //     of a row block to finish (agent-scope atomic counter) adds them in split
 //     order, writes fp16 y and re-arms the counter, so one launch does the
-//     whole GEMV and the result is bitwise deterministic.
+//     whole GEMV and the result is bitwise deterministic.  Nothing waits on
+//     another workgroup: every workgroup runs to completion unconditionally.
 #pragma once
 
 #include <hip/hip_fp16.h>
@@ -43,28 +44,75 @@ constexpr int kTileRows = 64;    // rows per tile = one wave, one row per lane
 constexpr int kMaxSeg = 6;       // kb <= 4 global + ks <= 2 salient bases
 constexpr int kCounterStride = 32;  // uint32 per reduction counter (128-byte spacing)
 
-struct Seg {
-  const u32x4 *bits;    // tiled words; element ((tile * nchunks + chunk) * 64 + lane)
-  const uint16_t *c;    // fp16 column scales [len]
-  const uint16_t *r;    // fp16 row scales [n]
-  int32_t len;          // columns of this segment (k or s)
-  int32_t nchunks;      // ceil(len / 128)
-  int32_t chunk0;       // first chunk of the segment in the concatenated chunk space
-  int32_t salient;      // 1: activation of compact column c is x[sal_idx[c]]
+// The segments of one layer (kb global bases over k columns, then ks salient
+// bases over s compact columns), addressed arithmetically: the descriptor of
+// any chunk or segment follows from these scalars without further loads.
+struct LayerArgs {
+  const u32x4 *bits_g;  // tiled words of global basis b at bits_g + b * tv_g
+  const u32x4 *bits_s;  // tiled words of salient basis b at bits_s + b * tv_s
+  const uint16_t *c_g;  // fp16 [kb][k]
+  const uint16_t *c_s;  // fp16 [ks][s], compact order
+  const uint16_t *r_g;  // fp16 [kb][n]
+  const uint16_t *r_s;  // fp16 [ks][n]
+  const int32_t *sal_idx;
+  int64_t tv_g, tv_s;   // 16-byte elements per tiled segment block
+  int64_t n, k, s;
+  int32_t kb, ks;
+  int32_t nc_g, nc_s;   // 128-column chunks per global / salient segment
 };
 
+// One segment as seen by the kernels.
+struct SegRef {
+  const u32x4 *bits;    // element ((tile * nchunks + chunk) * 64 + lane)
+  const uint16_t *c;
+  const uint16_t *r;
+  int64_t len;
+  int32_t nchunks;
+  int32_t salient;
+};
+
+__device__ __forceinline__ SegRef segment(const LayerArgs &L, int sidx) {
+  SegRef r;
+  if (sidx < L.kb) {
+    r.bits = L.bits_g + sidx * L.tv_g;
+    r.c = L.c_g + sidx * L.k;
+    r.r = L.r_g + sidx * L.n;
+    r.len = L.k;
+    r.nchunks = L.nc_g;
+    r.salient = 0;
+  } else {
+    const int b = sidx - L.kb;
+    r.bits = L.bits_s + b * L.tv_s;
+    r.c = L.c_s + b * L.s;
+    r.r = L.r_s + b * L.n;
+    r.len = L.s;
+    r.nchunks = L.nc_s;
+    r.salient = 1;
+  }
+  return r;
+}
+
+// Segment of chunk gc of the concatenated chunk space, and the chunk's index inside it.
+__device__ __forceinline__ int seg_of(const LayerArgs &L, int gc, int *cis) {
+  const int gch = L.kb * L.nc_g;
+  if (gc < gch) {
+    const int b = gc / L.nc_g;
+    *cis = gc - b * L.nc_g;
+    return b;
+  }
+  const int b = (gc - gch) / L.nc_s;
+  *cis = gc - gch - b * L.nc_s;
+  return L.kb + b;
+}
+
 struct GemvArgs {
-  Seg seg[kMaxSeg];
-  int32_t nseg;
+  LayerArgs L;
   int32_t total_chunks;
   int32_t row_tiles;
   int32_t row_blocks;
   int32_t splits;
   int32_t batch;
-  int64_t n;
-  int64_t k;
   int64_t n_pad;          // row_tiles * 64
-  const int32_t *sal_idx;
   const uint16_t *x;      // fp16 [batch][k]
   uint16_t *y;            // fp16 [batch][n]
   float *partials;        // [splits][batch][n_pad]
@@ -73,15 +121,6 @@ struct GemvArgs {
 
 __device__ __forceinline__ float h2f(uint16_t h) { return __half2float(__ushort_as_half(h)); }
 __device__ __forceinline__ uint16_t f2h(float f) { return __half_as_ushort(__float2half_rn(f)); }
-
-// Segment owning global chunk gc (uniform across the workgroup).
-__device__ __forceinline__ int seg_of(const GemvArgs &a, int gc) {
-  int s = 0;
-#pragma unroll
-  for (int i = 1; i < kMaxSeg; ++i)
-    if (i < a.nseg && gc >= a.seg[i].chunk0) s = i;
-  return s;
-}
 
 // Value number s of six scalars (s uniform).  Plain SSA values, never an
 // aggregate: an array or struct indexed by a runtime segment number would be
@@ -152,68 +191,145 @@ __global__ __launch_bounds__(WAVES * 64) void lut_gemv_kernel(const GemvArgs a) 
   __shared__ float s_v[CPB * NB * kChunkCols];   // [chunk][batch][column] scale-fused inputs
   __shared__ int s_last;
 
+  const LayerArgs &L = a.L;
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
   const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar address arithmetic
   const int rb = blockIdx.x % a.row_blocks;
   const int sp = blockIdx.x / a.row_blocks;
   const int tile = rb * WAVES + wave;
   const bool tile_ok = tile < a.row_tiles;
-  const int64_t row = (int64_t)tile * kTileRows + lane;
-  const bool row_ok = tile_ok && row < a.n;
+  const int ltile = min(tile, a.row_tiles - 1);  // waves past the last tile read the last one, store nothing
+  const int row = tile * kTileRows + lane;
+  const bool row_ok = tile_ok && row < L.n;
+  const int rrow = row_ok ? row : 0;
   const int c0 = sp * CPB;
   const int nch = min(CPB, a.total_chunks - c0);
 
-  // 1. stream this lane's 16 bytes of every chunk (issued first: longest latency)
-  u32x4 w[CPB];
+  // Segment and chunk-in-segment of each of the workgroup's chunks (uniform).
+  // Chunks past the range repeat the last one: a redundant load, never used.
+  int cseg[CPB], ccis[CPB];
+  {
+    int cis;
+    int sg = seg_of(L, c0, &cis);
+#pragma unroll
+    for (int ch = 0; ch < CPB; ++ch) {
+      cseg[ch] = sg;
+      ccis[ch] = cis;
+      if (ch + 1 < nch) {
+        ++cis;
+        if (cis == (sg < L.kb ? L.nc_g : L.nc_s)) {
+          cis = 0;
+          ++sg;
+        }
+      }
+    }
+  }
+  const int s_first = cseg[0];
+  const int s_lastseg = cseg[CPB - 1];
+  const bool any_salient = s_lastseg >= L.kb;  // segments run global first, then salient
+
+  // 1. Loads.  Inputs of the table build go first so that waiting for them
+  //    (loads retire in order) does not wait for the weight stream.  Every
+  //    load is unconditional from a valid address and dead items are zeroed
+  //    by a select, so all loads of a phase are in flight together.
+  constexpr int VPC = (NB * kChunkCols + NT - 1) / NT;  // v items per thread per chunk
+  bool vlive[CPB][VPC];
+  uint16_t vc[CPB][VPC];   // fp16 column scale
+  uint16_t vxv[CPB][VPC];  // fp16 activation
+  u32x4 w[CPB];            // this lane's 16 bytes of every chunk
+  int64_t xrow[CPB][VPC];  // b * k
+  int32_t xcol[CPB][VPC];  // column of x (gathered through sal_idx on salient segments)
 #pragma unroll
   for (int ch = 0; ch < CPB; ++ch) {
-    w[ch] = u32x4{0u, 0u, 0u, 0u};
-    if (ch < nch && tile_ok) {
-      const int gc = c0 + ch;
-      const Seg &sg = a.seg[seg_of(a, gc)];
-      const int cis = gc - sg.chunk0;
-      w[ch] = __builtin_nontemporal_load(sg.bits + ((int64_t)tile * sg.nchunks + cis) * kTileRows + lane);
+    const SegRef sg = segment(L, cseg[ch]);
+#pragma unroll
+    for (int i = 0; i < VPC; ++i) {
+      const int e = tid + i * NT;
+      const int b = e / kChunkCols;
+      const int cc = ccis[ch] * kChunkCols + (e & (kChunkCols - 1));
+      // non-short-circuit: a select, not a branch
+      const bool live = (ch < nch) & (e < NB * kChunkCols) & (b < a.batch) & (cc < sg.len);
+      vlive[ch][i] = live;
+      xrow[ch][i] = live ? (int64_t)b * L.k : 0;
+      xcol[ch][i] = live ? cc : 0;
+      vc[ch][i] = sg.c[xcol[ch][i]];
     }
   }
-  // row scales of the segments this workgroup touches
-  const int s_first = seg_of(a, c0);
-  const int s_lastseg = seg_of(a, c0 + nch - 1);
-  auto rload = [&](int s) -> float {
-    return (row_ok && s >= s_first && s <= s_lastseg) ? h2f(a.seg[s].r[row]) : 0.0f;
+  auto stream_weights = [&]() {
+#pragma unroll
+    for (int ch = 0; ch < CPB; ++ch) {
+      const SegRef sg = segment(L, cseg[ch]);
+      const u32x4 *base = sg.bits + ((int64_t)ltile * sg.nchunks + ccis[ch]) * kTileRows;
+      w[ch] = __builtin_nontemporal_load(base + lane);
+    }
   };
-  const float rv0 = rload(0), rv1 = rload(1), rv2 = rload(2), rv3 = rload(3), rv4 = rload(4), rv5 = rload(5);
+  if (!any_salient) {
+    // global chunks only: activations, then the weight stream
+#pragma unroll
+    for (int ch = 0; ch < CPB; ++ch)
+#pragma unroll
+      for (int i = 0; i < VPC; ++i) vxv[ch][i] = a.x[xrow[ch][i] + xcol[ch][i]];
+    stream_weights();
+  } else {
+    // some chunk is salient: gather indices first (VCM), then activations, then weights
+#pragma unroll
+    for (int ch = 0; ch < CPB; ++ch) {
+      const bool sal = cseg[ch] >= L.kb;
+#pragma unroll
+      for (int i = 0; i < VPC; ++i) {
+        const int32_t gi = L.sal_idx[sal ? xcol[ch][i] : 0];
+        xcol[ch][i] = sal ? gi : xcol[ch][i];
+      }
+    }
+#pragma unroll
+    for (int ch = 0; ch < CPB; ++ch)
+#pragma unroll
+      for (int i = 0; i < VPC; ++i) vxv[ch][i] = a.x[xrow[ch][i] + xcol[ch][i]];
+    stream_weights();
+  }
+  // row scales of the segments this workgroup touches (s_first .. s_lastseg, consecutive)
+  auto rptr = [&](int j) -> const uint16_t * { return segment(L, min(s_first + j, s_lastseg)).r + rrow; };
+  const uint16_t rr0 = *rptr(0), rr1 = *rptr(1), rr2 = *rptr(2), rr3 = *rptr(3), rr4 = *rptr(4), rr5 = *rptr(5);
 
   // 2. scale-fused inputs v = c * x (exact in fp32: product of two fp16 values)
-  for (int e = tid; e < nch * NB * kChunkCols; e += NT) {
-    const int ch = e / (NB * kChunkCols);
-    const int rem = e - ch * (NB * kChunkCols);
-    const int b = rem / kChunkCols;
-    const int col = rem - b * kChunkCols;
-    const int gc = c0 + ch;
-    const Seg &sg = a.seg[seg_of(a, gc)];
-    const int64_t cc = (int64_t)(gc - sg.chunk0) * kChunkCols + col;
-    float v = 0.0f;
-    if (b < a.batch && cc < sg.len) {
-      const int64_t xi = sg.salient ? (int64_t)a.sal_idx[cc] : cc;
-      v = h2f(sg.c[cc]) * h2f(a.x[(int64_t)b * a.k + xi]);
+#pragma unroll
+  for (int ch = 0; ch < CPB; ++ch)
+#pragma unroll
+    for (int i = 0; i < VPC; ++i) {
+      const int e = tid + i * NT;
+      if (e < NB * kChunkCols) s_v[ch * NB * kChunkCols + e] = vlive[ch][i] ? h2f(vc[ch][i]) * h2f(vxv[ch][i]) : 0.0f;
     }
-    s_v[(ch * NB + b) * kChunkCols + col] = v;
-  }
+  const float rv0 = h2f(rr0), rv1 = h2f(rr1), rv2 = h2f(rr2), rv3 = h2f(rr3), rv4 = h2f(rr4), rv5 = h2f(rr5);
   __syncthreads();
 
-  // 3. tables: the half with the top input at +1 is summed, the rest negated
-  for (int e = tid; e < nch * NB * SUB * HALF; e += NT) {
-    const int q = e % HALF;
-    const int j = (e / HALF) % SUB;
-    const int cb = e / (HALF * SUB);  // chunk * NB + batch row
-    const float *v = &s_v[cb * kChunkCols + j * G];
-    float t = v[G - 1];
+  // 3. tables: the half with the top input at +1 is summed, the rest negated.
+  //    Entry q of a sub-vector is v_{G-1} + sum_{i<G-1} sgn_i(q) * v_i in that
+  //    order; sgn_i = +-1 exactly, so each fma rounds like the add or subtract.
+  //    NT is a multiple of HALF, so a thread's pattern q (and its signs) is the
+  //    same in every iteration.
+  static_assert(NT % HALF == 0, "thread count must be a multiple of the half-table size");
+  constexpr int TITEMS = (CPB * NB * SUB * HALF + NT - 1) / NT;
+  {
+    const int q = tid & (HALF - 1);
+    float sgn[G - 1];
 #pragma unroll
-    for (int i = 0; i < G - 1; ++i) t = ((q >> i) & 1) ? t + v[i] : t - v[i];
-    float *tb = &s_tab[(cb * SUB + j) * TAB];
-    tb[q | HALF] = t;
-    tb[(HALF - 1) ^ q] = -t;
+    for (int i = 0; i < G - 1; ++i) sgn[i] = ((q >> i) & 1) ? 1.0f : -1.0f;
+#pragma unroll
+    for (int it = 0; it < TITEMS; ++it) {
+      const int e = tid + it * NT;
+      if (e < nch * NB * SUB * HALF) {
+        const int j = (e / HALF) & (SUB - 1);
+        const int cb = e / (HALF * SUB);  // chunk * NB + batch row
+        const float *v = &s_v[cb * kChunkCols + j * G];
+        float t = v[G - 1];
+#pragma unroll
+        for (int i = 0; i < G - 1; ++i) t = fmaf(sgn[i], v[i], t);
+        float *tb = &s_tab[(cb * SUB + j) * TAB];
+        tb[q | HALF] = t;
+        tb[(HALF - 1) ^ q] = -t;
+      }
+    }
   }
   __syncthreads();
 
@@ -225,9 +341,9 @@ __global__ __launch_bounds__(WAVES * 64) void lut_gemv_kernel(const GemvArgs a) 
 #pragma unroll
   for (int ch = 0; ch < CPB; ++ch) {
     if (ch < nch) {
-      const int s = seg_of(a, c0 + ch);
+      const int s = cseg[ch];
       if (s != cur) {
-        const float rc = pick6(cur, rv0, rv1, rv2, rv3, rv4, rv5);
+        const float rc = pick6(cur - s_first, rv0, rv1, rv2, rv3, rv4, rv5);
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
           part[b] += rc * acc[b];
@@ -241,7 +357,7 @@ __global__ __launch_bounds__(WAVES * 64) void lut_gemv_kernel(const GemvArgs a) 
     }
   }
   {
-    const float rc = pick6(cur, rv0, rv1, rv2, rv3, rv4, rv5);
+    const float rc = pick6(cur - s_first, rv0, rv1, rv2, rv3, rv4, rv5);
 #pragma unroll
     for (int b = 0; b < NB; ++b) part[b] += rc * acc[b];
   }
@@ -251,10 +367,23 @@ __global__ __launch_bounds__(WAVES * 64) void lut_gemv_kernel(const GemvArgs a) 
     if (row_ok) {
 #pragma unroll
       for (int b = 0; b < NB; ++b)
-        if (b < a.batch) a.y[(int64_t)b * a.n + row] = f2h(part[b]);
+        if (b < a.batch) a.y[(int64_t)b * L.n + row] = f2h(part[b]);
     }
     return;
   }
+  // splits > 1: publish the fp32 partials, count arrivals per row block; the
+  // last workgroup to arrive adds the partials in split order.
+  //
+  // Cross-workgroup visibility (workgroups of one row block run on different
+  // XCDs, whose L2 caches are not coherent with each other): the partials are
+  // only ever written and read with agent-scope atomic operations, which the
+  // compiler encodes with the device-coherent cache policy.  The writer waits
+  // until its stores have completed before the arrival counter is incremented,
+  // and the last arriver reads only after the counter told it so.  That is
+  // the ordering a release/acquire pair provides; the L2 write-back and
+  // invalidate that an agent-scope release/acquire would add serve plain
+  // (non-atomic) data, which this protocol does not use, and measured several
+  // times the cost of the whole GEMV.
   if (tile_ok) {
 #pragma unroll
     for (int b = 0; b < NB; ++b)
@@ -262,23 +391,31 @@ __global__ __launch_bounds__(WAVES * 64) void lut_gemv_kernel(const GemvArgs a) 
         __hip_atomic_store(&a.partials[((int64_t)sp * a.batch + b) * a.n_pad + row], part[b], __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
   }
-  __threadfence();
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores have completed
   __syncthreads();
   if (tid == 0) {
     const uint32_t prev =
-        __hip_atomic_fetch_add(&a.counters[rb * kCounterStride], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_add(&a.counters[rb * kCounterStride], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     s_last = (prev == (uint32_t)(a.splits - 1));
   }
   __syncthreads();
   if (!s_last) return;
-  __threadfence();
   if (row_ok) {
+    const int64_t stride = (int64_t)a.batch * a.n_pad;
     for (int b = 0; b < a.batch; ++b) {
+      const float *pp = a.partials + (int64_t)b * a.n_pad + row;
       float sum = 0.0f;
-      for (int p = 0; p < a.splits; ++p)
-        sum += __hip_atomic_load(&a.partials[((int64_t)p * a.batch + b) * a.n_pad + row], __ATOMIC_RELAXED,
-                                 __HIP_MEMORY_SCOPE_AGENT);
-      a.y[(int64_t)b * a.n + row] = f2h(sum);
+      int p = 0;
+      for (; p + 16 <= a.splits; p += 16) {  // sixteen loads in flight, summed in split order
+        float t[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u)
+          t[u] = __hip_atomic_load(pp + (int64_t)(p + u) * stride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+        for (int u = 0; u < 16; ++u) sum += t[u];
+      }
+      for (; p < a.splits; ++p) sum += __hip_atomic_load(pp + (int64_t)p * stride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      a.y[(int64_t)b * L.n + row] = f2h(sum);
     }
   }
   if (tid == 0) __hip_atomic_store(&a.counters[rb * kCounterStride], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -288,14 +425,11 @@ __global__ __launch_bounds__(WAVES * 64) void lut_gemv_kernel(const GemvArgs a) 
 // Half tables to global memory (the exported table builder)
 // --------------------------------------------------------------------------
 struct LutArgs {
-  Seg seg[kMaxSeg];
-  int32_t nseg;
+  LayerArgs L;
   int32_t g;
-  int64_t subs_per_batch;   // sum over segments of ceil(len/g)
-  int64_t sub0[kMaxSeg];    // first sub-vector of each segment within a batch row
-  int64_t k;
   int32_t batch;
-  const int32_t *sal_idx;
+  int64_t sub_g, sub_s;     // sub-vectors per global / salient segment: ceil(len/g)
+  int64_t subs_per_batch;   // kb * sub_g + ks * sub_s
   const uint16_t *x;
   float *lut;               // [batch][subs_per_batch][2^(g-1)]
 };
@@ -303,26 +437,25 @@ struct LutArgs {
 template <int G>
 __global__ __launch_bounds__(256) void build_lut_kernel(const LutArgs a) {
   constexpr int HALF = 1 << (G - 1);
+  const LayerArgs &L = a.L;
   const int64_t total = (int64_t)a.batch * a.subs_per_batch * HALF;
   for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total;
        e += (int64_t)gridDim.x * blockDim.x) {
     const int q = (int)(e % HALF);
     const int64_t sub = (e / HALF) % a.subs_per_batch;
     const int b = (int)(e / (HALF * a.subs_per_batch));
-    int s = 0;
-#pragma unroll
-    for (int i = 1; i < kMaxSeg; ++i)
-      if (i < a.nseg && sub >= a.sub0[i]) s = i;
-    const Seg &sg = a.seg[s];
-    const int64_t j = sub - a.sub0[s];
+    const int64_t gsubs = L.kb * a.sub_g;
+    const int sidx = sub < gsubs ? (int)(sub / a.sub_g) : L.kb + (int)((sub - gsubs) / a.sub_s);
+    const int64_t j = sub < gsubs ? sub - (int64_t)sidx * a.sub_g : sub - gsubs - (int64_t)(sidx - L.kb) * a.sub_s;
+    const SegRef sg = segment(L, sidx);
     float v[G];
 #pragma unroll
     for (int t = 0; t < G; ++t) {
       const int64_t cc = j * G + t;
       float val = 0.0f;
       if (cc < sg.len) {
-        const int64_t xi = sg.salient ? (int64_t)a.sal_idx[cc] : cc;
-        val = h2f(sg.c[cc]) * h2f(a.x[(int64_t)b * a.k + xi]);
+        const int64_t xi = sg.salient ? (int64_t)L.sal_idx[cc] : cc;
+        val = h2f(sg.c[cc]) * h2f(a.x[(int64_t)b * L.k + xi]);
       }
       v[t] = val;
     }
