@@ -54,8 +54,7 @@ struct Plan {
   int32_t total_chunks;
   int32_t splits;
   int64_t n_pad;
-  size_t partial_bytes;
-  size_t counter_bytes;
+  size_t acc_bytes;    // packed split-reduction words (splits > 1)
 };
 
 int32_t pow2_at_least(int64_t v) {
@@ -117,12 +116,15 @@ fluxbin_status make_plan(const fluxbin_layer_desc *d, Plan *p) {
     p->cpb = d->chunks_per_block;
   } else {
     p->cpb = cmax;
-    while (p->cpb > 1 && (int64_t)p->row_blocks * cdiv(p->total_chunks, p->cpb) < kTargetBlocks) p->cpb >>= 1;
+    while (p->cpb > 1 && (int64_t)p->row_blocks * cdiv(p->total_chunks, p->cpb) < kTargetBlocks &&
+           cdiv(p->total_chunks, p->cpb / 2) <= kMaxSplits)
+      p->cpb >>= 1;
   }
   p->splits = (int32_t)cdiv(p->total_chunks, p->cpb);
-  p->partial_bytes = p->splits > 1 ? (size_t)p->splits * d->max_batch * p->n_pad * sizeof(float) : 0;
-  p->partial_bytes = (p->partial_bytes + 255) / 256 * 256;
-  p->counter_bytes = p->splits > 1 ? (size_t)p->row_blocks * kCounterStride * sizeof(uint32_t) : 0;
+  if (p->splits > kMaxSplits)
+    return fail(FLUXBIN_ERR_UNSUPPORTED, "%d column splits exceed %d (too many 128-column chunks for chunks_per_block %d)",
+                p->splits, kMaxSplits, p->cpb);
+  p->acc_bytes = p->splits > 1 ? (size_t)d->max_batch * p->n_pad * sizeof(uint64_t) : 0;
   return FLUXBIN_OK;
 }
 
@@ -301,7 +303,7 @@ fluxbin_status fluxbin_workspace_size(const fluxbin_layer_desc *d, size_t *bytes
   Plan p;
   st = make_plan(d, &p);
   if (st) return st;
-  *bytes = p.partial_bytes + p.counter_bytes;
+  *bytes = p.acc_bytes;
   return ok();
 }
 
@@ -320,7 +322,7 @@ fluxbin_status fluxbin_create(const fluxbin_layer_desc *d, fluxbin_handle *out) 
   Plan p;
   st = make_plan(d, &p);
   if (st) return st;
-  const size_t need = p.partial_bytes + p.counter_bytes;
+  const size_t need = p.acc_bytes;
   if (need > 0) {
     if (!d->workspace || d->workspace_bytes < need)
       return fail(FLUXBIN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
@@ -340,9 +342,9 @@ fluxbin_status fluxbin_create(const fluxbin_layer_desc *d, fluxbin_handle *out) 
         return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "sal_idx not strictly ascending at %lld", (long long)i);
     }
   }
-  if (p.counter_bytes) {
-    hipError_t e = hipMemset((char *)d->workspace + p.partial_bytes, 0, p.counter_bytes);
-    if (e != hipSuccess) return hip_fail(e, "zeroing reduction counters");
+  if (p.acc_bytes) {
+    hipError_t e = hipMemset(d->workspace, 0, p.acc_bytes);
+    if (e != hipSuccess) return hip_fail(e, "zeroing the split-reduction words");
     e = hipDeviceSynchronize();
     if (e != hipSuccess) return hip_fail(e, "synchronising after create");
   }
@@ -435,8 +437,7 @@ fluxbin_status fluxbin_gemv(fluxbin_handle h, const uint16_t *x, uint16_t *y, in
   a.n_pad = p.n_pad;
   a.x = x;
   a.y = y;
-  a.partials = p.splits > 1 ? reinterpret_cast<float *>(d.workspace) : nullptr;
-  a.counters = p.splits > 1 ? reinterpret_cast<uint32_t *>((char *)d.workspace + p.partial_bytes) : nullptr;
+  a.acc = p.splits > 1 ? reinterpret_cast<uint64_t *>(d.workspace) : nullptr;
   const int64_t grid = (int64_t)p.row_blocks * p.splits;
   hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(kWaves * 64), 0, (hipStream_t)stream, a);
   hipError_t e = hipGetLastError();

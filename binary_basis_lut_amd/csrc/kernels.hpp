@@ -24,11 +24,11 @@
 //   * a workgroup of WAVES waves shares the tables of CPB consecutive chunks of
 //     the concatenated column space of all segments; a grid of
 //     row_blocks x splits workgroups covers the layer;
-//   * splits > 1: each workgroup writes fp32 partial sums; the last workgroup
-//     of a row block to finish (agent-scope atomic counter) adds them in split
-//     order, writes fp16 y and re-arms the counter, so one launch does the
-//     whole GEMV and the result is bitwise deterministic.  Nothing waits on
-//     another workgroup: every workgroup runs to completion unconditionally.
+//   * splits > 1: each workgroup adds its fp32 partial of every row, as an
+//     exact fixed-point integer, into a per-row 64-bit word that also counts
+//     arrivals; the lane whose atomic brings the last contribution writes the
+//     fp16 row.  One launch does the whole GEMV, the result is bitwise
+//     deterministic, and no workgroup ever waits for another.
 #pragma once
 
 #include <hip/hip_fp16.h>
@@ -42,7 +42,19 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kChunkCols = 128;  // columns per chunk = 4 sign words per row
 constexpr int kTileRows = 64;    // rows per tile = one wave, one row per lane
 constexpr int kMaxSeg = 6;       // kb <= 4 global + ks <= 2 salient bases
-constexpr int kCounterStride = 32;  // uint32 per reduction counter (128-byte spacing)
+// Split reduction: one 64-bit word per (batch row, output row) holds the
+// number of contributions so far (top 8 bits) and the sum of the
+// contributions' biased fixed-point values (low 56 bits).  Each contribution
+// is round(partial * 2^30), clamped to |.| < 2^47, plus a bias of 2^47, so it
+// lies in [0, 2^48) and up to 255 of them never carry into the count.
+constexpr int kCountShift = 56;
+constexpr int kMaxSplits = 255;
+constexpr uint64_t kOneArrival = 1ull << kCountShift;
+constexpr uint64_t kValueMask = kOneArrival - 1;
+constexpr int64_t kFixBias = 1ll << 47;
+constexpr float kFixScale = 1073741824.0f;          // 2^30
+constexpr float kFixInv = 1.0f / 1073741824.0f;     // 2^-30
+constexpr float kFixClamp = 140737479966720.0f;     // 2^47 - 2^23, the largest float below 2^47
 
 // The segments of one layer (kb global bases over k columns, then ks salient
 // bases over s compact columns), addressed arithmetically: the descriptor of
@@ -115,8 +127,7 @@ struct GemvArgs {
   int64_t n_pad;          // row_tiles * 64
   const uint16_t *x;      // fp16 [batch][k]
   uint16_t *y;            // fp16 [batch][n]
-  float *partials;        // [splits][batch][n_pad]
-  uint32_t *counters;     // [row_blocks * kCounterStride]
+  uint64_t *acc;          // [batch][n_pad] packed (arrivals, fixed-point sum); zero between calls
 };
 
 __device__ __forceinline__ float h2f(uint16_t h) { return __half2float(__ushort_as_half(h)); }
@@ -189,7 +200,6 @@ __global__ __launch_bounds__(WAVES * 64) void lut_gemv_kernel(const GemvArgs a) 
   constexpr int WPL = kChunkCols / 32;  // words per lane per chunk (4)
   __shared__ float s_tab[CPB * NB * SUB * TAB];  // [chunk][batch][sub-vector][pattern]
   __shared__ float s_v[CPB * NB * kChunkCols];   // [chunk][batch][column] scale-fused inputs
-  __shared__ int s_last;
 
   const LayerArgs &L = a.L;
   const int tid = threadIdx.x;
@@ -371,54 +381,33 @@ __global__ __launch_bounds__(WAVES * 64) void lut_gemv_kernel(const GemvArgs a) 
     }
     return;
   }
-  // splits > 1: publish the fp32 partials, count arrivals per row block; the
-  // last workgroup to arrive adds the partials in split order.
+  // splits > 1: every workgroup adds its partial sum of each row into that
+  // row's packed word with one agent-scope atomic (performed at the memory
+  // side, coherent across XCDs).  The atomic returns the previous word, so the
+  // lane that brings the last of `splits` contributions knows it is last and
+  // holds the complete sum: it writes y and clears the word for the next call.
+  // No workgroup waits for another, and since integer addition is exact the
+  // result does not depend on the order in which the splits arrive.
   //
-  // Cross-workgroup visibility (workgroups of one row block run on different
-  // XCDs, whose L2 caches are not coherent with each other): the partials are
-  // only ever written and read with agent-scope atomic operations, which the
-  // compiler encodes with the device-coherent cache policy.  The writer waits
-  // until its stores have completed before the arrival counter is incremented,
-  // and the last arriver reads only after the counter told it so.  That is
-  // the ordering a release/acquire pair provides; the L2 write-back and
-  // invalidate that an agent-scope release/acquire would add serve plain
-  // (non-atomic) data, which this protocol does not use, and measured several
-  // times the cost of the whole GEMV.
-  if (tile_ok) {
-#pragma unroll
-    for (int b = 0; b < NB; ++b)
-      if (b < a.batch)
-        __hip_atomic_store(&a.partials[((int64_t)sp * a.batch + b) * a.n_pad + row], part[b], __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-  }
-  __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores have completed
-  __syncthreads();
-  if (tid == 0) {
-    const uint32_t prev =
-        __hip_atomic_fetch_add(&a.counters[rb * kCounterStride], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = (prev == (uint32_t)(a.splits - 1));
-  }
-  __syncthreads();
-  if (!s_last) return;
+  // The fixed-point step quantises each partial to 2^-31 (absolute) and
+  // saturates partials beyond +-2^17, twice the largest fp16 output.
   if (row_ok) {
-    const int64_t stride = (int64_t)a.batch * a.n_pad;
-    for (int b = 0; b < a.batch; ++b) {
-      const float *pp = a.partials + (int64_t)b * a.n_pad + row;
-      float sum = 0.0f;
-      int p = 0;
-      for (; p + 16 <= a.splits; p += 16) {  // sixteen loads in flight, summed in split order
-        float t[16];
 #pragma unroll
-        for (int u = 0; u < 16; ++u)
-          t[u] = __hip_atomic_load(pp + (int64_t)(p + u) * stride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-#pragma unroll
-        for (int u = 0; u < 16; ++u) sum += t[u];
+    for (int b = 0; b < NB; ++b) {
+      if (b < a.batch) {
+        const float scaled = fminf(fmaxf(part[b] * kFixScale, -kFixClamp), kFixClamp);
+        const uint64_t contrib = (uint64_t)(__float2ll_rn(scaled) + kFixBias);
+        uint64_t *slot = a.acc + (int64_t)b * a.n_pad + row;
+        const uint64_t old =
+            __hip_atomic_fetch_add(slot, contrib + kOneArrival, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if ((int)(old >> kCountShift) == a.splits - 1) {
+          const int64_t total = (int64_t)((old & kValueMask) + contrib) - (int64_t)a.splits * kFixBias;
+          a.y[(int64_t)b * L.n + row] = f2h(__ll2float_rn(total) * kFixInv);
+          __hip_atomic_store(slot, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
       }
-      for (; p < a.splits; ++p) sum += __hip_atomic_load(pp + (int64_t)p * stride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      a.y[(int64_t)b * L.n + row] = f2h(sum);
     }
   }
-  if (tid == 0) __hip_atomic_store(&a.counters[rb * kCounterStride], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // --------------------------------------------------------------------------

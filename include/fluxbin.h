@@ -163,7 +163,7 @@ fluxbin_status fluxbin_vcm_gather(const int32_t *idx, int64_t s, const void *src
 fluxbin_status fluxbin_workspace_size(const fluxbin_layer_desc *d, size_t *bytes);
 
 /* Validate the description (copies sal_idx to the host to check it), zero the
- * workspace's reduction counters, and return a handle.  Synchronises the
+ * workspace's split-reduction words, and return a handle.  Synchronises the
  * device; not capturable.  The environment variable FLUXBIN_FAULT=launch,
  * read here, makes every launching call of this handle fail with
  * FLUXBIN_ERR_HIP before launching (error-path testing). */
@@ -188,6 +188,10 @@ fluxbin_status fluxbin_build_lut(fluxbin_handle h, const uint16_t *x, int64_t ba
 
 /* y = the layer applied to x.  x: fp16 [batch][k], y: fp16 [batch][n]
  * (round to nearest even), 0 <= batch <= max_batch (0 launches nothing).
+ * Tables and accumulation are fp32.  When the handle's plan splits the
+ * columns over several workgroups (fluxbin_plan.splits > 1), the partial
+ * sums of a row are combined exactly as 2^-30 fixed-point integers: each
+ * partial is rounded to 2^-31 (absolute) and partials beyond +-2^17 saturate.
  * Uses the handle's workspace: at most one call per handle may be in flight
  * at a time (use one handle per concurrent stream).  For a given handle the
  * result of row b does not depend on the other rows of the batch, and

@@ -69,14 +69,20 @@ def ws_status(fb, d):
 def test_workspace_size_matches_plan_arithmetic(fb):
     st, ws = ws_status(fb, good_desc(fb))
     assert st == fb.OK
-    # 66 chunks of 128 columns (2 x 32 global + 2 salient), 64 row tiles in 16 row blocks of 4 waves
-    row_blocks, total_chunks = 16, 66
-    cpb = 8
-    while cpb > 1 and row_blocks * -(-total_chunks // cpb) < 512:
-        cpb //= 2
-    splits = -(-total_chunks // cpb)
-    partial = -(-(splits * 1 * 4096 * 4) // 256) * 256
-    assert ws == partial + row_blocks * 128
+    # 66 chunks of 128 columns (2 x 32 global + 2 salient) over 16 row blocks: split, so one
+    # packed 64-bit reduction word per (batch row, padded output row)
+    assert ws == 1 * 4096 * 8
+    st, ws = ws_status(fb, good_desc(fb, max_batch=4, n=100))
+    assert st == fb.OK and ws == 4 * 128 * 8
+    # a single 128-column chunk needs no split and no workspace
+    st, ws = ws_status(fb, good_desc(fb, k=128, ks=0, s=0, kb=1))
+    assert st == fb.OK and ws == 0
+
+
+def test_too_many_splits_is_unsupported(fb):
+    # 255 splits at most: 2 x ceil(2^17 / 128) chunks with one chunk per workgroup is too many
+    st, _ = ws_status(fb, good_desc(fb, k=1 << 17, ks=0, s=0, chunks_per_block=1))
+    assert st == fb.ERR_UNSUPPORTED
 
 
 @pytest.mark.parametrize("field,value,status", [
