@@ -1,0 +1,93 @@
+"""Profiling driver: replay one workload shape through fluxbin_gemv, or run a plain device copy.
+
+Used under rocprofv3 to produce the kernel-trace and counter summaries kept in
+profiles/ (each summary names the exact command).  Two modes:
+
+  python3 -m binary_basis_lut_amd.profile_workload gemv --workload 2 --shape 0 --sets 256 --reps 2
+      builds `sets` distinct weight sets of the shape (resident in HBM, more
+      than the 256 MB Infinity Cache for the q_proj shape), captures one call
+      per set in a HIP graph and replays it `reps` times;
+
+  python3 -m binary_basis_lut_amd.profile_workload copy --bytes 1073741824 --reps 4
+      a plain device-to-device copy of known size (torch's copy kernel): the
+      reference that scales the FETCH_SIZE / WRITE_SIZE counters to bytes.
+"""
+from __future__ import annotations
+
+import argparse
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def run_gemv(args) -> None:
+    import numpy as np
+    import torch
+
+    from binary_basis_lut_amd import fluxbin as F
+    from binary_basis_lut_amd import inputs as I
+
+    dls, xs, ys = [], [], []
+    for i in range(args.sets):
+        lay = I.workload_layer(args.workload, args.shape, i)
+        x = I.workload_x(args.workload, lay, args.batch, args.shape, i)
+        dls.append(F.DeviceLayer(lay, max_batch=args.batch, chunks_per_block=args.chunks_per_block))
+        xs.append(torch.from_numpy(x.view(np.int16)).cuda())
+        ys.append(torch.empty((args.batch, lay.n), dtype=torch.int16, device="cuda"))
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        for i in range(args.sets):
+            dls[i].gemv(xs[i], ys[i], stream=stream)
+    stream.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(graph, stream=stream):
+            for i in range(args.sets):
+                dls[i].gemv(xs[i], ys[i], stream=stream)
+    torch.cuda.synchronize()
+    for _ in range(args.reps):
+        graph.replay()
+    torch.cuda.synchronize()
+    print(f"gemv workload {args.workload} shape {args.shape}: {args.sets} sets x {args.reps} replays, "
+          f"plan {dls[0].plan}", flush=True)
+    for d in dls:
+        d.close()
+
+
+def run_copy(args) -> None:
+    import torch
+
+    n = args.bytes // 4
+    src = torch.ones(n, dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(args.reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"copy: {args.reps} x {n * 4} bytes read and written", flush=True)
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    sub = ap.add_subparsers(dest="mode", required=True)
+    g = sub.add_parser("gemv")
+    g.add_argument("--workload", type=int, default=2)
+    g.add_argument("--shape", type=int, default=0)
+    g.add_argument("--sets", type=int, default=256)
+    g.add_argument("--reps", type=int, default=2)
+    g.add_argument("--batch", type=int, default=1)
+    g.add_argument("--chunks-per-block", type=int, default=0)
+    c = sub.add_parser("copy")
+    c.add_argument("--bytes", type=int, default=1 << 30)
+    c.add_argument("--reps", type=int, default=4)
+    args = ap.parse_args()
+    (run_gemv if args.mode == "gemv" else run_copy)(args)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
