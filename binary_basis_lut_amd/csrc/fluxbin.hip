@@ -43,12 +43,13 @@ bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-constexpr int kWaves = 4;          // waves per workgroup of the GEMV kernel
-constexpr int kTargetBlocks = 512; // enough workgroups for two per CU on 256 CUs
+constexpr int kTargetBlocks = 1024;  // about four workgroups per CU
 
 struct Plan {
+  int32_t waves;       // waves per workgroup (64 rows each)
   int32_t nb;          // compiled batch width (power of two >= max_batch)
   int32_t cpb;         // chunks per workgroup
+  int32_t pf;          // chunks of weights in flight per wave (2 or 8)
   int32_t row_tiles;
   int32_t row_blocks;
   int32_t total_chunks;
@@ -63,19 +64,7 @@ int32_t pow2_at_least(int64_t v) {
   return p;
 }
 
-// Largest chunks-per-workgroup whose tables fit the LDS budget of one workgroup.
-int32_t max_cpb(int32_t g, int32_t nb) {
-  const int32_t limit = g == 4 ? 32 : 4;  // CPB * NB: 64 KiB of tables either way
-  int32_t c = 8;
-  while (c > 1 && c * nb > limit) c >>= 1;
-  return c;
-}
 
-int32_t lds_bytes(int32_t g, int32_t nb, int32_t cpb) {
-  const int32_t tab = cpb * nb * (kChunkCols / g) * (1 << g) * 4;
-  const int32_t v = cpb * nb * kChunkCols * 4;
-  return tab + v + 16;
-}
 
 fluxbin_status validate_shape(const fluxbin_layer_desc *d) {
   if (!d) return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "desc is NULL");
@@ -95,31 +84,53 @@ fluxbin_status validate_shape(const fluxbin_layer_desc *d) {
   if (d->max_batch < 1 || d->max_batch > maxb)
     return fail(FLUXBIN_ERR_UNSUPPORTED, "max_batch = %lld (supported for g = %d: 1..%lld)",
                 (long long)d->max_batch, d->g, (long long)maxb);
-  if (d->chunks_per_block != 0 && d->chunks_per_block != 1 && d->chunks_per_block != 2 &&
-      d->chunks_per_block != 4 && d->chunks_per_block != 8)
-    return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "chunks_per_block = %d (0, 1, 2, 4 or 8)", d->chunks_per_block);
-  if (d->reserved != 0) return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "reserved field must be 0");
+  if (d->chunks_per_block < 0 || d->chunks_per_block > kMaxCpb)
+    return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "chunks_per_block = %d (0 = automatic, else 1..%d)", d->chunks_per_block,
+                kMaxCpb);
+  if (d->waves_per_block != 0 && d->waves_per_block != 4 && d->waves_per_block != 8)
+    return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "waves_per_block = %d (0, 4 or 8)", d->waves_per_block);
   return FLUXBIN_OK;
+}
+
+// Chunks per workgroup: about kTargetBlocks workgroups in all (measured on
+// MI355X over 4096..57344-row layers: fewer, longer ranges amortise the
+// table build, more workgroups hide latency), at least 2 chunks, a power of
+// two up to 8 and a multiple of 8 above (the prefetch depths), within the
+// LDS and register budget (cmax) and the split limit.
+int32_t auto_cpb(int32_t cmax, int32_t waves, int64_t row_tiles, int32_t total_chunks) {
+  int64_t c = (int64_t)row_tiles * total_chunks / ((int64_t)waves * kTargetBlocks);
+  c = std::max<int64_t>(c, 2);
+  if (c <= 8) {
+    int64_t p = 1;
+    while (p * 2 <= c) p *= 2;
+    c = p;
+  } else {
+    c = c / 8 * 8;
+  }
+  c = std::max<int64_t>(c, cdiv(total_chunks, kMaxSplits));
+  if (c > 8) c = cdiv(c, 8) * 8;
+  return (int32_t)std::max<int64_t>(1, std::min<int64_t>(c, cmax));
 }
 
 fluxbin_status make_plan(const fluxbin_layer_desc *d, Plan *p) {
   p->nb = pow2_at_least(d->max_batch);
-  const int32_t cmax = max_cpb(d->g, p->nb);
   p->row_tiles = (int32_t)cdiv(d->n, kTileRows);
-  p->row_blocks = (int32_t)cdiv(p->row_tiles, kWaves);
   p->n_pad = (int64_t)p->row_tiles * kTileRows;
   p->total_chunks = (int32_t)(d->kb * cdiv(d->k, kChunkCols) + d->ks * cdiv(d->s, kChunkCols));
-  if (d->chunks_per_block) {
-    if (d->chunks_per_block > cmax)
-      return fail(FLUXBIN_ERR_UNSUPPORTED, "chunks_per_block = %d exceeds %d for g = %d, max_batch = %lld",
-                  d->chunks_per_block, cmax, d->g, (long long)d->max_batch);
-    p->cpb = d->chunks_per_block;
+  if (d->waves_per_block) {
+    p->waves = d->waves_per_block;
   } else {
-    p->cpb = cmax;
-    while (p->cpb > 1 && (int64_t)p->row_blocks * cdiv(p->total_chunks, p->cpb) < kTargetBlocks &&
-           cdiv(p->total_chunks, p->cpb / 2) <= kMaxSplits)
-      p->cpb >>= 1;
+    // eight waves (512 rows) halve the per-row share of the table build: for
+    // the large g = 8 tables, and for very tall layers (measured on MI355X)
+    p->waves = (d->g == 8 || p->row_tiles >= 512) ? 8 : 4;
   }
+  const int32_t cmax = cpb_cap(d->g, p->nb, p->waves);
+  if (d->chunks_per_block > cmax)
+    return fail(FLUXBIN_ERR_UNSUPPORTED, "chunks_per_block = %d exceeds %d for g = %d, max_batch = %lld, %d waves",
+                d->chunks_per_block, cmax, d->g, (long long)d->max_batch, p->waves);
+  p->row_blocks = (int32_t)cdiv(p->row_tiles, p->waves);
+  p->cpb = d->chunks_per_block ? d->chunks_per_block : auto_cpb(cmax, p->waves, p->row_tiles, p->total_chunks);
+  p->pf = prefetch_depth(p->cpb);
   p->splits = (int32_t)cdiv(p->total_chunks, p->cpb);
   if (p->splits > kMaxSplits)
     return fail(FLUXBIN_ERR_UNSUPPORTED, "%d column splits exceed %d (too many 128-column chunks for chunks_per_block %d)",
@@ -130,54 +141,53 @@ fluxbin_status make_plan(const fluxbin_layer_desc *d, Plan *p) {
 
 }  // namespace
 
+typedef void (*gemv_fn)(const GemvArgs);
+
 struct fluxbin_layer {
   fluxbin_layer_desc d;
   Plan plan;
+  gemv_fn fn;                 // kernel instance for (g, batch width, waves)
+  size_t lds;                 // its dynamic LDS bytes
+  const int32_t *idx_or_dummy;  // sal_idx, or the library's one-element zero array when ks == 0
   bool fault_launch;
 };
+
+// A valid index array for layers without salient bases: the GEMV reads its
+// entry 0 (and ignores it) where a salient chunk would read its gather index.
+__device__ int32_t g_zero_index[4];
 
 // ---------------------------------------------------------------------------
 // launch table for the GEMV kernel
 // ---------------------------------------------------------------------------
 namespace {
 
-typedef void (*gemv_fn)(const GemvArgs);
-
-// Instances whose tables exceed the LDS budget (CPB * NB * table bytes > 64 KiB) are not built.
-template <int G, int NB, int CPB>
-gemv_fn instance() {
-  if constexpr (CPB * NB <= (G == 4 ? 32 : 4)) {
-    return lut_gemv_kernel<G, NB, CPB, kWaves>;
-  } else {
-    return nullptr;
-  }
+template <int G, int NB, int W>
+gemv_fn pick_pf(int pf) {
+  return pf == 8 ? lut_gemv_kernel<G, NB, W, 8>
+         : pf == 4 ? lut_gemv_kernel<G, NB, W, 4>
+         : pf == 2 ? lut_gemv_kernel<G, NB, W, 2>
+                   : nullptr;
 }
 
 template <int G, int NB>
-gemv_fn pick_cpb(int cpb) {
-  switch (cpb) {
-    case 1: return instance<G, NB, 1>();
-    case 2: return instance<G, NB, 2>();
-    case 4: return instance<G, NB, 4>();
-    case 8: return instance<G, NB, 8>();
-  }
-  return nullptr;
+gemv_fn pick_waves(int waves, int pf) {
+  return waves == 8 ? pick_pf<G, NB, 8>(pf) : waves == 4 ? pick_pf<G, NB, 4>(pf) : nullptr;
 }
 
-gemv_fn pick_gemv(int g, int nb, int cpb) {
+gemv_fn pick_gemv(int g, int nb, int waves, int pf) {
   if (g == 4) {
     switch (nb) {
-      case 1: return pick_cpb<4, 1>(cpb);
-      case 2: return pick_cpb<4, 2>(cpb);
-      case 4: return pick_cpb<4, 4>(cpb);
-      case 8: return pick_cpb<4, 8>(cpb);
-      case 16: return pick_cpb<4, 16>(cpb);
+      case 1: return pick_waves<4, 1>(waves, pf);
+      case 2: return pick_waves<4, 2>(waves, pf);
+      case 4: return pick_waves<4, 4>(waves, pf);
+      case 8: return pick_waves<4, 8>(waves, pf);
+      case 16: return pick_waves<4, 16>(waves, pf);
     }
   } else if (g == 8) {
     switch (nb) {
-      case 1: return pick_cpb<8, 1>(cpb);
-      case 2: return pick_cpb<8, 2>(cpb);
-      case 4: return pick_cpb<8, 4>(cpb);
+      case 1: return pick_waves<8, 1>(waves, pf);
+      case 2: return pick_waves<8, 2>(waves, pf);
+      case 4: return pick_waves<8, 4>(waves, pf);
     }
   }
   return nullptr;
@@ -348,8 +358,24 @@ fluxbin_status fluxbin_create(const fluxbin_layer_desc *d, fluxbin_handle *out) 
     e = hipDeviceSynchronize();
     if (e != hipSuccess) return hip_fail(e, "synchronising after create");
   }
+  gemv_fn fn = pick_gemv(d->g, p.nb, p.waves, p.pf);
+  if (!fn) return fail(FLUXBIN_ERR_UNSUPPORTED, "no kernel for g = %d, batch width %d, %d waves", d->g, p.nb, p.waves);
+  const size_t lds = (size_t)lds_bytes(d->g, p.nb, p.cpb);
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     (int)lds);
+  if (e != hipSuccess) return hip_fail(e, "setting the kernel's dynamic LDS size");
+  const int32_t *idx = d->sal_idx;
+  if (d->ks == 0) {
+    void *z = nullptr;
+    e = hipGetSymbolAddress(&z, HIP_SYMBOL(g_zero_index));
+    if (e != hipSuccess) return hip_fail(e, "locating the zero index array");
+    idx = static_cast<const int32_t *>(z);
+  }
   fluxbin_layer *h = new (std::nothrow) fluxbin_layer;
   if (!h) return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "out of host memory");
+  h->fn = fn;
+  h->lds = lds;
+  h->idx_or_dummy = idx;
   h->d = *d;
   h->plan = p;
   const char *f = getenv("FLUXBIN_FAULT");
@@ -367,7 +393,7 @@ fluxbin_status fluxbin_destroy(fluxbin_handle h) {
 fluxbin_status fluxbin_get_plan(fluxbin_handle h, fluxbin_plan *plan) {
   if (!h || !plan) return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "NULL argument");
   const Plan &p = h->plan;
-  plan->rows_per_block = kWaves * kTileRows;
+  plan->rows_per_block = p.waves * kTileRows;
   plan->chunks_per_block = p.cpb;
   plan->row_blocks = p.row_blocks;
   plan->splits = p.splits;
@@ -425,10 +451,10 @@ fluxbin_status fluxbin_gemv(fluxbin_handle h, const uint16_t *x, uint16_t *y, in
   if (h->fault_launch) return fail(FLUXBIN_ERR_HIP, "injected launch fault (FLUXBIN_FAULT=launch)");
   const fluxbin_layer_desc &d = h->d;
   const Plan &p = h->plan;
-  gemv_fn fn = pick_gemv(d.g, p.nb, p.cpb);
-  if (!fn) return fail(FLUXBIN_ERR_UNSUPPORTED, "no kernel for g = %d, nb = %d, cpb = %d", d.g, p.nb, p.cpb);
   GemvArgs a;
   a.L = layer_args(d);
+  a.idx_or_dummy = h->idx_or_dummy;
+  a.cpb = p.cpb;
   a.total_chunks = p.total_chunks;
   a.row_tiles = p.row_tiles;
   a.row_blocks = p.row_blocks;
@@ -439,7 +465,7 @@ fluxbin_status fluxbin_gemv(fluxbin_handle h, const uint16_t *x, uint16_t *y, in
   a.y = y;
   a.acc = p.splits > 1 ? reinterpret_cast<uint64_t *>(d.workspace) : nullptr;
   const int64_t grid = (int64_t)p.row_blocks * p.splits;
-  hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(kWaves * 64), 0, (hipStream_t)stream, a);
+  hipLaunchKernelGGL(h->fn, dim3((unsigned)grid), dim3(p.waves * 64), h->lds, (hipStream_t)stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "gemv launch");
   return ok();

@@ -73,39 +73,80 @@ struct LayerArgs {
   int32_t nc_g, nc_s;   // 128-column chunks per global / salient segment
 };
 
+#define FB_GLOBAL __attribute__((address_space(1)))
+
+// Uniform copies of kernel arguments.  readfirstlane makes each value an
+// opaque scalar-register value, so a later choice between two fields stays a
+// scalar select instead of becoming a per-lane load through a chosen address.
+// Pointers come back typed in the global address space (global_load, not flat).
+__device__ __forceinline__ int32_t uni(int32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ int64_t uni(int64_t v) {
+  const uint64_t u = (uint64_t)v;
+  return (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int32_t)(u >> 32)) << 32) |
+                   (uint32_t)__builtin_amdgcn_readfirstlane((int32_t)(uint32_t)u));
+}
+template <typename T>
+__device__ __forceinline__ const FB_GLOBAL T *uni(const T *p) {
+  return (const FB_GLOBAL T *)(uintptr_t)uni((int64_t)reinterpret_cast<uintptr_t>(p));
+}
+
+// A layer's arguments in scalar registers.
+struct ULayer {
+  const FB_GLOBAL u32x4 *bits_g, *bits_s;
+  const FB_GLOBAL uint16_t *c_g, *c_s, *r_g, *r_s;
+  const FB_GLOBAL int32_t *sal_idx;
+  int64_t tv_g, tv_s, n, k, s;
+  int32_t kb, ks, nc_g, nc_s;
+};
+
+__device__ __forceinline__ ULayer uniform_layer(const LayerArgs &a) {
+  ULayer L;
+  L.bits_g = uni(a.bits_g);
+  L.bits_s = uni(a.bits_s);
+  L.c_g = uni(a.c_g);
+  L.c_s = uni(a.c_s);
+  L.r_g = uni(a.r_g);
+  L.r_s = uni(a.r_s);
+  L.sal_idx = uni(a.sal_idx);
+  L.tv_g = uni(a.tv_g);
+  L.tv_s = uni(a.tv_s);
+  L.n = uni(a.n);
+  L.k = uni(a.k);
+  L.s = uni(a.s);
+  L.kb = uni(a.kb);
+  L.ks = uni(a.ks);
+  L.nc_g = uni(a.nc_g);
+  L.nc_s = uni(a.nc_s);
+  return L;
+}
+
 // One segment as seen by the kernels.
 struct SegRef {
-  const u32x4 *bits;    // element ((tile * nchunks + chunk) * 64 + lane)
-  const uint16_t *c;
-  const uint16_t *r;
+  const FB_GLOBAL u32x4 *bits;  // element ((tile * nchunks + chunk) * 64 + lane)
+  const FB_GLOBAL uint16_t *c;
+  const FB_GLOBAL uint16_t *r;
   int64_t len;
   int32_t nchunks;
   int32_t salient;
 };
 
-__device__ __forceinline__ SegRef segment(const LayerArgs &L, int sidx) {
+// Branch-free (scalar selects): loop bodies that step through segments stay
+// one basic block, so the compiler keeps each chunk's work together.
+__device__ __forceinline__ SegRef segment(const ULayer &L, int sidx) {
+  const bool g = sidx < L.kb;
+  const int b = g ? sidx : sidx - L.kb;
   SegRef r;
-  if (sidx < L.kb) {
-    r.bits = L.bits_g + sidx * L.tv_g;
-    r.c = L.c_g + sidx * L.k;
-    r.r = L.r_g + sidx * L.n;
-    r.len = L.k;
-    r.nchunks = L.nc_g;
-    r.salient = 0;
-  } else {
-    const int b = sidx - L.kb;
-    r.bits = L.bits_s + b * L.tv_s;
-    r.c = L.c_s + b * L.s;
-    r.r = L.r_s + b * L.n;
-    r.len = L.s;
-    r.nchunks = L.nc_s;
-    r.salient = 1;
-  }
+  r.bits = (g ? L.bits_g : L.bits_s) + b * (g ? L.tv_g : L.tv_s);
+  r.c = (g ? L.c_g : L.c_s) + b * (g ? L.k : L.s);
+  r.r = (g ? L.r_g : L.r_s) + b * L.n;
+  r.len = g ? L.k : L.s;
+  r.nchunks = g ? L.nc_g : L.nc_s;
+  r.salient = !g;
   return r;
 }
 
 // Segment of chunk gc of the concatenated chunk space, and the chunk's index inside it.
-__device__ __forceinline__ int seg_of(const LayerArgs &L, int gc, int *cis) {
+__device__ __forceinline__ int seg_of(const ULayer &L, int gc, int *cis) {
   const int gch = L.kb * L.nc_g;
   if (gc < gch) {
     const int b = gc / L.nc_g;
@@ -119,6 +160,8 @@ __device__ __forceinline__ int seg_of(const LayerArgs &L, int gc, int *cis) {
 
 struct GemvArgs {
   LayerArgs L;
+  const int32_t *idx_or_dummy;  // sal_idx, or a valid one-element array when ks == 0
+  int32_t cpb;            // 128-column chunks per workgroup (tables sized in dynamic LDS)
   int32_t total_chunks;
   int32_t row_tiles;
   int32_t row_blocks;
@@ -146,62 +189,146 @@ __device__ __forceinline__ float pick6(int s, float v0, float v1, float v2, floa
   return r;
 }
 
+#define FB_LDS __attribute__((address_space(3)))
+
+// fp32 at LDS byte address `addr`: the address goes to the instruction as is
+// (constant parts in its offset field), with no base added per access.
+__device__ __forceinline__ float lds_f32(uint32_t addr) {
+  return *reinterpret_cast<const FB_LDS float *>((uintptr_t)addr);
+}
+
+// LDS byte address of a shared-memory pointer.
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)(const FB_LDS void *)p;
+}
+
 // Byte `kk` of v, zero-extended (v_perm_b32: opaque to the optimiser, one VALU op).
 template <int kk>
 __device__ __forceinline__ uint32_t byte_of(uint32_t v) {
   return __builtin_amdgcn_perm(0u, v, 0x0c0c0c00u | kk);
 }
 
+// Table address of one lookup: byte kk of v (a pattern already scaled to a
+// byte offset) in bits 0-7, bits 8-23 taken from `base`, the LDS offset of the
+// chunk's tables (a multiple of 256 below 2^24): a single v_perm_b32.
+template <int kk>
+__device__ __forceinline__ uint32_t addr_of(uint32_t v, uint32_t base) {
+  return __builtin_amdgcn_perm(base, v, 0x0c060500u | kk);
+}
+
+// Accumulate the lookups of one 32-bit word (32 columns) of one row.  `base`
+// is the LDS byte address of the chunk's table block (a multiple of 256
+// below 2^24); j0 is the first sub-vector of the word.  Sub-vector j of batch
+// row b has its TAB-entry table at base + ((b * SUB + j) * TAB) * 4.
 template <int G, int NB>
-__device__ __forceinline__ void lookup_word(uint32_t w, const char *tb, float (&acc)[NB], int j0) {
+__device__ __forceinline__ void lookup_word(uint32_t w, uint32_t base, float (&acc)[NB], int j0) {
   constexpr int SUB = kChunkCols / G;
   constexpr int TAB = 1 << G;
   if constexpr (G == 4) {
     // nibble m of w at bits [4m, 4m+4); A holds nibbles 0,2,4,6 and B nibbles
-    // 1,3,5,7 as byte offsets (index * 4) of a 16-entry fp32 table.
+    // 1,3,5,7, each as a byte offset (index * 4) into a 16-entry fp32 table.
     const uint32_t A = (w << 2) & 0x3c3c3c3cu;
     const uint32_t B = (w >> 2) & 0x3c3c3c3cu;
-    const uint32_t ia[4] = {byte_of<0>(A), byte_of<1>(A), byte_of<2>(A), byte_of<3>(A)};
-    const uint32_t ib[4] = {byte_of<0>(B), byte_of<1>(B), byte_of<2>(B), byte_of<3>(B)};
+    const uint32_t ia[4] = {addr_of<0>(A, base), addr_of<1>(A, base), addr_of<2>(A, base), addr_of<3>(A, base)};
+    const uint32_t ib[4] = {addr_of<0>(B, base), addr_of<1>(B, base), addr_of<2>(B, base), addr_of<3>(B, base)};
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
-        const char *t0 = tb + ((b * SUB + j0 + 2 * kk) * TAB) * 4;
-        acc[b] += *reinterpret_cast<const float *>(t0 + ia[kk]);
-        acc[b] += *reinterpret_cast<const float *>(t0 + TAB * 4 + ib[kk]);
+        const int off0 = ((b * SUB + j0 + 2 * kk) * TAB) * 4;
+        acc[b] += lds_f32(ia[kk] + off0);
+        acc[b] += lds_f32(ib[kk] + off0 + TAB * 4);
       }
+      // wide batches: at most 2 * NB table reads in flight per step, or the
+      // scheduler hoists all of them and runs out of registers
+      if constexpr (NB >= 8) asm volatile("" ::: "memory");
     }
   } else {
-    // byte kk of w is the 8-bit pattern of sub-vector j0 + kk
-    const uint32_t W = w;
+    // byte kk of w is the 8-bit pattern of sub-vector j0 + kk; table offset = pattern * 4
     uint32_t ix[4];
-    ix[0] = (W << 2) & 0x3fcu;
-    ix[1] = (W >> 6) & 0x3fcu;
-    ix[2] = (W >> 14) & 0x3fcu;
-    ix[3] = (W >> 22) & 0x3fcu;
+    ix[0] = ((w << 2) & 0x3fcu) | base;
+    ix[1] = ((w >> 6) & 0x3fcu) | base;
+    ix[2] = ((w >> 14) & 0x3fcu) | base;
+    ix[3] = ((w >> 22) & 0x3fcu) | base;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
-        const char *t0 = tb + ((b * SUB + j0 + kk) * TAB) * 4;
-        acc[b] += *reinterpret_cast<const float *>(t0 + ix[kk]);
+        const int off0 = ((b * SUB + j0 + kk) * TAB) * 4;
+        acc[b] += lds_f32(ix[kk] + off0);
       }
+      if constexpr (NB >= 8) asm volatile("" ::: "memory");
     }
   }
 }
 
-template <int G, int NB, int CPB, int WAVES>
+// Segment and chunk-in-segment stepped to the next chunk (when `step`),
+// branch-free: scalar selects, so that loop bodies stay one basic block.
+__device__ __forceinline__ void next_chunk(const ULayer &L, int &sg, int &cis, bool step = true) {
+  const int n1 = cis + 1;
+  const bool wrap = n1 == (sg < L.kb ? L.nc_g : L.nc_s);
+  cis = step ? (wrap ? 0 : n1) : cis;
+  sg = step ? sg + (int)wrap : sg;
+}
+
+// Dynamic LDS of the GEMV kernel: [cpb][NB][SUB][TAB] fp32 tables, then
+// [cpb][NB][128] fp32 scale-fused inputs, then a 64-float sink for the
+// stores of unused input slots.
+constexpr int kLdsBudget = 80 * 1024;  // per workgroup: two workgroups per CU
+constexpr int kMaxCpb = 32;            // chunks per workgroup
+constexpr int kLdsSink = 64 * 4;
+
+__host__ __device__ constexpr int lds_per_chunk(int g, int nb) {
+  return nb * (kChunkCols / g) * (1 << g) * 4 + nb * kChunkCols * 4;
+}
+
+__host__ __device__ constexpr int lds_bytes(int g, int nb, int cpb) { return cpb * lds_per_chunk(g, nb) + kLdsSink; }
+
+constexpr int kMaxItems = 8;  // table-build inputs per thread (registers)
+
+__host__ __device__ constexpr int cmin(int a, int b) { return a < b ? a : b; }
+
+// Most chunks one workgroup may take for table width g, batch width nb and
+// `waves` waves: its tables must fit the LDS budget, and its table-build
+// inputs (nb * 128 per chunk) at most kMaxItems per thread.
+__host__ __device__ constexpr int cpb_cap(int g, int nb, int waves) {
+  return cmin(cmin(kMaxCpb, (kLdsBudget - kLdsSink) / lds_per_chunk(g, nb)), kMaxItems * waves * 64 / (nb * kChunkCols)) < 1
+             ? 1
+             : cmin(cmin(kMaxCpb, (kLdsBudget - kLdsSink) / lds_per_chunk(g, nb)), kMaxItems * waves * 64 / (nb * kChunkCols));
+}
+
+// Prefetch depth for a workgroup range of cpb chunks: the deepest of 8, 4, 2
+// that the range fills (a shorter range would re-read its last chunk).
+__host__ __device__ constexpr int prefetch_depth(int cpb) { return cpb >= 8 ? 8 : cpb >= 4 ? 4 : 2; }
+
+// Most chunks a kernel instance with prefetch depth pf serves.
+__host__ __device__ constexpr int cpb_for_depth(int pf, int cap) { return pf == 8 ? cap : cmin(2 * pf - 1, cap); }
+
+template <bool B>
+struct BoolTag {
+  static constexpr bool value = B;
+};
+
+template <int G, int NB, int WAVES, int PF>
 __global__ __launch_bounds__(WAVES * 64) void lut_gemv_kernel(const GemvArgs a) {
   constexpr int NT = WAVES * 64;
-  constexpr int SUB = kChunkCols / G;  // sub-vectors per chunk
-  constexpr int TAB = 1 << G;          // full table entries
+  constexpr int SUB = kChunkCols / G;      // sub-vectors per chunk
+  constexpr int TAB = 1 << G;              // full table entries
   constexpr int HALF = TAB / 2;
-  constexpr int WPL = kChunkCols / 32;  // words per lane per chunk (4)
-  __shared__ float s_tab[CPB * NB * SUB * TAB];  // [chunk][batch][sub-vector][pattern]
-  __shared__ float s_v[CPB * NB * kChunkCols];   // [chunk][batch][column] scale-fused inputs
+  constexpr int WPL = kChunkCols / 32;     // words per lane per chunk (4)
+  constexpr int CTB = NB * SUB * TAB * 4;  // table bytes of one chunk (all batch rows)
+  static_assert(CTB % 256 == 0, "chunk table blocks must be 256-byte aligned");
+  static_assert(NT % HALF == 0, "thread count must be a multiple of the half-table size");
+  static_assert(PF >= 1 && PF <= 8, "prefetch depth");
+  extern __shared__ __align__(1024) float smem[];
 
-  const LayerArgs &L = a.L;
+  const ULayer L = uniform_layer(a.L);  // scalar registers: field selects stay scalar
+  const int cpb = a.cpb;
+  float *s_tab = smem;
+  const uint32_t tab_base = lds_addr(s_tab);  // 1024-aligned (table addresses are merged bytewise)
+  float *s_v = smem + cpb * (CTB / 4);
+  float *s_sink = s_v + cpb * NB * kChunkCols;
+
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar address arithmetic
@@ -213,122 +340,138 @@ __global__ __launch_bounds__(WAVES * 64) void lut_gemv_kernel(const GemvArgs a) 
   const int row = tile * kTileRows + lane;
   const bool row_ok = tile_ok && row < L.n;
   const int rrow = row_ok ? row : 0;
-  const int c0 = sp * CPB;
-  const int nch = min(CPB, a.total_chunks - c0);
+  const int c0 = sp * cpb;
+  const int nch = min(cpb, a.total_chunks - c0);
 
-  // Segment and chunk-in-segment of each of the workgroup's chunks (uniform).
-  // Chunks past the range repeat the last one: a redundant load, never used.
-  int cseg[CPB], ccis[CPB];
-  {
-    int cis;
-    int sg = seg_of(L, c0, &cis);
+  // Chunk map of the workgroup's range, one chunk per lane (nch <= 32 < 64):
+  // lane l holds the segment and chunk-in-segment of chunk c0 + l, and a
+  // uniform chunk's entry is read out of its lane.
+  int mcis;
+  const int mseg = seg_of(L, c0 + min(lane, nch - 1), &mcis);
+  auto seg_at = [&](int ch) { return __builtin_amdgcn_readlane(mseg, ch); };
+  auto cis_at = [&](int ch) { return __builtin_amdgcn_readlane(mcis, ch); };
+  const int s0 = seg_at(0), cis0 = cis_at(0), s_last = seg_at(nch - 1);
+
+  // The rest of the kernel exists twice: for workgroups whose range holds
+  // global segments only, and for those that reach a salient segment (these
+  // fetch gather indices before their activations).  Separate copies keep
+  // each copy's memory waits exact: where two paths join, the compiler's
+  // waits are those of the slower path.  The branch is uniform.
+  auto body = [&](auto sal_tag) {
+    constexpr bool SAL = decltype(sal_tag)::value;
+    // Vector-memory loads complete in issue order, and the compiler's waits are
+    // exact only for loads issued on every path of a branch-free stretch.  The
+    // prologue requests row scales, column scales and activations first and PF
+    // chunks of weights after them (a workgroup with fewer chunks re-reads its
+    // last one), so that waiting for the table-build inputs never waits for
+    // HBM and the weights stay in flight during the table build.  A workgroup
+    // whose range reaches a salient segment fetches gather indices (VCM)
+    // instead of activations before the weights, and the activations after.
+    const FB_GLOBAL int32_t *uidx = uni(a.idx_or_dummy);
+    const FB_GLOBAL uint16_t *ux = uni(a.x);
+    // row scales of the segments this workgroup touches (s0 .. s_last, consecutive)
+    auto rptr = [&](int j) { return segment(L, min(s0 + j, s_last)).r + rrow; };
+    const uint16_t rr0 = *rptr(0), rr1 = *rptr(1), rr2 = *rptr(2), rr3 = *rptr(3), rr4 = *rptr(4), rr5 = *rptr(5);
+
+    u32x4 wb[PF];
+    int ps = s0, pcis = cis0, pidx = 0;  // next chunk to load and its index in the range
+    auto load_next = [&]() -> u32x4 {
+      const SegRef S = segment(L, ps);
+      const FB_GLOBAL u32x4 *base = S.bits + ((int64_t)ltile * S.nchunks + pcis) * kTileRows;
+      const u32x4 w = __builtin_nontemporal_load(base + lane);
+      const bool step = pidx < nch - 1;  // past the last chunk the last one is read again
+      next_chunk(L, ps, pcis, step);
+      pidx += (int)step;
+      return w;
+    };
+    auto issue_weights = [&]() {
 #pragma unroll
-    for (int ch = 0; ch < CPB; ++ch) {
-      cseg[ch] = sg;
-      ccis[ch] = cis;
-      if (ch + 1 < nch) {
-        ++cis;
-        if (cis == (sg < L.kb ? L.nc_g : L.nc_s)) {
-          cis = 0;
-          ++sg;
-        }
+      for (int u = 0; u < PF; ++u) wb[u] = load_next();
+    };
+
+    // Table-build items (chunk, batch row, column) of the range: item e is
+    // handled by thread e % NT; a wave's 64 items share chunk and batch row.
+    // Every item slot loads (items past the range re-read the last chunk's
+    // inputs and are dropped).
+    constexpr int CMAX = cpb_for_depth(PF, cpb_cap(G, NB, WAVES));  // chunks, at most
+    constexpr int VPT = (CMAX * NB * kChunkCols + NT - 1) / NT;  // items per thread, at most
+    static_assert(VPT <= kMaxItems, "table-build inputs per thread");
+    static_assert(kChunkCols % 64 == 0 && NT % 64 == 0, "a wave's items must share chunk and batch row");
+    const int items = nch * NB * kChunkCols;
+    // Per item: uniform row pointer into x, per-lane 32-bit column offsets
+    // (loads then take a scalar base and a 32-bit vector offset).
+    bool live[VPT], sal[VPT];
+    const FB_GLOBAL uint16_t *xrow[VPT];
+    uint32_t ccl[VPT];
+    uint32_t cvl[VPT], xvl[VPT];  // 32-bit: the compiler would otherwise pack pairs, waiting early
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int ebase = min(i * NT + wave * 64, items - 64);  // uniform
+      const int ch = ebase / (NB * kChunkCols);
+      const int b = (ebase / kChunkCols) % NB;
+      const int sg = seg_at(ch);
+      const int cis = cis_at(ch);
+      const SegRef S = segment(L, sg);
+      const bool brow = b < a.batch;  // uniform; batch rows past `batch` do not exist
+      const uint32_t cc = (uint32_t)(cis * kChunkCols + (ebase & (kChunkCols - 1)) + lane);
+      live[i] = brow & (cc < (uint32_t)S.len);  // non-short-circuit: a select, not a branch
+      sal[i] = S.salient;
+      ccl[i] = live[i] ? cc : 0u;
+      xrow[i] = ux + (brow ? b : 0) * L.k;
+      cvl[i] = S.c[ccl[i]];
+    }
+    // Inputs to LDS.  No select or branch takes a loaded value as an operand
+    // (the compiler would turn it into a branch around the load): unused slots
+    // are zeroed by masking the fp16 bits and stored to the sink.
+    float rv0, rv1, rv2, rv3, rv4, rv5;  // row scales as fp32
+    auto stage = [&]() {
+      rv0 = h2f(rr0), rv1 = h2f(rr1), rv2 = h2f(rr2), rv3 = h2f(rr3), rv4 = h2f(rr4), rv5 = h2f(rr5);
+#pragma unroll
+      for (int i = 0; i < VPT; ++i) {
+        const uint32_t m = live[i] ? 0xffffu : 0u;
+        float *dst = i * NT + wave * 64 < items ? s_v + i * NT + tid : s_sink + lane;
+        *dst = h2f((uint16_t)(cvl[i] & m)) * h2f((uint16_t)(xvl[i] & m));
       }
-    }
-  }
-  const int s_first = cseg[0];
-  const int s_lastseg = cseg[CPB - 1];
-  const bool any_salient = s_lastseg >= L.kb;  // segments run global first, then salient
-
-  // 1. Loads.  Inputs of the table build go first so that waiting for them
-  //    (loads retire in order) does not wait for the weight stream.  Every
-  //    load is unconditional from a valid address and dead items are zeroed
-  //    by a select, so all loads of a phase are in flight together.
-  constexpr int VPC = (NB * kChunkCols + NT - 1) / NT;  // v items per thread per chunk
-  bool vlive[CPB][VPC];
-  uint16_t vc[CPB][VPC];   // fp16 column scale
-  uint16_t vxv[CPB][VPC];  // fp16 activation
-  u32x4 w[CPB];            // this lane's 16 bytes of every chunk
-  int64_t xrow[CPB][VPC];  // b * k
-  int32_t xcol[CPB][VPC];  // column of x (gathered through sal_idx on salient segments)
+    };
+    // sched_barrier: the scheduler must not move work that waits for earlier
+    // loads above the weight requests (that wait would hold them back).
+    if constexpr (!SAL) {
 #pragma unroll
-  for (int ch = 0; ch < CPB; ++ch) {
-    const SegRef sg = segment(L, cseg[ch]);
+      for (int i = 0; i < VPT; ++i) xvl[i] = xrow[i][ccl[i]];
+      __builtin_amdgcn_sched_barrier(0);
+      issue_weights();
+      __builtin_amdgcn_sched_barrier(0);
+      stage();
+      asm volatile("; lut_gemv prologue: global segments" ::: "memory");
+    } else {
+      uint32_t gi[VPT];
 #pragma unroll
-    for (int i = 0; i < VPC; ++i) {
-      const int e = tid + i * NT;
-      const int b = e / kChunkCols;
-      const int cc = ccis[ch] * kChunkCols + (e & (kChunkCols - 1));
-      // non-short-circuit: a select, not a branch
-      const bool live = (ch < nch) & (e < NB * kChunkCols) & (b < a.batch) & (cc < sg.len);
-      vlive[ch][i] = live;
-      xrow[ch][i] = live ? (int64_t)b * L.k : 0;
-      xcol[ch][i] = live ? cc : 0;
-      vc[ch][i] = sg.c[xcol[ch][i]];
-    }
-  }
-  auto stream_weights = [&]() {
+      for (int i = 0; i < VPT; ++i) gi[i] = (uint32_t)uidx[sal[i] ? ccl[i] : 0u];
+      __builtin_amdgcn_sched_barrier(0);
+      issue_weights();
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int ch = 0; ch < CPB; ++ch) {
-      const SegRef sg = segment(L, cseg[ch]);
-      const u32x4 *base = sg.bits + ((int64_t)ltile * sg.nchunks + ccis[ch]) * kTileRows;
-      w[ch] = __builtin_nontemporal_load(base + lane);
-    }
-  };
-  if (!any_salient) {
-    // global chunks only: activations, then the weight stream
-#pragma unroll
-    for (int ch = 0; ch < CPB; ++ch)
-#pragma unroll
-      for (int i = 0; i < VPC; ++i) vxv[ch][i] = a.x[xrow[ch][i] + xcol[ch][i]];
-    stream_weights();
-  } else {
-    // some chunk is salient: gather indices first (VCM), then activations, then weights
-#pragma unroll
-    for (int ch = 0; ch < CPB; ++ch) {
-      const bool sal = cseg[ch] >= L.kb;
-#pragma unroll
-      for (int i = 0; i < VPC; ++i) {
-        const int32_t gi = L.sal_idx[sal ? xcol[ch][i] : 0];
-        xcol[ch][i] = sal ? gi : xcol[ch][i];
+      for (int i = 0; i < VPT; ++i) {
+        const uint32_t sm = 0u - (uint32_t)sal[i];  // all ones on salient items
+        xvl[i] = xrow[i][ccl[i] + ((gi[i] - ccl[i]) & sm)];
       }
+      stage();
+      asm volatile("; lut_gemv prologue: salient segments" ::: "memory");
     }
-#pragma unroll
-    for (int ch = 0; ch < CPB; ++ch)
-#pragma unroll
-      for (int i = 0; i < VPC; ++i) vxv[ch][i] = a.x[xrow[ch][i] + xcol[ch][i]];
-    stream_weights();
-  }
-  // row scales of the segments this workgroup touches (s_first .. s_lastseg, consecutive)
-  auto rptr = [&](int j) -> const uint16_t * { return segment(L, min(s_first + j, s_lastseg)).r + rrow; };
-  const uint16_t rr0 = *rptr(0), rr1 = *rptr(1), rr2 = *rptr(2), rr3 = *rptr(3), rr4 = *rptr(4), rr5 = *rptr(5);
+    __syncthreads();
 
-  // 2. scale-fused inputs v = c * x (exact in fp32: product of two fp16 values)
+    // Tables: the half with the top input at +1 is summed, the rest negated.
+    // Entry q of a sub-vector is v_{G-1} + sum_{i<G-1} sgn_i(q) * v_i in that
+    // order; sgn_i = +-1 exactly, so each fma rounds like the add or subtract.
+    // NT is a multiple of HALF, so a thread's pattern q is fixed.
+    {
+      const int q = tid & (HALF - 1);
+      float sgn[G - 1];
 #pragma unroll
-  for (int ch = 0; ch < CPB; ++ch)
-#pragma unroll
-    for (int i = 0; i < VPC; ++i) {
-      const int e = tid + i * NT;
-      if (e < NB * kChunkCols) s_v[ch * NB * kChunkCols + e] = vlive[ch][i] ? h2f(vc[ch][i]) * h2f(vxv[ch][i]) : 0.0f;
-    }
-  const float rv0 = h2f(rr0), rv1 = h2f(rr1), rv2 = h2f(rr2), rv3 = h2f(rr3), rv4 = h2f(rr4), rv5 = h2f(rr5);
-  __syncthreads();
-
-  // 3. tables: the half with the top input at +1 is summed, the rest negated.
-  //    Entry q of a sub-vector is v_{G-1} + sum_{i<G-1} sgn_i(q) * v_i in that
-  //    order; sgn_i = +-1 exactly, so each fma rounds like the add or subtract.
-  //    NT is a multiple of HALF, so a thread's pattern q (and its signs) is the
-  //    same in every iteration.
-  static_assert(NT % HALF == 0, "thread count must be a multiple of the half-table size");
-  constexpr int TITEMS = (CPB * NB * SUB * HALF + NT - 1) / NT;
-  {
-    const int q = tid & (HALF - 1);
-    float sgn[G - 1];
-#pragma unroll
-    for (int i = 0; i < G - 1; ++i) sgn[i] = ((q >> i) & 1) ? 1.0f : -1.0f;
-#pragma unroll
-    for (int it = 0; it < TITEMS; ++it) {
-      const int e = tid + it * NT;
-      if (e < nch * NB * SUB * HALF) {
+      for (int i = 0; i < G - 1; ++i) sgn[i] = ((q >> i) & 1) ? 1.0f : -1.0f;
+      const int tcount = nch * NB * SUB * HALF;
+#pragma unroll 4
+      for (int e = tid; e < tcount; e += NT) {
         const int j = (e / HALF) & (SUB - 1);
         const int cb = e / (HALF * SUB);  // chunk * NB + batch row
         const float *v = &s_v[cb * kChunkCols + j * G];
@@ -340,73 +483,104 @@ __global__ __launch_bounds__(WAVES * 64) void lut_gemv_kernel(const GemvArgs a) 
         tb[(HALF - 1) ^ q] = -t;
       }
     }
-  }
-  __syncthreads();
+    __syncthreads();
 
-  // 4. lookups: sign patterns index the tables; fp32 accumulation per segment
-  float part[NB], acc[NB];
+    // Lookups, chunk by chunk, with PF chunks of weights in flight: once a
+    // chunk's 16 bytes are consumed the chunk PF ahead is requested in its place.
+    float part[NB], acc[NB];
 #pragma unroll
-  for (int b = 0; b < NB; ++b) part[b] = acc[b] = 0.0f;
-  int cur = s_first;
+    for (int b = 0; b < NB; ++b) part[b] = acc[b] = 0.0f;
+    int cur = s0;              // segment being accumulated
+    int ls = s0, lcis = cis0;  // chunk being looked up
+    // After each chunk, if the next one starts another segment, the finished
+    // segment is folded in with its row scale.  Branch-free (selects), so a
+    // chunk's table reads and the adds that consume them share one block.
+    auto consume = [&](int ch, const u32x4 w) {
+      const uint32_t base = tab_base + (uint32_t)(ch * CTB);
 #pragma unroll
-  for (int ch = 0; ch < CPB; ++ch) {
-    if (ch < nch) {
-      const int s = cseg[ch];
-      if (s != cur) {
-        const float rc = pick6(cur - s_first, rv0, rv1, rv2, rv3, rv4, rv5);
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
-          part[b] += rc * acc[b];
-          acc[b] = 0.0f;
-        }
-        cur = s;
+      for (int q = 0; q < WPL; ++q) {
+        lookup_word<G, NB>(w[q], base, acc, q * (32 / G));
+        // wider batches: one word's table reads at a time
+        if constexpr (NB >= 4) asm volatile("" ::: "memory");
       }
-      const char *tb = reinterpret_cast<const char *>(&s_tab[ch * NB * SUB * TAB]);
+      next_chunk(L, ls, lcis);
+      const bool fold = ls != cur;  // uniform
+      const float rc = pick6(cur - s0, rv0, rv1, rv2, rv3, rv4, rv5);
 #pragma unroll
-      for (int q = 0; q < WPL; ++q) lookup_word<G, NB>(w[ch][q], tb, acc, q * (32 / G));
+      for (int b = 0; b < NB; ++b) {
+        part[b] = fold ? fmaf(rc, acc[b], part[b]) : part[b];
+        acc[b] = fold ? 0.0f : acc[b];
+      }
+      cur = ls;
+      // the next chunk's table reads stay behind this chunk's (registers)
+      asm volatile("" ::: "memory");
+    };
+    int ch0 = 0;
+    for (; ch0 + PF < nch; ch0 += PF) {
+#pragma unroll
+      for (int u = 0; u < PF; ++u) {
+        // consumed before the refill is issued into the same registers: with
+        // both alive the compiler would rotate registers with copies that wait
+        consume(ch0 + u, wb[u]);
+        wb[u] = load_next();
+        __builtin_amdgcn_sched_barrier(0);  // issue the refill here, not later
+      }
     }
-  }
-  {
-    const float rc = pick6(cur - s_first, rv0, rv1, rv2, rv3, rv4, rv5);
 #pragma unroll
-    for (int b = 0; b < NB; ++b) part[b] += rc * acc[b];
-  }
+    for (int u = 0; u < PF; ++u)
+      if (ch0 + u < nch) consume(ch0 + u, wb[u]);
+    if (cur <= s_last) {  // the range ended inside a segment: fold its remainder
+      const float rc = pick6(cur - s0, rv0, rv1, rv2, rv3, rv4, rv5);
+#pragma unroll
+      for (int b = 0; b < NB; ++b) part[b] = fmaf(rc, acc[b], part[b]);
+    }
 
-  // 5. output
-  if (a.splits == 1) {
+    // Output
+    if (a.splits == 1) {
+      if (row_ok) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+          if (b < a.batch) a.y[(int64_t)b * L.n + row] = f2h(part[b]);
+      }
+      return;
+    }
+    // splits > 1: every workgroup adds its partial sum of each row into that
+    // row's packed word with one agent-scope atomic (performed at the memory
+    // side, coherent across XCDs).  The atomic returns the previous word, so the
+    // lane that brings the last of `splits` contributions knows it is last and
+    // holds the complete sum: it writes y and clears the word for the next call.
+    // No workgroup waits for another, and since integer addition is exact the
+    // result does not depend on the order in which the splits arrive.
+    //
+    // The fixed-point step quantises each partial to 2^-31 (absolute) and
+    // saturates partials beyond +-2^17, twice the largest fp16 output.
     if (row_ok) {
 #pragma unroll
-      for (int b = 0; b < NB; ++b)
-        if (b < a.batch) a.y[(int64_t)b * L.n + row] = f2h(part[b]);
-    }
-    return;
-  }
-  // splits > 1: every workgroup adds its partial sum of each row into that
-  // row's packed word with one agent-scope atomic (performed at the memory
-  // side, coherent across XCDs).  The atomic returns the previous word, so the
-  // lane that brings the last of `splits` contributions knows it is last and
-  // holds the complete sum: it writes y and clears the word for the next call.
-  // No workgroup waits for another, and since integer addition is exact the
-  // result does not depend on the order in which the splits arrive.
-  //
-  // The fixed-point step quantises each partial to 2^-31 (absolute) and
-  // saturates partials beyond +-2^17, twice the largest fp16 output.
-  if (row_ok) {
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      if (b < a.batch) {
-        const float scaled = fminf(fmaxf(part[b] * kFixScale, -kFixClamp), kFixClamp);
-        const uint64_t contrib = (uint64_t)(__float2ll_rn(scaled) + kFixBias);
-        uint64_t *slot = a.acc + (int64_t)b * a.n_pad + row;
-        const uint64_t old =
-            __hip_atomic_fetch_add(slot, contrib + kOneArrival, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if ((int)(old >> kCountShift) == a.splits - 1) {
-          const int64_t total = (int64_t)((old & kValueMask) + contrib) - (int64_t)a.splits * kFixBias;
-          a.y[(int64_t)b * L.n + row] = f2h(__ll2float_rn(total) * kFixInv);
-          __hip_atomic_store(slot, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int b = 0; b < NB; ++b) {
+        if (b < a.batch) {
+          const float scaled = fminf(fmaxf(part[b] * kFixScale, -kFixClamp), kFixClamp);
+          const uint64_t contrib = (uint64_t)(__float2ll_rn(scaled) + kFixBias);
+          uint64_t *slot = a.acc + (int64_t)b * a.n_pad + row;
+          const uint64_t old =
+              __hip_atomic_fetch_add(slot, contrib + kOneArrival, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if ((int)(old >> kCountShift) == a.splits - 1) {
+            const int64_t total = (int64_t)((old & kValueMask) + contrib) - (int64_t)a.splits * kFixBias;
+            a.y[(int64_t)b * L.n + row] = f2h(__ll2float_rn(total) * kFixInv);
+            __hip_atomic_store(slot, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
         }
       }
     }
+    if constexpr (SAL) {
+      asm volatile("; lut_gemv end: salient" ::: "memory");
+    } else {
+      asm volatile("; lut_gemv end: global" ::: "memory");
+    }
+  };
+  if (s_last < L.kb) {
+    body(BoolTag<false>{});
+  } else {
+    body(BoolTag<true>{});
   }
 }
 
@@ -426,7 +600,7 @@ struct LutArgs {
 template <int G>
 __global__ __launch_bounds__(256) void build_lut_kernel(const LutArgs a) {
   constexpr int HALF = 1 << (G - 1);
-  const LayerArgs &L = a.L;
+  const ULayer L = uniform_layer(a.L);
   const int64_t total = (int64_t)a.batch * a.subs_per_batch * HALF;
   for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total;
        e += (int64_t)gridDim.x * blockDim.x) {

@@ -38,7 +38,7 @@ class LayerDesc(ctypes.Structure):
         ("bits_global", P), ("r_global", P), ("c_global", P),
         ("bits_sal", P), ("r_sal", P), ("c_sal", P), ("sal_idx", P),
         ("workspace", P), ("workspace_bytes", ctypes.c_size_t),
-        ("chunks_per_block", I32), ("reserved", I32),
+        ("chunks_per_block", I32), ("waves_per_block", I32),
     ]
 
 
@@ -200,7 +200,8 @@ class DeviceLayer:
     tensors owned by this object, which keeps them alive for the handle.
     """
 
-    def __init__(self, layer, max_batch: int = 1, chunks_per_block: int = 0, device="cuda"):
+    def __init__(self, layer, max_batch: int = 1, chunks_per_block: int = 0, waves_per_block: int = 0,
+                 device="cuda"):
         import numpy as np
         import torch
 
@@ -233,7 +234,7 @@ class DeviceLayer:
             self.sal_idx = up(layer.sal_idx, np.int32)
         else:
             self.bits_s = self.r_s = self.c_s = self.sal_idx = None
-        desc = self.make_desc(chunks_per_block)
+        desc = self.make_desc(chunks_per_block, waves_per_block)
         ws = fluxbin_workspace_size(desc)
         self.workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev) if ws else None
         desc.workspace = _ptr(self.workspace)
@@ -243,7 +244,7 @@ class DeviceLayer:
         self.handle = fluxbin_create(desc)
         self.plan = fluxbin_get_plan(self.handle)
 
-    def make_desc(self, chunks_per_block: int = 0) -> LayerDesc:
+    def make_desc(self, chunks_per_block: int = 0, waves_per_block: int = 0) -> LayerDesc:
         L = self.layer
         d = LayerDesc()
         d.abi_version = ABI_VERSION
@@ -253,6 +254,7 @@ class DeviceLayer:
         d.bits_sal, d.r_sal, d.c_sal, d.sal_idx = (_ptr(self.bits_s), _ptr(self.r_s), _ptr(self.c_s),
                                                    _ptr(self.sal_idx))
         d.chunks_per_block = chunks_per_block
+        d.waves_per_block = waves_per_block
         return d
 
     def gemv(self, x, y, batch=None, stream=None):

@@ -109,8 +109,11 @@ typedef struct {
   const int32_t *sal_idx;      /* [s] salient columns, strictly ascending, in [0, k) */
   void *workspace;             /* >= fluxbin_workspace_size() bytes, 256-B aligned; may be NULL if that size is 0 */
   size_t workspace_bytes;
-  int32_t chunks_per_block;    /* tuning: 0 = automatic, else 1, 2, 4 or 8 (128-column chunks per workgroup) */
-  int32_t reserved;            /* must be 0 */
+  int32_t chunks_per_block;    /* tuning: 0 = automatic, else 1..32 128-column chunks per workgroup; the
+                                  limit for a given g, batch width and waves_per_block follows from 80 KiB
+                                  of tables per workgroup and 8 table-build inputs per thread
+                                  (FLUXBIN_ERR_UNSUPPORTED beyond it) */
+  int32_t waves_per_block;     /* tuning: 0 = automatic, else 4 or 8 (64 output rows per wave) */
 } fluxbin_layer_desc;
 
 /* How a handle splits the work (read-only introspection). */
@@ -120,7 +123,7 @@ typedef struct {
   int32_t row_blocks;       /* workgroups along the rows */
   int32_t splits;           /* workgroups along the concatenated columns of all segments */
   int32_t total_chunks;     /* sum over segments of ceil(len/128) */
-  int32_t lds_bytes;        /* static LDS per workgroup at max_batch */
+  int32_t lds_bytes;        /* dynamic LDS per workgroup at max_batch */
   int64_t grid;             /* workgroups per fluxbin_gemv launch */
 } fluxbin_plan;
 

@@ -88,7 +88,7 @@ def test_too_many_splits_is_unsupported(fb):
 @pytest.mark.parametrize("field,value,status", [
     ("abi_version", 2, 1), ("g", 3, 2), ("g", 16, 2), ("kb", 0, 2), ("kb", 5, 2), ("ks", 3, 2), ("ks", -1, 2),
     ("n", 0, 1), ("k", 0, 1), ("s", 0, 1), ("s", 5000, 1), ("max_batch", 0, 2), ("max_batch", 17, 2),
-    ("chunks_per_block", 3, 1), ("reserved", 1, 1),
+    ("chunks_per_block", 33, 1), ("chunks_per_block", -1, 1), ("waves_per_block", 2, 1), ("waves_per_block", 16, 1),
 ])
 def test_workspace_size_rejects(fb, field, value, status):
     st, _ = ws_status(fb, good_desc(fb, **{field: value}))

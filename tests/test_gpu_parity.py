@@ -272,30 +272,43 @@ def test_workload5_llama70b(fb, orc, shape_idx):
 # ----------------------------------------------------------------------------- edge cases
 
 EDGE = [
-    # g, n, k, kb, ks, s, batch, cpb
-    (4, 1, 1, 1, 0, 0, 1, 0),
-    (4, 63, 5, 1, 1, 1, 1, 0),
-    (4, 65, 127, 3, 2, 127, 2, 0),
-    (4, 2000, 33, 2, 1, 33, 5, 0),
-    (4, 777, 1031, 4, 2, 500, 16, 0),
-    (4, 4096, 4096, 2, 1, 256, 1, 1),
-    (4, 4096, 4096, 2, 1, 256, 1, 2),
-    (4, 4096, 4096, 2, 1, 256, 1, 4),
-    (4, 4096, 4096, 2, 1, 256, 1, 8),
-    (4, 257, 11008, 2, 1, 224, 8, 4),
-    (8, 1, 8, 1, 0, 0, 1, 0),
-    (8, 100, 1000, 4, 2, 999, 3, 0),
-    (8, 4096, 4096, 3, 1, 96, 1, 1),
-    (8, 4096, 4096, 3, 1, 96, 1, 4),
+    # g, n, k, kb, ks, s, batch, cpb, waves
+    (4, 1, 1, 1, 0, 0, 1, 0, 0),
+    (4, 63, 5, 1, 1, 1, 1, 0, 0),
+    (4, 65, 127, 3, 2, 127, 2, 0, 0),
+    (4, 2000, 33, 2, 1, 33, 5, 0, 0),
+    (4, 777, 1031, 4, 2, 500, 16, 0, 0),
+    (4, 4096, 4096, 2, 1, 256, 1, 1, 0),
+    (4, 4096, 4096, 2, 1, 256, 1, 2, 0),
+    (4, 4096, 4096, 2, 1, 256, 1, 4, 0),
+    (4, 4096, 4096, 2, 1, 256, 1, 8, 0),
+    (4, 4096, 4096, 2, 1, 256, 1, 2, 8),
+    (4, 1000, 4096, 2, 1, 96, 3, 4, 8),
+    (4, 577, 300, 1, 1, 40, 1, 1, 4),
+    (4, 257, 11008, 2, 1, 224, 8, 2, 0),
+    (4, 257, 11008, 2, 1, 224, 8, 3, 8),
+    # long workgroup ranges (8-deep prefetch): segment changes inside a range,
+    # a last range shorter than the prefetch depth, the largest range
+    (4, 4096, 4096, 2, 1, 256, 1, 16, 4),
+    (4, 300, 4096, 4, 2, 1000, 1, 20, 8),
+    (4, 300, 4096, 4, 2, 1000, 1, 31, 8),
+    (4, 130, 2500, 3, 1, 700, 2, 9, 8),
+    (8, 1, 8, 1, 0, 0, 1, 0, 0),
+    (8, 100, 1000, 4, 2, 999, 3, 0, 0),
+    (8, 4096, 4096, 3, 1, 96, 1, 1, 0),
+    (8, 4096, 4096, 3, 1, 96, 1, 4, 0),
+    (8, 4096, 4096, 3, 1, 96, 2, 2, 8),
 ]
 
 
-@pytest.mark.parametrize("g,n,k,kb,ks,s,batch,cpb", EDGE)
-def test_gemv_edge_cases(fb, orc, g, n, k, kb, ks, s, batch, cpb):
-    note(f"edge g={g} n={n} k={k} kb={kb} ks={ks} s={s} batch={batch} cpb={cpb}")
+@pytest.mark.parametrize("g,n,k,kb,ks,s,batch,cpb,waves", EDGE)
+def test_gemv_edge_cases(fb, orc, g, n, k, kb, ks, s, batch, cpb, waves):
+    note(f"edge g={g} n={n} k={k} kb={kb} ks={ks} s={s} batch={batch} cpb={cpb} waves={waves}")
     layer = I.make_layer(n, k, kb, ks, g, s=s if ks else None, outlier_frac=0.01, seed=(63, n, k))
     x = I.make_x(layer, batch, seed=(63, n, k))
-    dl = fb.DeviceLayer(layer, max_batch=batch, chunks_per_block=cpb)
+    dl = fb.DeviceLayer(layer, max_batch=batch, chunks_per_block=cpb, waves_per_block=waves)
+    if waves:
+        assert dl.plan["rows_per_block"] == 64 * waves
     y16 = gemv(fb, dl, x)
     rows = None if n <= 4096 else I.stream(64, n).choice(n, 1024, replace=False)
     check_y(orc, layer, x, y16, dl.plan, rows=rows)
