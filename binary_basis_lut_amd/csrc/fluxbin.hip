@@ -214,6 +214,29 @@ LayerArgs layer_args(const fluxbin_layer_desc &d) {
   return L;
 }
 
+// Base pointers of every segment of a GEMV call (unused entries repeat the
+// last segment, so that any index the kernel clamps to stays valid).
+void gemv_segments(const fluxbin_layer_desc &d, SegDesc (&seg)[kMaxSeg]) {
+  const int64_t tw_g = fluxbin_tiled_words(d.n, d.k), tw_s = d.ks > 0 ? fluxbin_tiled_words(d.n, d.s) : 0;
+  const int32_t nc_g = (int32_t)cdiv(d.k, kChunkCols), nc_s = d.ks > 0 ? (int32_t)cdiv(d.s, kChunkCols) : 1;
+  int i = 0;
+  for (int b = 0; b < d.kb; ++b, ++i) {
+    seg[i].bits = reinterpret_cast<const u32x4 *>(d.bits_global) + b * tw_g / 4;
+    seg[i].c = d.c_global + b * d.k;
+    seg[i].r = d.r_global + b * d.n;
+    seg[i].len = (int32_t)d.k;
+    seg[i].nchunks = nc_g;
+  }
+  for (int b = 0; b < d.ks; ++b, ++i) {
+    seg[i].bits = reinterpret_cast<const u32x4 *>(d.bits_sal) + b * tw_s / 4;
+    seg[i].c = d.c_sal + b * d.s;
+    seg[i].r = d.r_sal + b * d.n;
+    seg[i].len = (int32_t)d.s;
+    seg[i].nchunks = nc_s;
+  }
+  for (; i < kMaxSeg; ++i) seg[i] = seg[i - 1];
+}
+
 int grid_for(int64_t items, int per_thread_block = 256) {
   int64_t g = cdiv(items, per_thread_block);
   if (g < 1) g = 1;
@@ -453,6 +476,7 @@ fluxbin_status fluxbin_gemv(fluxbin_handle h, const uint16_t *x, uint16_t *y, in
   const Plan &p = h->plan;
   GemvArgs a;
   a.L = layer_args(d);
+  gemv_segments(d, a.seg);
   a.idx_or_dummy = h->idx_or_dummy;
   a.cpb = p.cpb;
   a.total_chunks = p.total_chunks;

@@ -145,6 +145,30 @@ __device__ __forceinline__ SegRef segment(const ULayer &L, int sidx) {
   return r;
 }
 
+// One segment as the GEMV kernel receives it: base pointers precomputed on
+// the host, so that the kernel reads them (scalar loads from its argument
+// block, indexed by a uniform segment number) instead of recomputing them.
+struct SegDesc {
+  const u32x4 *bits;     // tiled words: element (tile * nchunks + chunk) * 64 + lane
+  const uint16_t *c;     // fp16 column scales of the segment
+  const uint16_t *r;     // fp16 row scales of the segment
+  int32_t len;           // columns
+  int32_t nchunks;       // ceil(len / 128)
+};
+
+// Segment `sidx` (uniform) of a GEMV call, pointers in the global address space.
+__device__ __forceinline__ SegRef gemv_segment(const SegDesc (&seg)[kMaxSeg], int kb, int sidx) {
+  const SegDesc &d = seg[sidx];
+  SegRef r;
+  r.bits = (const FB_GLOBAL u32x4 *)(uintptr_t)d.bits;
+  r.c = (const FB_GLOBAL uint16_t *)(uintptr_t)d.c;
+  r.r = (const FB_GLOBAL uint16_t *)(uintptr_t)d.r;
+  r.len = d.len;
+  r.nchunks = d.nchunks;
+  r.salient = sidx >= kb;
+  return r;
+}
+
 // Segment of chunk gc of the concatenated chunk space, and the chunk's index inside it.
 __device__ __forceinline__ int seg_of(const ULayer &L, int gc, int *cis) {
   const int gch = L.kb * L.nc_g;
@@ -159,6 +183,7 @@ __device__ __forceinline__ int seg_of(const ULayer &L, int gc, int *cis) {
 }
 
 struct GemvArgs {
+  SegDesc seg[kMaxSeg];   // kb global segments, then ks salient ones
   LayerArgs L;
   const int32_t *idx_or_dummy;  // sal_idx, or a valid one-element array when ks == 0
   int32_t cpb;            // 128-column chunks per workgroup (tables sized in dynamic LDS)
@@ -370,13 +395,13 @@ __global__ __launch_bounds__(WAVES * 64) void lut_gemv_kernel(const GemvArgs a) 
     const FB_GLOBAL int32_t *uidx = uni(a.idx_or_dummy);
     const FB_GLOBAL uint16_t *ux = uni(a.x);
     // row scales of the segments this workgroup touches (s0 .. s_last, consecutive)
-    auto rptr = [&](int j) { return segment(L, min(s0 + j, s_last)).r + rrow; };
+    auto rptr = [&](int j) { return gemv_segment(a.seg, L.kb, min(s0 + j, s_last)).r + rrow; };
     const uint16_t rr0 = *rptr(0), rr1 = *rptr(1), rr2 = *rptr(2), rr3 = *rptr(3), rr4 = *rptr(4), rr5 = *rptr(5);
 
     u32x4 wb[PF];
     int ps = s0, pcis = cis0, pidx = 0;  // next chunk to load and its index in the range
     auto load_next = [&]() -> u32x4 {
-      const SegRef S = segment(L, ps);
+      const SegRef S = gemv_segment(a.seg, L.kb, ps);
       const FB_GLOBAL u32x4 *base = S.bits + ((int64_t)ltile * S.nchunks + pcis) * kTileRows;
       const u32x4 w = __builtin_nontemporal_load(base + lane);
       const bool step = pidx < nch - 1;  // past the last chunk the last one is read again
@@ -411,7 +436,7 @@ __global__ __launch_bounds__(WAVES * 64) void lut_gemv_kernel(const GemvArgs a) 
       const int b = (ebase / kChunkCols) % NB;
       const int sg = seg_at(ch);
       const int cis = cis_at(ch);
-      const SegRef S = segment(L, sg);
+      const SegRef S = gemv_segment(a.seg, L.kb, sg);
       const bool brow = b < a.batch;  // uniform; batch rows past `batch` do not exist
       const uint32_t cc = (uint32_t)(cis * kChunkCols + (ebase & (kChunkCols - 1)) + lane);
       live[i] = brow & (cc < (uint32_t)S.len);  // non-short-circuit: a select, not a branch
