@@ -30,6 +30,21 @@ def weight_bytes(n: int, k: int, s: int, kb: int, ks: int) -> int:
     return packed_sign_bytes(n, k, s, kb, ks) + scales + index
 
 
+def grouped_weight_bytes(n: int, k: int, kb: int, ks: int, row_group: int, sal_group: int) -> int:
+    """Per-call weight-side bytes of the block-wise row-scale format.
+
+    Sign words of every segment, one fp16 row scale per (row, group of
+    `row_group` columns) per basis (global and salient alike), fp16 column
+    scales, int32 index; the salient width is sal_group per group.
+    """
+    ng = -(-k // row_group)
+    s = ng * sal_group if ks else 0
+    row_scales = 2 * (kb + ks) * n * ng
+    col_scales = 2 * (kb * k + ks * s)
+    index = 4 * s if ks else 0
+    return packed_sign_bytes(n, k, s, kb, ks) + row_scales + col_scales + index
+
+
 def activation_bytes(n: int, k: int, batch: int) -> int:
     """fp16 x in and fp16 y out."""
     return 2 * batch * (k + n)
@@ -52,8 +67,7 @@ def dense_f16_bytes(n: int, k: int, batch: int = 1) -> int:
 
 # ---------------------------------------------------------------------------
 # The pages' own storage and shared-memory models (used to pin the reading of
-# the printed numbers; the block-wise row-scale format itself is not on the
-# hot path built here).
+# the printed numbers).
 # ---------------------------------------------------------------------------
 
 def pages_abw_bits(kb: int, ks: int, group: int, salient_per_group: int) -> float:

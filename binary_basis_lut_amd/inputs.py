@@ -21,6 +21,12 @@ layer shapes; no trained weights, datasets or calibration text are used):
   calibration-set size (FluxBin summary, appendix D.4);
 * |S| for a fraction f of K is f*K rounded up to a multiple of 32.
 
+Block-wise row-scale layers (the pages' g128 storage, FluxBin summary,
+appendix C.2) draw one row scale per (row, 128-column group) per basis from
+the same distribution, and take their salient columns per group: the s
+columns of largest calibration variance inside each group of 128 (ties to
+the lower index), so that |S| = s * ceil(K / 128).
+
 Every tensor has its own stream: numpy PCG64 seeded by
 SeedSequence([base_seed, config, layer, linear, tensor]).
 """
@@ -117,6 +123,11 @@ class Layer:
     c_s: np.ndarray             # uint16 [ks][s]
     sal_idx: np.ndarray         # int32 [s]
     outliers: np.ndarray = field(default_factory=lambda: np.zeros(0, np.int64))
+    # 0: one row scale per row per basis (r_g [kb][n], r_s [ks][n]).  Else the
+    # block-wise format: r_g [kb][n][G], r_s [ks][n][G], G = ceil(k / row_group),
+    # with sal_group salient columns taken from every group of row_group columns.
+    row_group: int = 0
+    sal_group: int = 0
 
     def packed_bytes(self) -> int:
         return (self.bits_g.nbytes + self.bits_s.nbytes)
@@ -145,6 +156,46 @@ def make_layer(n: int, k: int, kb: int, ks: int, g: int, sal_frac: float = 0.0,
         r_s = np.zeros((0, n), np.uint16)
         c_s = np.zeros((0, 0), np.uint16)
     return Layer(n, k, s, kb, ks, g, bits_g, r_g, c_g, bits_s, r_s, c_s, sal, outl)
+
+
+def select_salient_grouped(rng: np.random.Generator, k: int, group: int, per_group: int, outliers: np.ndarray,
+                           mult: float = 20.0) -> np.ndarray:
+    """The per_group highest-variance channels of every `group`-column block, ascending int32."""
+    cal = rng.normal(0.0, 1.0, size=(NCAL, k))
+    if outliers.size:
+        cal[:, outliers] *= mult
+    var = cal.astype(np.float16).astype(np.float64).var(axis=0, ddof=1)
+    picked = []
+    for g0 in range(0, k, group):
+        cols = np.arange(g0, min(g0 + group, k))
+        if cols.size < per_group:
+            raise ValueError(f"group at column {g0} has {cols.size} columns, fewer than {per_group}")
+        order = np.lexsort((cols, -var[cols]))  # descending variance, ties to lower index
+        picked.append(np.sort(cols[order[:per_group]]))
+    return np.concatenate(picked).astype(np.int32)
+
+
+def make_grouped_layer(n: int, k: int, kb: int, ks: int, g: int, row_group: int = 128, sal_group: int = 8,
+                       outlier_frac: float = 0.0, seed: tuple = (0, 0, 0)) -> Layer:
+    """Draw one layer in the block-wise row-scale format (`seed` = (config, layer, linear))."""
+    ng = (k + row_group - 1) // row_group
+    outl = outlier_channels(stream(*seed, T_OUTLIER), k, outlier_frac)
+    bits_g = np.stack([sign_words(stream(*seed, T_BITS_G, b), n, k) for b in range(kb)])
+    r_g = scales(stream(*seed, T_R_G), (kb, n, ng))
+    c_g = scales(stream(*seed, T_C_G), (kb, k))
+    if ks:
+        sal = select_salient_grouped(stream(*seed, T_CAL), k, row_group, sal_group, outl)
+        s = int(sal.size)
+        bits_s = np.stack([sign_words(stream(*seed, T_BITS_S, b), n, s) for b in range(ks)])
+        r_s = scales(stream(*seed, T_R_S), (ks, n, ng))
+        c_s = scales(stream(*seed, T_C_S), (ks, s))
+    else:
+        s, sal_group = 0, 0
+        sal = np.zeros(0, np.int32)
+        bits_s = np.zeros((0, n, 0), np.uint32)
+        r_s = np.zeros((0, n, ng), np.uint16)
+        c_s = np.zeros((0, 0), np.uint16)
+    return Layer(n, k, s, kb, ks, g, bits_g, r_g, c_g, bits_s, r_s, c_s, sal, outl, row_group, sal_group)
 
 
 def make_x(layer: Layer, batch: int, seed: tuple = (0, 0, 0)) -> np.ndarray:
@@ -237,6 +288,40 @@ def dyadic_layer(n: int, k: int, kb: int, ks: int, g: int, s: int, seed: int = 7
         c_s = np.zeros((0, 0), np.uint16)
     layer = Layer(n, k, s, kb, ks, g, bits_g, r_g, c_g, bits_s, r_s, c_s, sal)
     return layer
+
+
+def dyadic_grouped_layer(n: int, k: int, kb: int, ks: int, g: int, row_group: int, sal_group: int,
+                         seed: int = 7) -> Layer:
+    """Block-wise row-scale layer with the dyadic value sets of dyadic_layer (exact in fp32).
+
+    Salient columns: sal_group random columns of every row_group-column block.
+    """
+    rng = stream(97, seed)
+    c_choices = np.array([0.25, 0.5, 1.0])
+    r_choices = np.array([0.5, 1.0])
+    ng = (k + row_group - 1) // row_group
+
+    def pick(choices, shape):
+        return choices[rng.integers(0, len(choices), size=shape)].astype(np.float16).view(np.uint16)
+
+    bits_g = np.stack([sign_words(rng, n, k) for _ in range(kb)])
+    r_g = pick(r_choices, (kb, n, ng))
+    c_g = pick(c_choices, (kb, k))
+    if ks:
+        sal = np.concatenate([np.sort(rng.choice(np.arange(g0, min(g0 + row_group, k)), size=sal_group,
+                                                 replace=False)) for g0 in range(0, k, row_group)]).astype(np.int32)
+        s = int(sal.size)
+        bits_s = np.stack([sign_words(rng, n, s) for _ in range(ks)])
+        r_s = pick(r_choices, (ks, n, ng))
+        c_s = pick(c_choices, (ks, s))
+    else:
+        s, sal_group = 0, 0
+        sal = np.zeros(0, np.int32)
+        bits_s = np.zeros((0, n, 0), np.uint32)
+        r_s = np.zeros((0, n, ng), np.uint16)
+        c_s = np.zeros((0, 0), np.uint16)
+    return Layer(n, k, s, kb, ks, g, bits_g, r_g, c_g, bits_s, r_s, c_s, sal, np.zeros(0, np.int64),
+                 row_group, sal_group)
 
 
 def dyadic_x(k: int, batch: int, seed: int = 8) -> np.ndarray:

@@ -28,14 +28,21 @@
  *     3.1.2: binary digits reinterpreted as {-1,+1});
  *   - bits are packed along the input dimension, least significant bit first:
  *     word w of a row holds column 32w+t at bit t; padding bits are 0;
- *   - the row scale is one fp16 value per output row per basis;
+ *   - the row scale is one fp16 value per output row per basis, or, in the
+ *     block-wise format, one per output row per basis per group of
+ *     `row_group` input columns (FluxBin summary, appendix C.2: the global
+ *     part keeps block-wise row scales; a salient column takes the scale of
+ *     the group its original column falls in);
  *   - the salient column scale c_s is stored in compact (VCM) order;
  *   - fp16 inputs, fp64 arithmetic, results returned in fp64.
  *
  * Parity status: the dense product is pinned by closed forms (popcount
  * identity, one-hot column selection, the LUT Tensor Core page's 1x4 times
  * 4xN worked shape with dyadic inputs), exact integer brute force on tiny
- * problems, and agreement with the separately written LUT route.
+ * problems, and agreement with the separately written LUT route.  The
+ * block-wise row scales are pinned by reduction to the per-row product (all
+ * group scales of a row equal; a single non-zero group on activations
+ * zeroed outside it) and by exact integer brute force.
  */
 #include <math.h>
 #include <stdint.h>
@@ -165,6 +172,24 @@ ORC_EXPORT void orc_tile_words(const uint32_t *canon, int64_t rows, int64_t cols
   }
 }
 
+/* Tiled row-scale layout of the block-wise format: a [rows][groups] fp16
+ * matrix whose groups fall `m` to a 128-column chunk.  Rows are padded to a
+ * multiple of 64 and groups to a multiple of m; element (row r, group q) is
+ * stored at ((floor(r/64) * NC + floor(q/m)) * 64 + r mod 64) * m + q mod m,
+ * NC = ceil(groups/m), so that a row's scales for one chunk are contiguous
+ * and a 64-row tile's scales for one chunk form one block.  Padding is 0. */
+ORC_EXPORT int64_t orc_tiled_scale_elems(int64_t rows, int64_t groups, int64_t m) {
+  return ((rows + 63) / 64) * ((groups + m - 1) / m) * 64 * m;
+}
+
+ORC_EXPORT void orc_tile_scales(const uint16_t *canon, int64_t rows, int64_t groups, int64_t m, uint16_t *tiled) {
+  int64_t nc = (groups + m - 1) / m;
+  memset(tiled, 0, (size_t)orc_tiled_scale_elems(rows, groups, m) * sizeof(uint16_t));
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t q = 0; q < groups; ++q)
+      tiled[(((r / 64) * nc + q / m) * 64 + (r % 64)) * m + (q % m)] = canon[r * groups + q];
+}
+
 /* VCM on sign bits: compact column c of the destination is source column
  * idx[c].  src canonical [rows][ceil(k/32)], dst canonical [rows][ceil(s/32)]. */
 ORC_EXPORT void orc_vcm_gather_bits(const uint32_t *src, int64_t rows, int64_t k, const int32_t *idx,
@@ -185,14 +210,23 @@ ORC_EXPORT void orc_vcm_gather_bits(const uint32_t *src, int64_t rows, int64_t k
 typedef struct {
   int64_t n, k, s;
   int32_t kb, ks;
+  int64_t row_group;      /* 0: one row scale per row; else columns per row-scale group */
+  int64_t ngroups;        /* row scales per row per basis: 1, or ceil(k / row_group) */
   const uint32_t *bits_g; /* [kb][n][ceil(k/32)] */
-  const uint16_t *r_g;    /* [kb][n] */
+  const uint16_t *r_g;    /* [kb][n][ngroups] */
   const uint16_t *c_g;    /* [kb][k] */
   const uint32_t *bits_s; /* [ks][n][ceil(s/32)] */
-  const uint16_t *r_s;    /* [ks][n] */
+  const uint16_t *r_s;    /* [ks][n][ngroups] */
   const uint16_t *c_s;    /* [ks][s], compact order */
   const int32_t *idx;     /* [s], salient column of compact column c */
 } orc_layer;
+
+/* Row-scale group of input column j (0 when there is one scale per row). */
+static inline int64_t group_of(int64_t row_group, int64_t j) { return row_group ? j / row_group : 0; }
+
+static inline int64_t group_count(int64_t row_group, int64_t k) {
+  return row_group ? (k + row_group - 1) / row_group : 1;
+}
 
 static double *halves(const uint16_t *h, int64_t count) {
   double *d = (double *)malloc((size_t)(count > 0 ? count : 1) * sizeof(double));
@@ -207,27 +241,37 @@ static void reconstruct_row(const orc_layer *L, const double *cg, const double *
   for (int64_t j = 0; j < L->k; ++j) wrow[j] = 0.0;
   for (int32_t b = 0; b < L->kb; ++b) {
     const uint32_t *row = L->bits_g + ((int64_t)b * L->n + i) * wk;
-    double r = orc_half_to_double(L->r_g[(int64_t)b * L->n + i]);
-    for (int64_t j = 0; j < L->k; ++j) wrow[j] += r * sign_at(row, j) * cg[(int64_t)b * L->k + j];
+    const uint16_t *rrow = L->r_g + ((int64_t)b * L->n + i) * L->ngroups;
+    for (int64_t j = 0; j < L->k; ++j) {
+      double r = orc_half_to_double(rrow[group_of(L->row_group, j)]);
+      wrow[j] += r * sign_at(row, j) * cg[(int64_t)b * L->k + j];
+    }
   }
   for (int32_t b = 0; b < L->ks; ++b) {
     const uint32_t *row = L->bits_s + ((int64_t)b * L->n + i) * ws;
-    double r = orc_half_to_double(L->r_s[(int64_t)b * L->n + i]);
-    for (int64_t c = 0; c < L->s; ++c)
+    const uint16_t *rrow = L->r_s + ((int64_t)b * L->n + i) * L->ngroups;
+    for (int64_t c = 0; c < L->s; ++c) {
+      double r = orc_half_to_double(rrow[group_of(L->row_group, L->idx[c])]);
       wrow[L->idx[c]] += r * sign_at(row, c) * cs[(int64_t)b * L->s + c];
+    }
   }
 }
 
 /* y[b][t] = sum_j W_hat[rows[t]][j] * x[b][j] and mag[b][t] = sum_j |W_hat x|
  * for each listed row t (all n rows when rows == NULL; then nrows must be n).
- * y and mag are [batch][nrows].  nthreads <= 0 uses the OpenMP default. */
-ORC_EXPORT int orc_gemv_dense(int64_t n, int64_t k, int64_t s, int32_t kb, int32_t ks,
+ * y and mag are [batch][nrows].  nthreads <= 0 uses the OpenMP default.
+ * row_group = 0: r_g [kb][n], r_s [ks][n]; row_group > 0: r_g [kb][n][G],
+ * r_s [ks][n][G] with G = ceil(k / row_group), and the salient scale of
+ * compact column c is that of group floor(idx[c] / row_group).
+ * Returns 1 for a row index out of range, 2 for a negative row_group. */
+ORC_EXPORT int orc_gemv_dense(int64_t n, int64_t k, int64_t s, int32_t kb, int32_t ks, int64_t row_group,
                               const uint32_t *bits_g, const uint16_t *r_g, const uint16_t *c_g,
                               const uint32_t *bits_s, const uint16_t *r_s, const uint16_t *c_s,
                               const int32_t *idx, const uint16_t *x, int64_t batch,
                               const int64_t *rows, int64_t nrows, double *y, double *mag,
                               int32_t nthreads) {
-  orc_layer L = {n, k, s, kb, ks, bits_g, r_g, c_g, bits_s, r_s, c_s, idx};
+  if (row_group < 0) return 2;
+  orc_layer L = {n, k, s, kb, ks, row_group, group_count(row_group, k), bits_g, r_g, c_g, bits_s, r_s, c_s, idx};
   double *cg = halves(c_g, (int64_t)kb * k);
   double *cs = halves(c_s, (int64_t)ks * s);
   double *xd = halves(x, batch * k);
@@ -306,21 +350,29 @@ static inline uint32_t pattern_at(const uint32_t *row_words, int32_t g, int64_t 
 
 /* y via the LUT route in fp64: per segment and batch row, build every
  * sub-vector's 2^g table from the scale-fused inputs, look each row's bit
- * pattern up, accumulate, then apply the row scale after accumulation.
- * y is [batch][nrows] like orc_gemv_dense. */
-ORC_EXPORT int orc_gemv_lut(int64_t n, int64_t k, int64_t s, int32_t kb, int32_t ks, int32_t g,
+ * pattern up and accumulate per row-scale group, then apply each group's row
+ * scale to its partial sum and add the groups (with row_group = 0 there is
+ * one group: the row scale is applied once, after accumulation).
+ * y is [batch][nrows] like orc_gemv_dense, scales laid out as there.
+ * Returns 1 for an unsupported g, 2 when a sub-vector's columns fall in two
+ * row-scale groups (the block-wise format then has no per-group sum). */
+ORC_EXPORT int orc_gemv_lut(int64_t n, int64_t k, int64_t s, int32_t kb, int32_t ks, int64_t row_group, int32_t g,
                             const uint32_t *bits_g, const uint16_t *r_g, const uint16_t *c_g,
                             const uint32_t *bits_s, const uint16_t *r_s, const uint16_t *c_s,
                             const int32_t *idx, const uint16_t *x, int64_t batch,
                             const int64_t *rows, int64_t nrows, double *y) {
   if (g <= 0 || g > 16 || 32 % g) return 1;
+  if (row_group < 0) return 2;
+  const int64_t ng = group_count(row_group, k);
+  int err = 0;
   double *cg = halves(c_g, (int64_t)kb * k);
   double *cs = halves(c_s, (int64_t)ks * s);
   double *xd = halves(x, batch * k);
   int64_t tsize = (int64_t)1 << g;
   double v[16];
+  double *partial = (double *)malloc((size_t)ng * sizeof(double));
   for (int64_t i = 0; i < batch * nrows; ++i) y[i] = 0.0;
-  for (int32_t seg = 0; seg < kb + ks; ++seg) {
+  for (int32_t seg = 0; seg < kb + ks && !err; ++seg) {
     int salient = seg >= kb;
     int32_t sb = salient ? seg - kb : seg;
     int64_t len = salient ? s : k;
@@ -328,10 +380,20 @@ ORC_EXPORT int orc_gemv_lut(int64_t n, int64_t k, int64_t s, int32_t kb, int32_t
     int64_t wpr = words_per_row(len);
     const double *c = salient ? cs + (int64_t)sb * s : cg + (int64_t)sb * k;
     const uint32_t *bits = salient ? bits_s + (int64_t)sb * n * wpr : bits_g + (int64_t)sb * n * wpr;
-    const uint16_t *r = salient ? r_s + (int64_t)sb * n : r_g + (int64_t)sb * n;
+    const uint16_t *r = salient ? r_s + (int64_t)sb * n * ng : r_g + (int64_t)sb * n * ng;
+    /* row-scale group of every sub-vector: that of its columns' original positions */
+    int64_t *sub_group = (int64_t *)malloc((size_t)(nsub > 0 ? nsub : 1) * sizeof(int64_t));
+    for (int64_t j = 0; j < nsub; ++j) {
+      for (int32_t t = 0; t < g; ++t) {
+        int64_t col = j * g + t;
+        if (col >= len) break;
+        int64_t grp = group_of(row_group, salient ? idx[col] : col);
+        if (t == 0) sub_group[j] = grp;
+        else if (grp != sub_group[j]) err = 2;
+      }
+    }
     double *tables = (double *)malloc((size_t)(nsub > 0 ? nsub : 1) * tsize * sizeof(double));
-    double *acc = (double *)calloc((size_t)(nrows > 0 ? nrows : 1), sizeof(double));
-    for (int64_t b = 0; b < batch; ++b) {
+    for (int64_t b = 0; b < batch && !err; ++b) {
       const double *xb = xd + b * k;
       for (int64_t j = 0; j < nsub; ++j) {
         fused_inputs(g, j, len, c, xb, salient ? idx : NULL, v);
@@ -340,22 +402,21 @@ ORC_EXPORT int orc_gemv_lut(int64_t n, int64_t k, int64_t s, int32_t kb, int32_t
       for (int64_t t = 0; t < nrows; ++t) {
         int64_t i = rows ? rows[t] : t;
         const uint32_t *row = bits + i * wpr;
+        for (int64_t q = 0; q < ng; ++q) partial[q] = 0.0;
+        for (int64_t j = 0; j < nsub; ++j) partial[sub_group[j]] += tables[j * tsize + pattern_at(row, g, j)];
         double a = 0.0;
-        for (int64_t j = 0; j < nsub; ++j) a += tables[j * tsize + pattern_at(row, g, j)];
-        acc[t] = a;
-      }
-      for (int64_t t = 0; t < nrows; ++t) {
-        int64_t i = rows ? rows[t] : t;
-        y[b * nrows + t] += orc_half_to_double(r[i]) * acc[t];
+        for (int64_t q = 0; q < ng; ++q) a += orc_half_to_double(r[i * ng + q]) * partial[q];
+        y[b * nrows + t] += a;
       }
     }
     free(tables);
-    free(acc);
+    free(sub_group);
   }
+  free(partial);
   free(cg);
   free(cs);
   free(xd);
-  return 0;
+  return err;
 }
 
 /* Half tables as exported by the GPU library's table builder:

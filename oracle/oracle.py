@@ -66,9 +66,12 @@ def _declare(L):
     L.orc_tile_words.argtypes = [P, I64, I64, P]
     L.orc_vcm_gather_bits.argtypes = [P, I64, I64, P, I64, P]
     L.orc_gemv_dense.restype = ctypes.c_int
-    L.orc_gemv_dense.argtypes = [I64, I64, I64, I32, I32, P, P, P, P, P, P, P, P, I64, P, I64, P, P, I32]
+    L.orc_gemv_dense.argtypes = [I64, I64, I64, I32, I32, I64, P, P, P, P, P, P, P, P, I64, P, I64, P, P, I32]
     L.orc_gemv_lut.restype = ctypes.c_int
-    L.orc_gemv_lut.argtypes = [I64, I64, I64, I32, I32, I32, P, P, P, P, P, P, P, P, I64, P, I64, P]
+    L.orc_gemv_lut.argtypes = [I64, I64, I64, I32, I32, I64, I32, P, P, P, P, P, P, P, P, I64, P, I64, P]
+    L.orc_tiled_scale_elems.restype = I64
+    L.orc_tiled_scale_elems.argtypes = [I64, I64, I64]
+    L.orc_tile_scales.argtypes = [P, I64, I64, I64, P]
     L.orc_lut_explicit.argtypes = [I32, P, P]
     L.orc_half_luts.restype = ctypes.c_int
     L.orc_half_luts.argtypes = [I64, I64, I32, I32, I32, P, P, P, P, I64, P, P]
@@ -130,6 +133,15 @@ def tile_words(canon, cols: int) -> np.ndarray:
     return out
 
 
+def tile_scales(canon, m: int) -> np.ndarray:
+    """Row scales uint16 [rows][groups] -> tiled block-wise layout (flat uint16), m groups per chunk."""
+    canon = _c(canon, np.uint16)
+    rows, groups = canon.shape
+    out = np.empty(lib().orc_tiled_scale_elems(rows, groups, m), np.uint16)
+    lib().orc_tile_scales(_p(canon), rows, groups, m, _p(out))
+    return out
+
+
 def vcm_gather_bits(src, k: int, idx) -> np.ndarray:
     src = _c(src, np.uint32)
     idx = _c(idx, np.int32)
@@ -157,8 +169,16 @@ def _layer_arrays(layer):
             bits_s, r_s, c_s, idx)
 
 
+def _row_group(layer) -> int:
+    return int(getattr(layer, "row_group", 0) or 0)
+
+
 def gemv_dense(layer, x, rows=None, nthreads: int = 0):
-    """fp64 y = W_hat x and mag = sum_j |W_hat_ij x_j|, each [batch][len(rows) or n]."""
+    """fp64 y = W_hat x and mag = sum_j |W_hat_ij x_j|, each [batch][len(rows) or n].
+
+    Row scales are per row ([basis][n]) or, when ``layer.row_group`` > 0,
+    block-wise ([basis][n][ceil(k / row_group)]).
+    """
     x = _c(x, np.uint16)
     batch = x.shape[0]
     arrs = _layer_arrays(layer)
@@ -166,10 +186,10 @@ def gemv_dense(layer, x, rows=None, nthreads: int = 0):
     nrows = layer.n if rows is None else rows_a.size
     y = np.empty((batch, nrows), np.float64)
     mag = np.empty((batch, nrows), np.float64)
-    err = lib().orc_gemv_dense(layer.n, layer.k, layer.s, layer.kb, layer.ks, *[_p(a) for a in arrs],
-                               _p(x), batch, _p(rows_a), nrows, _p(y), _p(mag), nthreads)
+    err = lib().orc_gemv_dense(layer.n, layer.k, layer.s, layer.kb, layer.ks, _row_group(layer),
+                               *[_p(a) for a in arrs], _p(x), batch, _p(rows_a), nrows, _p(y), _p(mag), nthreads)
     if err:
-        raise ValueError("row index out of range")
+        raise ValueError("row index out of range" if err == 1 else "negative row_group")
     return y, mag
 
 
@@ -182,10 +202,10 @@ def gemv_lut(layer, x, g: int | None = None, rows=None):
     nrows = layer.n if rows is None else rows_a.size
     y = np.empty((batch, nrows), np.float64)
     g = layer.g if g is None else g
-    err = lib().orc_gemv_lut(layer.n, layer.k, layer.s, layer.kb, layer.ks, g, *[_p(a) for a in arrs],
-                             _p(x), batch, _p(rows_a), nrows, _p(y))
+    err = lib().orc_gemv_lut(layer.n, layer.k, layer.s, layer.kb, layer.ks, _row_group(layer), g,
+                             *[_p(a) for a in arrs], _p(x), batch, _p(rows_a), nrows, _p(y))
     if err:
-        raise ValueError("unsupported g")
+        raise ValueError("unsupported g" if err == 1 else "a sub-vector spans two row-scale groups")
     return y
 
 

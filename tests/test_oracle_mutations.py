@@ -15,6 +15,7 @@ import pytest
 
 from binary_basis_lut_amd import inputs as I
 
+from .test_oracle_grouped import exact_y_grouped
 from .test_oracle_pins import bits_of, exact_y, f16, layer_from
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -33,12 +34,20 @@ MUTANTS = {
     "salient_scale_indexed_by_column": ("wrow[L->idx[c]] += r * sign_at(row, c) * cs[(int64_t)b * L->s + c];",
                                         "wrow[L->idx[c]] += r * sign_at(row, c) * cs[(int64_t)b * L->s + L->idx[c] % L->s];"),
     "last_basis_dropped": ("for (int32_t b = 0; b < L->kb; ++b) {", "for (int32_t b = 0; b + 1 < L->kb; ++b) {"),
-    "row_scale_transposed": ("double r = orc_half_to_double(L->r_g[(int64_t)b * L->n + i]);",
-                             "double r = orc_half_to_double(L->r_g[(int64_t)b * L->n + (i * 7 + 1) % L->n]);"),
+    "row_scale_transposed": ("const uint16_t *rrow = L->r_g + ((int64_t)b * L->n + i) * L->ngroups;",
+                             "const uint16_t *rrow = L->r_g + ((int64_t)b * L->n + (i * 7 + 1) % L->n) * L->ngroups;"),
     "column_scale_wrong_basis": ("wrow[j] += r * sign_at(row, j) * cg[(int64_t)b * L->k + j];",
                                  "wrow[j] += r * sign_at(row, j) * cg[j];"),
     "product_not_accumulated": ("acc += p;\n          am += fabs(p);", "acc = p;\n          am += fabs(p);"),
     "half_rounding_truncates": ("double q = rint(ldexp(a, 10 - e));", "double q = floor(ldexp(a, 10 - e));"),
+    "grouped_salient_scale_by_compact_column": ("rrow[group_of(L->row_group, L->idx[c])]",
+                                                "rrow[group_of(L->row_group, c)]"),
+    "grouped_global_scale_first_group_only": ("double r = orc_half_to_double(rrow[group_of(L->row_group, j)]);",
+                                              "double r = orc_half_to_double(rrow[0]);"),
+    "grouped_scales_of_first_basis": ("const uint16_t *rrow = L->r_g + ((int64_t)b * L->n + i) * L->ngroups;",
+                                      "const uint16_t *rrow = L->r_g + ((int64_t)0 * L->n + i) * L->ngroups;"),
+    "grouped_group_boundary_off_by_one": ("{ return row_group ? j / row_group : 0; }",
+                                          "{ return row_group ? (j > 0 ? (j - 1) / row_group : 0) : 0; }"),
 }
 
 
@@ -98,7 +107,37 @@ def chk_half_numpy(O):
     return np.array_equal(O.double_to_half(v), v.astype(np.float16).view(np.uint16))
 
 
-CHECKS = [chk_popcount, chk_one_hot, chk_bruteforce, chk_half_numpy]
+def chk_grouped_one_hot(O):
+    """Block-wise format: only group q of one basis scaled equals the per-row product on that group."""
+    n, k = 20, 512
+    lay = I.make_grouped_layer(n, k, 2, 2, 4, 128, 8, seed=(39, 0, 0))
+    x = I.make_x(lay, 1, seed=(39, 0, 0))
+    rv = I.scales(I.stream(40), (n,))
+    for basis, q in [(("g", 1), 2), (("s", 0), 1), (("s", 1), 3)]:
+        r_g = np.zeros((2, n, 4), np.uint16)
+        r_s = np.zeros((2, n, 4), np.uint16)
+        rr_g = np.zeros((2, n), np.uint16)
+        rr_s = np.zeros((2, n), np.uint16)
+        (r_g if basis[0] == "g" else r_s)[basis[1], :, q] = rv
+        (rr_g if basis[0] == "g" else rr_s)[basis[1]] = rv
+        xm = x.copy()
+        xm[:, :q * 128] = 0
+        xm[:, (q + 1) * 128:] = 0
+        grp = I.Layer(n, k, lay.s, 2, 2, 4, lay.bits_g, r_g, lay.c_g, lay.bits_s, r_s, lay.c_s, lay.sal_idx,
+                      lay.outliers, 128, 8)
+        row = I.Layer(n, k, lay.s, 2, 2, 4, lay.bits_g, rr_g, lay.c_g, lay.bits_s, rr_s, lay.c_s, lay.sal_idx)
+        if not np.array_equal(O.gemv_dense(grp, x)[0], O.gemv_dense(row, xm)[0]):
+            return False
+    return True
+
+
+def chk_grouped_bruteforce(O):
+    lay = I.dyadic_grouped_layer(4, 384, 2, 2, 4, 128, 8, seed=5)
+    x = I.dyadic_x(384, 1, seed=6)
+    return np.array_equal(O.gemv_dense(lay, x)[0], exact_y_grouped(lay, x))
+
+
+CHECKS = [chk_popcount, chk_one_hot, chk_bruteforce, chk_half_numpy, chk_grouped_one_hot, chk_grouped_bruteforce]
 
 
 def test_unmutated_oracle_passes_every_check(orc):
