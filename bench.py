@@ -13,6 +13,11 @@ R calls are captured once in a HIP graph (torch.cuda.CUDAGraph) and the graph
 is replayed; the timed region is bracketed by torch.cuda.synchronize() and
 HIP events recorded on the replay stream.
 
+--format blockwise measures the same shape in the pages' block-wise row-scale
+storage instead (one fp16 row scale per row per basis per 128-column group,
+two global and two salient bases, --sal-group salient columns per group:
+about 2.63 bits per weight at 8, 2.75 at 16; FluxBin summary, appendix C.2).
+
 Prints one JSON line.  Extra figures go to --out (default gpurun_out/bench_detail.json).
 """
 from __future__ import annotations
@@ -38,7 +43,8 @@ PAGES_A100_US = 41.0    # FluxBin summary, appendix E.4: isolated 4096x4096 2-bi
 
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for p in ["binary_basis_lut_amd/csrc/kernels.hpp", "binary_basis_lut_amd/csrc/fluxbin.hip"]:
+    for p in ["binary_basis_lut_amd/csrc/common.hpp", "binary_basis_lut_amd/csrc/gemv_kernel.hpp",
+              "binary_basis_lut_amd/csrc/fluxbin.hip"]:
         h.update((ROOT / p).read_bytes())
     return h.hexdigest()[:16]
 
@@ -57,10 +63,10 @@ def measured_traffic(bytes_per_launch_alg: float):
     return d.get("hbm_bytes_per_launch"), d.get("note")
 
 
-def cpu_baseline(layer, x, budget_s: float):
-    """Time the fp64 oracle (as it is) on the host cores: whole q_proj GEMVs of one weight set."""
+def cpu_baseline(layer, x, budget_s: float, wb: int):
+    """Time the fp64 oracle (as it is) on the host cores: whole q_proj GEMVs of one weight set
+    (wb = the call's weight-side bytes)."""
     from oracle import oracle as O
-    from binary_basis_lut_amd import accounting as A
     threads = len(os.sched_getaffinity(0))
     O.gemv_dense(layer, x, nthreads=threads)  # warm caches and thread pool
     calls, t0 = 0, time.perf_counter()
@@ -71,13 +77,13 @@ def cpu_baseline(layer, x, budget_s: float):
         if el >= budget_s:
             break
     per_call = el / calls
-    wb = A.weight_bytes(layer.n, layer.k, layer.s, layer.kb, layer.ks)
+    fmt = "block-wise row scales" if getattr(layer, "row_group", 0) else "per-row scales"
     return {
         "value": round(wb / per_call / 1e9, 4),
         "unit": "GB/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": f"{calls} full 4096x4096 q_proj GEMVs (2 global + 1 salient basis, fp64 dense "
+        "sample": f"{calls} full 4096x4096 q_proj GEMVs ({layer.kb} global + {layer.ks} salient bases, {fmt}, fp64 dense "
                   f"reconstruction row by row, OpenMP over rows), {el:.1f} s; {per_call * 1e3:.2f} ms per call",
     }
 
@@ -92,6 +98,10 @@ def main() -> int:
     ap.add_argument("--no-graph", action="store_true", help="launch every call from Python instead")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--format", choices=["per-row", "blockwise"], default="per-row",
+                    help="row-scale storage: per row per basis (default), or per row per 128-column group")
+    ap.add_argument("--sal-group", type=int, default=8, choices=[8, 16],
+                    help="blockwise: salient columns per 128-column group")
     ap.add_argument("--out", default=str(ROOT / "gpurun_out" / "bench_detail.json"))
     args = ap.parse_args()
 
@@ -111,6 +121,17 @@ def main() -> int:
     torch.cuda.set_device(0)
     wl = I.WORKLOADS[WORKLOAD_ID]
     sh = wl.shapes[0]
+    blockwise = args.format == "blockwise"
+    kb, ks = (2, 2) if blockwise else (wl.kb, wl.ks)
+
+    def make(i):
+        if blockwise:
+            lay = I.make_grouped_layer(sh.n, sh.k, kb, ks, wl.g, 128, args.sal_group, outlier_frac=wl.outlier_frac,
+                                       seed=(WORKLOAD_ID, i, 100 + args.sal_group))
+            return lay, I.make_x(lay, 1, seed=(WORKLOAD_ID, i, 100 + args.sal_group))
+        lay = I.workload_layer(WORKLOAD_ID, 0, i)
+        return lay, I.workload_x(WORKLOAD_ID, lay, 1, 0, i)
+
     R = max(1, args.sets)
     steps = max(R, int(math.ceil(args.steps / R)) * R)
     warm = max(R, int(math.ceil(args.warmup / R)) * R)
@@ -118,8 +139,7 @@ def main() -> int:
     t_gen = time.perf_counter()
     layers, dls, xs, ys = [], [], [], []
     for i in range(R):
-        lay = I.workload_layer(WORKLOAD_ID, 0, i)
-        x_np = I.workload_x(WORKLOAD_ID, lay, 1, 0, i)
+        lay, x_np = make(i)
         dl = F.DeviceLayer(lay, max_batch=1, chunks_per_block=args.chunks_per_block)
         dls.append(dl)
         xs.append(torch.from_numpy(x_np.view(np.int16)).cuda())
@@ -130,7 +150,8 @@ def main() -> int:
     t_gen = time.perf_counter() - t_gen
     plan = dls[0].plan
     lay0, x0 = layers[0]
-    bytes_per_gemv = A.weight_bytes(sh.n, sh.k, lay0.s, wl.kb, wl.ks)
+    bytes_per_gemv = (A.grouped_weight_bytes(sh.n, sh.k, kb, ks, 128, args.sal_group) if blockwise
+                      else A.weight_bytes(sh.n, sh.k, lay0.s, wl.kb, wl.ks))
     act_bytes = A.activation_bytes(sh.n, sh.k, 1)
 
     # parity spot check of the timed configuration (set 0) against the oracle
@@ -203,8 +224,8 @@ def main() -> int:
     dense_us = d0.elapsed_time(d1) * 1e3 / (8 * Rd)
     del wd
 
-    traffic, traffic_note = measured_traffic(bytes_per_gemv)
-    cpu = None if args.no_cpu else cpu_baseline(lay0, x0, args.cpu_seconds)
+    traffic, traffic_note = (None, "no counters for this format") if blockwise else measured_traffic(bytes_per_gemv)
+    cpu = None if args.no_cpu else cpu_baseline(lay0, x0, args.cpu_seconds, bytes_per_gemv)
 
     line = {
         "metric": "packed-weight GB/s (LUT GEMV, weight-side bytes per call / time per call)",
@@ -220,8 +241,9 @@ def main() -> int:
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": wl.name,
-            "k": sh.k, "n": sh.n, "kb": wl.kb, "ks": wl.ks, "s": lay0.s, "g": wl.g, "batch": 1,
+            "workload": (f"llama2_7b_q_proj_4096x4096_kb2_ks2_g128_s{args.sal_group}_g4" if blockwise else wl.name),
+            "row_scales": "per 128-column group" if blockwise else "per row",
+            "k": sh.k, "n": sh.n, "kb": kb, "ks": ks, "s": lay0.s, "g": wl.g, "batch": 1,
             "weight_sets_resident": R,
             "bytes_per_gemv": bytes_per_gemv,
             "us_per_gemv": round(us_per_gemv, 4),

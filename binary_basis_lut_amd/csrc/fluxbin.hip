@@ -1,7 +1,9 @@
 // fluxbin.hip -- C ABI of libfluxbin.so (declared in include/fluxbin.h).
 //
 // Host side: argument validation (pure host work, before any HIP call),
-// work planning, kernel launches.  The kernels live in kernels.hpp.
+// work planning, kernel launches.  The GEMV kernel instances live in the
+// gemv_g*_rs*.hip translation units (gemv_kernel.hpp), the other kernels in
+// aux_kernels.hpp.
 #include "fluxbin.h"
 
 #include <hip/hip_runtime.h>
@@ -14,7 +16,7 @@
 #include <new>
 #include <vector>
 
-#include "kernels.hpp"
+#include "aux_kernels.hpp"
 
 using namespace fluxbin;
 
@@ -53,6 +55,8 @@ struct Plan {
   int32_t row_tiles;
   int32_t row_blocks;
   int32_t total_chunks;
+  int32_t gchunks;     // chunks of the first range part (all chunks, or the global ones when block-wise)
+  int32_t gsplits;     // workgroup ranges over the first part
   int32_t splits;
   int64_t n_pad;
   size_t acc_bytes;    // packed split-reduction words (splits > 1)
@@ -89,6 +93,22 @@ fluxbin_status validate_shape(const fluxbin_layer_desc *d) {
                 kMaxCpb);
   if (d->waves_per_block != 0 && d->waves_per_block != 4 && d->waves_per_block != 8)
     return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "waves_per_block = %d (0, 4 or 8)", d->waves_per_block);
+  if (d->row_group != 0 && d->row_group != kChunkCols)
+    return fail(FLUXBIN_ERR_UNSUPPORTED, "row_group = %d (supported: 0 = per row, 128 = block-wise)", d->row_group);
+  if (d->row_group == 0 || d->ks == 0) {
+    if (d->sal_group != 0)
+      return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "sal_group = %d must be 0 without block-wise salient bases",
+                  d->sal_group);
+  } else {
+    if (d->sal_group != 8 && d->sal_group != 16)
+      return fail(FLUXBIN_ERR_UNSUPPORTED, "sal_group = %d (supported: 8, 16)", d->sal_group);
+    if (d->sal_group % d->g)
+      return fail(FLUXBIN_ERR_UNSUPPORTED, "sal_group = %d is not a multiple of g = %d", d->sal_group, d->g);
+    const int64_t want = cdiv(d->k, d->row_group) * d->sal_group;
+    if (d->s != want)
+      return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "s = %lld, block-wise format needs sal_group * ceil(k / 128) = %lld",
+                  (long long)d->s, (long long)want);
+  }
   return FLUXBIN_OK;
 }
 
@@ -131,7 +151,15 @@ fluxbin_status make_plan(const fluxbin_layer_desc *d, Plan *p) {
   p->row_blocks = (int32_t)cdiv(p->row_tiles, p->waves);
   p->cpb = d->chunks_per_block ? d->chunks_per_block : auto_cpb(cmax, p->waves, p->row_tiles, p->total_chunks);
   p->pf = prefetch_depth(p->cpb);
-  p->splits = (int32_t)cdiv(p->total_chunks, p->cpb);
+  if (d->row_group) {
+    // block-wise: global and salient chunks take separate workgroup ranges
+    p->gchunks = (int32_t)(d->kb * cdiv(d->k, kChunkCols));
+    p->gsplits = (int32_t)cdiv(p->gchunks, p->cpb);
+    p->splits = p->gsplits + (int32_t)cdiv(p->total_chunks - p->gchunks, p->cpb);
+  } else {
+    p->gchunks = p->total_chunks;
+    p->splits = p->gsplits = (int32_t)cdiv(p->total_chunks, p->cpb);
+  }
   if (p->splits > kMaxSplits)
     return fail(FLUXBIN_ERR_UNSUPPORTED, "%d column splits exceed %d (too many 128-column chunks for chunks_per_block %d)",
                 p->splits, kMaxSplits, p->cpb);
@@ -141,12 +169,10 @@ fluxbin_status make_plan(const fluxbin_layer_desc *d, Plan *p) {
 
 }  // namespace
 
-typedef void (*gemv_fn)(const GemvArgs);
-
 struct fluxbin_layer {
   fluxbin_layer_desc d;
   Plan plan;
-  gemv_fn fn;                 // kernel instance for (g, batch width, waves)
+  gemv_fn fn;                 // kernel instance for (g, row-scale format, batch width, waves, depth)
   size_t lds;                 // its dynamic LDS bytes
   const int32_t *idx_or_dummy;  // sal_idx, or the library's one-element zero array when ks == 0
   bool fault_launch;
@@ -161,35 +187,9 @@ __device__ int32_t g_zero_index[4];
 // ---------------------------------------------------------------------------
 namespace {
 
-template <int G, int NB, int W>
-gemv_fn pick_pf(int pf) {
-  return pf == 8 ? lut_gemv_kernel<G, NB, W, 8>
-         : pf == 4 ? lut_gemv_kernel<G, NB, W, 4>
-         : pf == 2 ? lut_gemv_kernel<G, NB, W, 2>
-                   : nullptr;
-}
-
-template <int G, int NB>
-gemv_fn pick_waves(int waves, int pf) {
-  return waves == 8 ? pick_pf<G, NB, 8>(pf) : waves == 4 ? pick_pf<G, NB, 4>(pf) : nullptr;
-}
-
-gemv_fn pick_gemv(int g, int nb, int waves, int pf) {
-  if (g == 4) {
-    switch (nb) {
-      case 1: return pick_waves<4, 1>(waves, pf);
-      case 2: return pick_waves<4, 2>(waves, pf);
-      case 4: return pick_waves<4, 4>(waves, pf);
-      case 8: return pick_waves<4, 8>(waves, pf);
-      case 16: return pick_waves<4, 16>(waves, pf);
-    }
-  } else if (g == 8) {
-    switch (nb) {
-      case 1: return pick_waves<8, 1>(waves, pf);
-      case 2: return pick_waves<8, 2>(waves, pf);
-      case 4: return pick_waves<8, 4>(waves, pf);
-    }
-  }
+gemv_fn pick_gemv(int g, int rs, int nb, int waves, int pf) {
+  if (g == 4) return rs ? gemv_pick_g4_rs1(nb, waves, pf) : gemv_pick_g4_rs0(nb, waves, pf);
+  if (g == 8) return rs ? gemv_pick_g8_rs1(nb, waves, pf) : gemv_pick_g8_rs0(nb, waves, pf);
   return nullptr;
 }
 
@@ -219,18 +219,22 @@ LayerArgs layer_args(const fluxbin_layer_desc &d) {
 void gemv_segments(const fluxbin_layer_desc &d, SegDesc (&seg)[kMaxSeg]) {
   const int64_t tw_g = fluxbin_tiled_words(d.n, d.k), tw_s = d.ks > 0 ? fluxbin_tiled_words(d.n, d.s) : 0;
   const int32_t nc_g = (int32_t)cdiv(d.k, kChunkCols), nc_s = d.ks > 0 ? (int32_t)cdiv(d.s, kChunkCols) : 1;
+  // row-scale elements per basis: n, or the tiled block-wise blocks
+  const int64_t groups = d.row_group ? cdiv(d.k, d.row_group) : 0;
+  const int64_t rs_g = d.row_group ? fluxbin_tiled_scale_elems(d.n, groups, 1) : d.n;
+  const int64_t rs_s = d.row_group && d.ks > 0 ? fluxbin_tiled_scale_elems(d.n, groups, kChunkCols / d.sal_group) : d.n;
   int i = 0;
   for (int b = 0; b < d.kb; ++b, ++i) {
     seg[i].bits = reinterpret_cast<const u32x4 *>(d.bits_global) + b * tw_g / 4;
     seg[i].c = d.c_global + b * d.k;
-    seg[i].r = d.r_global + b * d.n;
+    seg[i].r = d.r_global + b * rs_g;
     seg[i].len = (int32_t)d.k;
     seg[i].nchunks = nc_g;
   }
   for (int b = 0; b < d.ks; ++b, ++i) {
     seg[i].bits = reinterpret_cast<const u32x4 *>(d.bits_sal) + b * tw_s / 4;
     seg[i].c = d.c_sal + b * d.s;
-    seg[i].r = d.r_sal + b * d.n;
+    seg[i].r = d.r_sal + b * rs_s;
     seg[i].len = (int32_t)d.s;
     seg[i].nchunks = nc_s;
   }
@@ -269,6 +273,32 @@ const char *fluxbin_last_error(void) { return g_err; }
 int64_t fluxbin_tiled_words(int64_t rows, int64_t cols) {
   if (rows <= 0 || cols <= 0) return 0;
   return cdiv(rows, kTileRows) * cdiv(cols, kChunkCols) * kTileRows * 4;
+}
+
+int64_t fluxbin_tiled_scale_elems(int64_t rows, int64_t groups, int64_t groups_per_chunk) {
+  if (rows <= 0 || groups <= 0 || groups_per_chunk < 1 || groups_per_chunk > kChunkCols) return 0;
+  return cdiv(rows, kTileRows) * cdiv(groups, groups_per_chunk) * kTileRows * groups_per_chunk;
+}
+
+fluxbin_status fluxbin_relayout_scales(const uint16_t *src, int64_t rows, int64_t groups, int64_t groups_per_chunk,
+                                       int32_t src_layout, int32_t dst_layout, uint16_t *dst, void *stream) {
+  if (rows < 0 || groups < 0) return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "negative size");
+  if (groups_per_chunk < 1 || groups_per_chunk > kChunkCols)
+    return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "groups_per_chunk = %lld (1..%d)", (long long)groups_per_chunk,
+                kChunkCols);
+  for (int32_t l : {src_layout, dst_layout})
+    if (l != FLUXBIN_LAYOUT_ROWMAJOR && l != FLUXBIN_LAYOUT_TILED)
+      return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "layout = %d", l);
+  if (rows == 0 || groups == 0) return ok();
+  if (!src || !dst) return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "NULL pointer");
+  if (src == dst) return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "src and dst must not overlap");
+  const int64_t elems = dst_layout == FLUXBIN_LAYOUT_ROWMAJOR ? rows * groups
+                                                             : fluxbin_tiled_scale_elems(rows, groups, groups_per_chunk);
+  hipLaunchKernelGGL(relayout_scales_kernel, dim3(grid_for(elems)), dim3(256), 0, (hipStream_t)stream, src, rows,
+                     groups, groups_per_chunk, src_layout, dst_layout, dst, elems);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "relayout_scales launch");
+  return ok();
 }
 
 fluxbin_status fluxbin_pack(const int8_t *signs, int64_t rows, int64_t cols, int64_t ld, int32_t layout,
@@ -351,6 +381,8 @@ fluxbin_status fluxbin_create(const fluxbin_layer_desc *d, fluxbin_handle *out) 
     if (!d->bits_sal || !d->r_sal || !d->c_sal || !d->sal_idx)
       return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "salient pointers must be non-NULL when ks > 0");
     if (!aligned(d->bits_sal, 16)) return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "bits_sal not 16-byte aligned");
+    if (d->row_group && !aligned(d->r_sal, 16))
+      return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "r_sal not 16-byte aligned (block-wise scales)");
   }
   Plan p;
   st = make_plan(d, &p);
@@ -373,6 +405,10 @@ fluxbin_status fluxbin_create(const fluxbin_layer_desc *d, fluxbin_handle *out) 
                     (long long)d->k);
       if (i > 0 && idx[i] <= idx[i - 1])
         return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "sal_idx not strictly ascending at %lld", (long long)i);
+      if (d->row_group && idx[i] / d->row_group != i / d->sal_group)
+        return fail(FLUXBIN_ERR_INVALID_ARGUMENT,
+                    "sal_idx[%lld] = %d is not in column group %lld (block-wise: %d salient columns per group)",
+                    (long long)i, idx[i], (long long)(i / d->sal_group), d->sal_group);
     }
   }
   if (p.acc_bytes) {
@@ -381,7 +417,7 @@ fluxbin_status fluxbin_create(const fluxbin_layer_desc *d, fluxbin_handle *out) 
     e = hipDeviceSynchronize();
     if (e != hipSuccess) return hip_fail(e, "synchronising after create");
   }
-  gemv_fn fn = pick_gemv(d->g, p.nb, p.waves, p.pf);
+  gemv_fn fn = pick_gemv(d->g, d->row_group ? 1 : 0, p.nb, p.waves, p.pf);
   if (!fn) return fail(FLUXBIN_ERR_UNSUPPORTED, "no kernel for g = %d, batch width %d, %d waves", d->g, p.nb, p.waves);
   const size_t lds = (size_t)lds_bytes(d->g, p.nb, p.cpb);
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -480,6 +516,9 @@ fluxbin_status fluxbin_gemv(fluxbin_handle h, const uint16_t *x, uint16_t *y, in
   a.idx_or_dummy = h->idx_or_dummy;
   a.cpb = p.cpb;
   a.total_chunks = p.total_chunks;
+  a.gsplits = p.gsplits;
+  a.gchunks = p.gchunks;
+  a.sal16 = d.row_group && d.ks > 0 && d.sal_group == 8 ? 1 : 0;
   a.row_tiles = p.row_tiles;
   a.row_blocks = p.row_blocks;
   a.splits = p.splits;

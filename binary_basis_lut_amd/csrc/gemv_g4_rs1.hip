@@ -1,0 +1,8 @@
+// gemv_g4_rs1.hip -- LUT GEMV kernel instances for g = 4, block-wise row scales.
+#include "gemv_kernel.hpp"
+
+namespace fluxbin {
+
+gemv_fn gemv_pick_g4_rs1(int nb, int waves, int pf) { return gemv_pick<4, 1>(nb, waves, pf); }
+
+}  // namespace fluxbin

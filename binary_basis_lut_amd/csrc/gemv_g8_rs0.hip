@@ -1,0 +1,8 @@
+// gemv_g8_rs0.hip -- LUT GEMV kernel instances for g = 8, per-row row scales.
+#include "gemv_kernel.hpp"
+
+namespace fluxbin {
+
+gemv_fn gemv_pick_g8_rs0(int nb, int waves, int pf) { return gemv_pick<8, 0>(nb, waves, pf); }
+
+}  // namespace fluxbin

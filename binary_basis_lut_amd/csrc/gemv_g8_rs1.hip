@@ -1,0 +1,8 @@
+// gemv_g8_rs1.hip -- LUT GEMV kernel instances for g = 8, block-wise row scales.
+#include "gemv_kernel.hpp"
+
+namespace fluxbin {
+
+gemv_fn gemv_pick_g8_rs1(int nb, int waves, int pf) { return gemv_pick<8, 1>(nb, waves, pf); }
+
+}  // namespace fluxbin

@@ -20,7 +20,7 @@ if not LIB_PATH.exists():
 
 _lib = ctypes.CDLL(str(LIB_PATH))
 
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
 LAYOUT_ROWMAJOR, LAYOUT_TILED = 0, 1
@@ -39,6 +39,7 @@ class LayerDesc(ctypes.Structure):
         ("bits_sal", P), ("r_sal", P), ("c_sal", P), ("sal_idx", P),
         ("workspace", P), ("workspace_bytes", ctypes.c_size_t),
         ("chunks_per_block", I32), ("waves_per_block", I32),
+        ("row_group", I32), ("sal_group", I32),
     ]
 
 
@@ -72,6 +73,8 @@ _decl("fluxbin_last_error", ctypes.c_char_p, [])
 _decl("fluxbin_tiled_words", I64, [I64, I64])
 _decl("fluxbin_pack", ctypes.c_int, [P, I64, I64, I64, I32, P, P, P])
 _decl("fluxbin_relayout", ctypes.c_int, [P, I64, I64, I32, I32, P, P])
+_decl("fluxbin_tiled_scale_elems", I64, [I64, I64, I64])
+_decl("fluxbin_relayout_scales", ctypes.c_int, [P, I64, I64, I64, I32, I32, P, P])
 _decl("fluxbin_vcm_gather", ctypes.c_int, [P, I64, P, I64, I64, I32, P, P])
 _decl("fluxbin_workspace_size", ctypes.c_int, [ctypes.POINTER(LayerDesc), ctypes.POINTER(ctypes.c_size_t)])
 _decl("fluxbin_create", ctypes.c_int, [ctypes.POINTER(LayerDesc), ctypes.POINTER(P)])
@@ -84,8 +87,9 @@ _decl("fluxbin_dense_gemv_f16", ctypes.c_int, [P, I64, I64, P, P, I64, P])
 
 SYMBOLS = [
     "fluxbin_abi_version", "fluxbin_status_string", "fluxbin_last_error", "fluxbin_tiled_words", "fluxbin_pack",
-    "fluxbin_relayout", "fluxbin_vcm_gather", "fluxbin_workspace_size", "fluxbin_create", "fluxbin_destroy",
-    "fluxbin_get_plan", "fluxbin_lut_size", "fluxbin_build_lut", "fluxbin_gemv", "fluxbin_dense_gemv_f16",
+    "fluxbin_relayout", "fluxbin_tiled_scale_elems", "fluxbin_relayout_scales", "fluxbin_vcm_gather",
+    "fluxbin_workspace_size", "fluxbin_create", "fluxbin_destroy", "fluxbin_get_plan", "fluxbin_lut_size",
+    "fluxbin_build_lut", "fluxbin_gemv", "fluxbin_dense_gemv_f16",
 ]
 
 
@@ -137,6 +141,15 @@ def fluxbin_pack(signs, rows, cols, ld, layout, packed, invalid_count=None, stre
 def fluxbin_relayout(src, rows, cols, src_layout, dst_layout, dst, stream=None):
     _check(_lib.fluxbin_relayout(_ptr(src), rows, cols, src_layout, dst_layout, _ptr(dst), _stream(stream)),
            "fluxbin_relayout")
+
+
+def fluxbin_tiled_scale_elems(rows: int, groups: int, groups_per_chunk: int) -> int:
+    return int(_lib.fluxbin_tiled_scale_elems(rows, groups, groups_per_chunk))
+
+
+def fluxbin_relayout_scales(src, rows, groups, groups_per_chunk, src_layout, dst_layout, dst, stream=None):
+    _check(_lib.fluxbin_relayout_scales(_ptr(src), rows, groups, groups_per_chunk, src_layout, dst_layout, _ptr(dst),
+                                        _stream(stream)), "fluxbin_relayout_scales")
 
 
 def fluxbin_vcm_gather(idx, s, src, rows, cols, dtype, dst, stream=None):
@@ -196,8 +209,10 @@ class DeviceLayer:
     """Upload one synthetic layer (binary_basis_lut_amd.inputs.Layer) and create its handle.
 
     Canonical sign words are copied to the device and converted to the tiled
-    layout with fluxbin_relayout; scales, index and workspace are torch CUDA
-    tensors owned by this object, which keeps them alive for the handle.
+    layout with fluxbin_relayout; block-wise row scales ([basis][n][groups])
+    are converted to the tiled scale layout with fluxbin_relayout_scales.
+    Scales, index and workspace are torch CUDA tensors owned by this object,
+    which keeps them alive for the handle.
     """
 
     def __init__(self, layer, max_batch: int = 1, chunks_per_block: int = 0, waves_per_block: int = 0,
@@ -219,7 +234,22 @@ class DeviceLayer:
         for b in range(layer.kb):
             fluxbin_relayout(canon[b], n, k, LAYOUT_ROWMAJOR, LAYOUT_TILED, self.bits_g[b * tw_g:(b + 1) * tw_g])
         del canon
-        self.r_g = up(layer.r_g, np.int16)
+        rgroup = int(getattr(layer, "row_group", 0) or 0)
+        self.row_group = rgroup
+        self.sal_group = int(getattr(layer, "sal_group", 0) or 0) if layer.ks else 0
+
+        def tiled_scales(r, bases, m):
+            """[bases][n][groups] canonical -> concatenated tiled blocks (m groups per chunk)."""
+            groups = r.shape[2]
+            te = fluxbin_tiled_scale_elems(n, groups, m)
+            out = torch.zeros(max(bases * te, 8), dtype=torch.int16, device=dev)
+            canon_r = up(r, np.int16)
+            for b in range(bases):
+                fluxbin_relayout_scales(canon_r[b], n, groups, m, LAYOUT_ROWMAJOR, LAYOUT_TILED,
+                                        out[b * te:(b + 1) * te])
+            return out
+
+        self.r_g = tiled_scales(layer.r_g, layer.kb, 1) if rgroup else up(layer.r_g, np.int16)
         self.c_g = up(layer.c_g, np.int16)
         if layer.ks:
             tw_s = fluxbin_tiled_words(n, s)
@@ -229,7 +259,8 @@ class DeviceLayer:
                 fluxbin_relayout(canon_s[b], n, s, LAYOUT_ROWMAJOR, LAYOUT_TILED,
                                  self.bits_s[b * tw_s:(b + 1) * tw_s])
             del canon_s
-            self.r_s = up(layer.r_s, np.int16)
+            self.r_s = (tiled_scales(layer.r_s, layer.ks, 128 // self.sal_group) if rgroup
+                        else up(layer.r_s, np.int16))
             self.c_s = up(layer.c_s, np.int16)
             self.sal_idx = up(layer.sal_idx, np.int32)
         else:
@@ -255,6 +286,8 @@ class DeviceLayer:
                                                    _ptr(self.sal_idx))
         d.chunks_per_block = chunks_per_block
         d.waves_per_block = waves_per_block
+        d.row_group = self.row_group
+        d.sal_group = self.sal_group
         return d
 
     def gemv(self, x, y, batch=None, stream=None):

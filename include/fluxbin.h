@@ -8,7 +8,12 @@
  *
  * where (.) is the element-wise product, every B is a +-1 matrix stored as
  * packed sign bits, r are per-row and c per-column fp16 scales, and S is the
- * ordered list of salient columns.  This is the inference form of the
+ * ordered list of salient columns.  In the block-wise format (desc.row_group
+ * = 128) each r holds one scale per row per 128-column group of x, and a
+ * salient column takes the scale of the group its original column lies in
+ * (the storage of the FluxBin summary, appendix C.2: dense global bits with
+ * column scales and block-wise row scales, plus a few salient columns per
+ * group).  This is the inference form of the
  * decoupled row-column binary decomposition with salient-aware hybrid bases
  * (FluxBin: Flexible LUT-based Ultra-low-bit LLM Inference by
  * Algorithm-Kernel Synergy, paperlayer.ai summary, section 3 "Methodology",
@@ -50,7 +55,7 @@
 extern "C" {
 #endif
 
-#define FLUXBIN_ABI_VERSION 1
+#define FLUXBIN_ABI_VERSION 2
 
 typedef enum {
   FLUXBIN_OK = 0,
@@ -101,10 +106,10 @@ typedef struct {
   int64_t s;             /* salient columns |S|: 0 when ks == 0, else 1..k */
   int64_t max_batch;     /* largest batch a call may pass: 1..16 (g = 8: 1..4) */
   const uint32_t *bits_global; /* TILED words, kb blocks of fluxbin_tiled_words(n, k), 16-B aligned */
-  const uint16_t *r_global;    /* fp16 [kb][n] row scales */
+  const uint16_t *r_global;    /* fp16 row scales: [kb][n], or block-wise (see row_group) */
   const uint16_t *c_global;    /* fp16 [kb][k] column scales */
   const uint32_t *bits_sal;    /* TILED words, ks blocks of fluxbin_tiled_words(n, s), 16-B aligned */
-  const uint16_t *r_sal;       /* fp16 [ks][n] */
+  const uint16_t *r_sal;       /* fp16 [ks][n], or block-wise (see row_group) */
   const uint16_t *c_sal;       /* fp16 [ks][s], compact order (entry c belongs to column sal_idx[c]) */
   const int32_t *sal_idx;      /* [s] salient columns, strictly ascending, in [0, k) */
   void *workspace;             /* >= fluxbin_workspace_size() bytes, 256-B aligned; may be NULL if that size is 0 */
@@ -114,6 +119,17 @@ typedef struct {
                                   of tables per workgroup and 8 table-build inputs per thread
                                   (FLUXBIN_ERR_UNSUPPORTED beyond it) */
   int32_t waves_per_block;     /* tuning: 0 = automatic, else 4 or 8 (64 output rows per wave) */
+  int32_t row_group;           /* row-scale format.  0: one scale per row per basis, r_global fp16 [kb][n],
+                                  r_sal fp16 [ks][n].  128: block-wise, one scale per row per basis per group
+                                  of 128 columns of x; with G = ceil(k/128), r_global holds kb blocks of
+                                  fluxbin_tiled_scale_elems(n, G, 1) and r_sal (16-B aligned) ks blocks of
+                                  fluxbin_tiled_scale_elems(n, G, 128/sal_group), each the TILED scale layout
+                                  of a [n][G] matrix (see fluxbin_relayout_scales).  Other values:
+                                  FLUXBIN_ERR_UNSUPPORTED */
+  int32_t sal_group;           /* block-wise with ks > 0: salient columns per 128-column group, 8 or 16 (a
+                                  multiple of g).  S must take exactly sal_group columns from every group:
+                                  s == sal_group * G and sal_idx[c] / 128 == c / sal_group (checked by
+                                  fluxbin_create).  Must be 0 otherwise. */
 } fluxbin_layer_desc;
 
 /* How a handle splits the work (read-only introspection). */
@@ -150,6 +166,24 @@ fluxbin_status fluxbin_pack(const int8_t *signs, int64_t rows, int64_t cols, int
  * TILED, or a copy when they are equal).  src and dst must not overlap. */
 fluxbin_status fluxbin_relayout(const uint32_t *src, int64_t rows, int64_t cols, int32_t src_layout,
                                 int32_t dst_layout, uint32_t *dst, void *stream);
+
+/* Elements of the TILED scale layout for a rows x groups fp16 matrix of
+ * block-wise row scales, groups_per_chunk (1..128) groups to a 128-column
+ * chunk (host-side arithmetic; 0 for invalid sizes). */
+int64_t fluxbin_tiled_scale_elems(int64_t rows, int64_t groups, int64_t groups_per_chunk);
+
+/* Convert block-wise row scales between the row-major [rows][groups] fp16
+ * matrix (FLUXBIN_LAYOUT_ROWMAJOR) and the TILED scale layout, or copy.
+ * TILED: rows padded to a multiple of 64, groups to a multiple of m =
+ * groups_per_chunk; element (row r, group q) at
+ *     ((floor(r/64) * NC + floor(q/m)) * 64 + (r mod 64)) * m + (q mod m),
+ * NC = ceil(groups/m), padding 0.  The m scales one row needs for one
+ * 128-column chunk are contiguous, and those of a 64-row tile form one
+ * block, which fluxbin_gemv streams beside the tile's sign words.  Global
+ * bases use m = 1, salient bases m = 128 / sal_group.  src and dst must not
+ * overlap; every destination element, padding included, is written. */
+fluxbin_status fluxbin_relayout_scales(const uint16_t *src, int64_t rows, int64_t groups, int64_t groups_per_chunk,
+                                       int32_t src_layout, int32_t dst_layout, uint16_t *dst, void *stream);
 
 /* Virtual Columnar Mapping gather (FluxBin summary, section 3 bullet "Virtual
  * Columnar Mapping"): dst column c = src column idx[c], for c < s, of a
@@ -191,7 +225,10 @@ fluxbin_status fluxbin_build_lut(fluxbin_handle h, const uint16_t *x, int64_t ba
 
 /* y = the layer applied to x.  x: fp16 [batch][k], y: fp16 [batch][n]
  * (round to nearest even), 0 <= batch <= max_batch (0 launches nothing).
- * Tables and accumulation are fp32.  When the handle's plan splits the
+ * Tables and accumulation are fp32.  Per-row scales multiply a segment's
+ * accumulated sum; block-wise scales multiply the sum of each global chunk
+ * (one group) and of each 8 salient columns (one group, or half of one when
+ * sal_group = 16), before those sums are added.  When the handle's plan splits the
  * columns over several workgroups (fluxbin_plan.splits > 1), the partial
  * sums of a row are combined exactly as 2^-30 fixed-point integers: each
  * partial is rounded to 2^-31 (absolute) and partials beyond +-2^17 saturate.

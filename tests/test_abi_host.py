@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported(fb):
 
 
 def test_abi_version_and_strings(fb):
-    assert fb.fluxbin_abi_version() == fb.ABI_VERSION == 1
+    assert fb.fluxbin_abi_version() == fb.ABI_VERSION == 2
     assert fb.fluxbin_status_string(fb.OK) == "ok"
     assert "invalid" in fb.fluxbin_status_string(fb.ERR_INVALID_ARGUMENT)
     assert fb.fluxbin_status_string(99) == "unknown status"
@@ -86,9 +86,10 @@ def test_too_many_splits_is_unsupported(fb):
 
 
 @pytest.mark.parametrize("field,value,status", [
-    ("abi_version", 2, 1), ("g", 3, 2), ("g", 16, 2), ("kb", 0, 2), ("kb", 5, 2), ("ks", 3, 2), ("ks", -1, 2),
+    ("abi_version", 1, 1), ("g", 3, 2), ("g", 16, 2), ("kb", 0, 2), ("kb", 5, 2), ("ks", 3, 2), ("ks", -1, 2),
     ("n", 0, 1), ("k", 0, 1), ("s", 0, 1), ("s", 5000, 1), ("max_batch", 0, 2), ("max_batch", 17, 2),
     ("chunks_per_block", 33, 1), ("chunks_per_block", -1, 1), ("waves_per_block", 2, 1), ("waves_per_block", 16, 1),
+    ("row_group", 64, 2), ("row_group", -1, 2), ("sal_group", 8, 1),
 ])
 def test_workspace_size_rejects(fb, field, value, status):
     st, _ = ws_status(fb, good_desc(fb, **{field: value}))
@@ -145,3 +146,60 @@ def test_empty_work_is_a_no_op(fb):
     assert s("fluxbin_pack", None, 0, 5, 5, 0, None, None, None) == fb.OK
     assert s("fluxbin_relayout", None, 5, 0, 0, 1, None, None) == fb.OK
     assert s("fluxbin_vcm_gather", None, 0, None, 5, 5, 1, None, None) == fb.OK
+
+
+@pytest.mark.parametrize("rows,groups,m", [(1, 1, 1), (4096, 32, 1), (4096, 32, 16), (100, 86, 8), (65, 3, 16)])
+def test_tiled_scale_elems(fb, rows, groups, m):
+    assert fb.fluxbin_tiled_scale_elems(rows, groups, m) == -(-rows // 64) * -(-groups // m) * 64 * m
+    assert fb.fluxbin_tiled_scale_elems(rows, groups, 0) == 0
+    assert fb.fluxbin_tiled_scale_elems(rows, groups, 129) == 0
+    assert fb.fluxbin_tiled_scale_elems(0, groups, m) == 0
+
+
+def grouped_desc(fb, **kw):
+    """q_proj shape in the pages' 2b-s8-g128 storage: 2 + 2 bases, 8 salient columns per 128."""
+    base = dict(kb=2, ks=2, s=8 * 32, row_group=128, sal_group=8)
+    base.update(kw)
+    return good_desc(fb, **base)
+
+
+def test_block_wise_plan_keeps_global_and_salient_ranges_apart(fb):
+    # 64 global + 4 salient chunks; with 8 chunks per workgroup: 8 global ranges + 1 salient range
+    st, ws = ws_status(fb, grouped_desc(fb, chunks_per_block=8))
+    assert st == fb.OK and ws == 4096 * 8
+    # one global chunk (k = 128) and one salient chunk: two ranges, hence a split reduction
+    st, ws = ws_status(fb, grouped_desc(fb, k=128, s=8, chunks_per_block=2, kb=1, ks=1))
+    assert st == fb.OK and ws == 4096 * 8
+    # the same layer without salient bases fits one range and needs no workspace
+    st, ws = ws_status(fb, grouped_desc(fb, k=128, s=0, ks=0, sal_group=0, chunks_per_block=2, kb=1))
+    assert st == fb.OK and ws == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(sal_group=4), 2), (dict(sal_group=32), 2), (dict(sal_group=0), 2), (dict(s=255), 1), (dict(s=512), 1),
+    (dict(g=8, sal_group=8), 0), (dict(g=8, sal_group=16, s=16 * 32), 0), (dict(ks=0, s=0, sal_group=0), 0),
+    (dict(ks=0, s=0, sal_group=8), 1), (dict(k=300, s=8 * 3), 0), (dict(k=300, s=8 * 2), 1),
+])
+def test_block_wise_desc_validation(fb, kw, status):
+    st, _ = ws_status(fb, grouped_desc(fb, **kw))
+    assert st == status, fb.fluxbin_last_error()
+
+
+def test_relayout_scales_rejects_on_the_host(fb):
+    s = fb.raw_status
+    assert s("fluxbin_relayout_scales", 0x1000, 5, 5, 0, 0, 1, 0x2000, None) == fb.ERR_INVALID_ARGUMENT  # m = 0
+    assert s("fluxbin_relayout_scales", 0x1000, 5, 5, 129, 0, 1, 0x2000, None) == fb.ERR_INVALID_ARGUMENT
+    assert s("fluxbin_relayout_scales", 0x1000, 5, 5, 1, 0, 2, 0x2000, None) == fb.ERR_INVALID_ARGUMENT
+    assert s("fluxbin_relayout_scales", 0x1000, 5, 5, 1, 0, 1, 0x1000, None) == fb.ERR_INVALID_ARGUMENT
+    assert s("fluxbin_relayout_scales", None, 5, 5, 1, 0, 1, 0x2000, None) == fb.ERR_INVALID_ARGUMENT
+    assert s("fluxbin_relayout_scales", None, 0, 5, 1, 0, 1, None, None) == fb.OK
+
+
+def test_block_wise_create_checks_salient_scale_alignment(fb):
+    h = ctypes.c_void_p()
+    d = grouped_desc(fb)
+    d.bits_global = d.r_global = d.c_global = 0x1000
+    d.bits_sal = d.c_sal = d.sal_idx = 0x2000
+    d.r_sal = 0x2002
+    assert fb.raw_status("fluxbin_create", ctypes.byref(d), ctypes.byref(h)) == fb.ERR_INVALID_ARGUMENT
+    assert "r_sal" in fb.fluxbin_last_error()

@@ -48,9 +48,22 @@ def gemv(fb, dl, x_np):
 
 
 def magnitude(layer, x_np, rows):
-    """sum over segments of |r| * sum_cols |c * x|: the scale of every fp32 rounding in one row."""
+    """sum over segments of |r| * sum_cols |c * x|: the scale of every fp32 rounding in one row
+    (block-wise row scales: the sum over groups of |r| * the group's sum of |c * x|)."""
     xd = x_np.view(np.float16).astype(np.float64)
     out = np.zeros((xd.shape[0], len(rows)))
+    if getattr(layer, "row_group", 0):
+        G = layer.row_group
+        for b in range(layer.kb):
+            cx = np.abs(xd) * np.abs(layer.c_g[b].view(np.float16).astype(np.float64))[None, :]
+            grp = np.add.reduceat(cx, np.arange(0, layer.k, G), axis=1)                     # [batch][groups]
+            out += grp @ np.abs(layer.r_g[b][rows].view(np.float16).astype(np.float64)).T
+        for b in range(layer.ks):
+            cx = np.abs(xd[:, layer.sal_idx]) * np.abs(layer.c_s[b].view(np.float16).astype(np.float64))[None, :]
+            grp = np.zeros((xd.shape[0], -(-layer.k // G)))
+            np.add.at(grp.T, layer.sal_idx // G, cx.T)
+            out += grp @ np.abs(layer.r_s[b][rows].view(np.float16).astype(np.float64)).T
+        return out
     for b in range(layer.kb):
         a = np.abs(xd) @ np.abs(layer.c_g[b].view(np.float16).astype(np.float64))
         out += np.abs(layer.r_g[b][rows].view(np.float16).astype(np.float64))[None, :] * a[:, None]
