@@ -49,11 +49,11 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(bytes_per_launch_alg: float):
-    """HBM bytes per launch from the committed counter summary, if it was taken on this kernel source."""
-    f = ROOT / "profiles" / "lut_gemv_q_proj_4096_counters.json"
+def measured_traffic(name: str):
+    """HBM bytes per launch from the committed counter summary `name`, if it was taken on this kernel source."""
+    f = ROOT / "profiles" / name
     if not f.exists():
-        return None, None
+        return None, "no counter summary for this workload"
     try:
         d = json.loads(f.read_text())
     except Exception:
@@ -224,7 +224,8 @@ def main() -> int:
     dense_us = d0.elapsed_time(d1) * 1e3 / (8 * Rd)
     del wd
 
-    traffic, traffic_note = (None, "no counters for this format") if blockwise else measured_traffic(bytes_per_gemv)
+    traffic, traffic_note = measured_traffic(f"lut_gemv_q_proj_4096_blockwise_s{args.sal_group}_counters.json"
+                                             if blockwise else "lut_gemv_q_proj_4096_counters.json")
     cpu = None if args.no_cpu else cpu_baseline(lay0, x0, args.cpu_seconds, bytes_per_gemv)
 
     line = {

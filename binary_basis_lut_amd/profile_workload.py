@@ -6,7 +6,10 @@ profiles/ (each summary names the exact command).  Two modes:
   python3 -m binary_basis_lut_amd.profile_workload gemv --workload 2 --shape 0 --sets 256 --reps 2
       builds `sets` distinct weight sets of the shape (resident in HBM, more
       than the 256 MB Infinity Cache for the q_proj shape), captures one call
-      per set in a HIP graph and replays it `reps` times;
+      per set in a HIP graph and replays it `reps` times, and prints the time
+      per call (HIP events around the replays);  --format blockwise draws the
+      shape in the block-wise row-scale storage instead (--kb global and --ks
+      salient bases, --sal-group salient columns per 128-column group);
 
   python3 -m binary_basis_lut_amd.profile_workload copy --bytes 1073741824 --reps 4
       a plain device-to-device copy of known size (torch's copy kernel): the
@@ -27,13 +30,23 @@ def run_gemv(args) -> None:
     import numpy as np
     import torch
 
+    from binary_basis_lut_amd import accounting as A
     from binary_basis_lut_amd import fluxbin as F
     from binary_basis_lut_amd import inputs as I
 
+    wl = I.WORKLOADS[args.workload]
+    sh = wl.shapes[args.shape]
+    blockwise = args.format == "blockwise"
     dls, xs, ys = [], [], []
     for i in range(args.sets):
-        lay = I.workload_layer(args.workload, args.shape, i)
-        x = I.workload_x(args.workload, lay, args.batch, args.shape, i)
+        if blockwise:
+            seed = (args.workload, i, 100 + args.sal_group + 1000 * args.shape)
+            lay = I.make_grouped_layer(sh.n, sh.k, args.kb, args.ks, wl.g, 128, args.sal_group,
+                                       outlier_frac=wl.outlier_frac, seed=seed)
+            x = I.make_x(lay, args.batch, seed=seed)
+        else:
+            lay = I.workload_layer(args.workload, args.shape, i)
+            x = I.workload_x(args.workload, lay, args.batch, args.shape, i)
         dls.append(F.DeviceLayer(lay, max_batch=args.batch, chunks_per_block=args.chunks_per_block))
         xs.append(torch.from_numpy(x.view(np.int16)).cuda())
         ys.append(torch.empty((args.batch, lay.n), dtype=torch.int16, device="cuda"))
@@ -49,11 +62,20 @@ def run_gemv(args) -> None:
             for i in range(args.sets):
                 dls[i].gemv(xs[i], ys[i], stream=stream)
     torch.cuda.synchronize()
-    for _ in range(args.reps):
-        graph.replay()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for _ in range(args.reps):
+            graph.replay()
+        e1.record(stream)
     torch.cuda.synchronize()
-    print(f"gemv workload {args.workload} shape {args.shape}: {args.sets} sets x {args.reps} replays, "
-          f"plan {dls[0].plan}", flush=True)
+    us = e0.elapsed_time(e1) * 1e3 / (args.reps * args.sets)
+    lay = dls[0].layer
+    wb = (A.grouped_weight_bytes(lay.n, lay.k, lay.kb, lay.ks, 128, args.sal_group) if blockwise
+          else A.weight_bytes(lay.n, lay.k, lay.s, lay.kb, lay.ks))
+    print(f"gemv workload {args.workload} shape {args.shape} ({sh.name} {sh.k}->{sh.n}, {args.format}): "
+          f"{args.sets} sets x {args.reps} replays, {us:.3f} us per call, {wb / us / 1e3:.1f} GB/s of "
+          f"{wb} weight-side bytes, plan {dls[0].plan}", flush=True)
     for d in dls:
         d.close()
 
@@ -81,6 +103,10 @@ def main() -> int:
     g.add_argument("--reps", type=int, default=2)
     g.add_argument("--batch", type=int, default=1)
     g.add_argument("--chunks-per-block", type=int, default=0)
+    g.add_argument("--format", choices=["per-row", "blockwise"], default="per-row")
+    g.add_argument("--kb", type=int, default=2, help="blockwise: global bases")
+    g.add_argument("--ks", type=int, default=2, help="blockwise: salient bases")
+    g.add_argument("--sal-group", type=int, default=8, choices=[8, 16])
     c = sub.add_parser("copy")
     c.add_argument("--bytes", type=int, default=1 << 30)
     c.add_argument("--reps", type=int, default=4)
