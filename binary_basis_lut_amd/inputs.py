@@ -257,6 +257,38 @@ def workload_x(cid: int, layer_obj: Layer, batch: int, shape_idx: int = 0, layer
 
 
 # --------------------------------------------------------------------------
+# Inputs of the offline decomposition (dense synthetic weights)
+# --------------------------------------------------------------------------
+# A synthetic stand-in for one trained linear layer: fp16 N(0, 0.02) entries
+# scaled by a log-normal factor per row and per column (sigma 0.3), so that
+# rows and columns differ in magnitude, the anisotropy the row-column
+# decomposition is meant to capture.  Column weights of the weighted least
+# squares stand in for the diagonal of the calibration Hessian 2 X X^T: the
+# mean square of NCAL calibration draws of each input channel (same
+# activation distribution and outlier channels as make_x).
+
+T_W, T_W_ROW, T_W_COL = 20, 21, 22
+
+
+def decomp_matrix(n: int, k: int, seed: tuple = (0, 0, 0)) -> np.ndarray:
+    """fp16 [n][k] synthetic weights as raw uint16 bits."""
+    v = stream(*seed, T_W).normal(0.0, 0.02, size=(n, k))
+    v *= np.exp(stream(*seed, T_W_ROW).normal(0.0, 0.3, size=(n, 1)))
+    v *= np.exp(stream(*seed, T_W_COL).normal(0.0, 0.3, size=(1, k)))
+    return v.astype(np.float16).view(np.uint16)
+
+
+def calibration_weights(k: int, outlier_frac: float = 0.0, seed: tuple = (0, 0, 0)) -> np.ndarray:
+    """fp64 [k] per-column weights: mean over NCAL draws of fp16(x_j)^2."""
+    outl = outlier_channels(stream(*seed, T_OUTLIER), k, outlier_frac)
+    cal = stream(*seed, T_CAL).normal(0.0, 1.0, size=(NCAL, k))
+    if outl.size:
+        cal[:, outl] *= 20.0
+    cal = cal.astype(np.float16).astype(np.float64)
+    return (cal * cal).mean(axis=0)
+
+
+# --------------------------------------------------------------------------
 # Small structured inputs used by the exact-arithmetic tests
 # --------------------------------------------------------------------------
 

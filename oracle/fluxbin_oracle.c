@@ -42,7 +42,11 @@
  * problems, and agreement with the separately written LUT route.  The
  * block-wise row scales are pinned by reduction to the per-row product (all
  * group scales of a row equal; a single non-zero group on activations
- * zeroed outside it) and by exact integer brute force.
+ * zeroed outside it) and by exact integer brute force.  The offline
+ * decomposition's steps are pinned by the properties the pages assign them:
+ * each scale step lands on the vertex of its least-squares quadratic, the
+ * sign step is the exhaustive per-element optimum, the error never rises
+ * over the steps, and a matrix that is one scaled binary basis is recovered.
  */
 #include <math.h>
 #include <stdint.h>
@@ -481,6 +485,203 @@ ORC_EXPORT void orc_dense_f16_gemv(const uint16_t *w, int64_t n, int64_t k, cons
     }
   }
   free(xd);
+}
+
+/* ---------------------------------------------------------------------- */
+/* Offline decomposition W ~ sum_b diag(r_b) B_b diag(c_b)                  */
+/* ---------------------------------------------------------------------- */
+/* FluxBin summary, section 3 bullets "Quantization" (decoupled row-column
+ * binary bases summed over decomposition orders) and "Parameter
+ * Optimization" (alternating minimisation with weighted least squares; all
+ * 2^Kb sign combinations evaluated jointly), appendix A.1 (with the binary
+ * basis and the column scales fixed, each row scale is an independent scalar
+ * least-squares problem with a closed form) and A.2 (with the scales fixed,
+ * the error separates into independent per-element problems; exhaustive
+ * search over the Kb signs of one element is globally optimal).
+ *
+ * Objective: E = sum_ij d_j (W_ij - W_hat_ij)^2, d_j > 0 per-column weights
+ * (NULL: all 1).  Layouts: W fp16 [n][k]; bits canonical words
+ * [kb][n][ceil(k/32)]; r fp64 [kb][n]; c fp64 [kb][k].  Readings where the
+ * pages are silent (each is listed in the design notes):
+ *   - the residual of basis b is R = W - sum_{l != b} diag(r_l) B_l diag(c_l);
+ *   - row step:    r_b,i = sum_j d_j R_ij B_b,ij c_b,j / sum_j d_j c_b,j^2;
+ *   - column step: c_b,j = sum_i R_ij B_b,ij r_b,i / sum_i r_b,i^2 (the
+ *     weight d_j cancels); a zero denominator gives a zero scale;
+ *   - sign step: for every element the combination m in [0, 2^kb) (bit b of
+ *     m set = sign +1 on basis b) minimising |W_ij - s_m|, with
+ *     s_m = sum_b (+-) r_b,i c_b,j accumulated in basis order from 0, each
+ *     product rounded to fp64 once; ties go to the smallest m;
+ *   - initialisation: bases in order; basis b takes the signs of the
+ *     residual of the bases before it (R >= 0 gives +1), c_b = 1, then one row
+ *     step and one column step;
+ *   - one iteration: row then column step of every basis in order, then the
+ *     sign step;
+ *   - output: scales rounded to fp16 (nearest even), then one more sign step
+ *     against the rounded scales. */
+
+/* sum over bases l != skip of r_l,i B_l,ij c_l,j (skip = -1: every basis). */
+static double approx_at(int64_t n, int64_t k, int32_t kb, const uint32_t *bits, const double *r, const double *c,
+                        int64_t i, int64_t j, int32_t skip) {
+  int64_t wpr = words_per_row(k);
+  double a = 0.0;
+  for (int32_t b = 0; b < kb; ++b) {
+    if (b == skip) continue;
+    a += r[(int64_t)b * n + i] * sign_at(bits + ((int64_t)b * n + i) * wpr, j) * c[(int64_t)b * k + j];
+  }
+  return a;
+}
+
+/* Row step of basis `basis`: r_out[i] for every row (other bases as given). */
+ORC_EXPORT void orc_decomp_row_scales(const uint16_t *w, int64_t n, int64_t k, int32_t kb, int32_t basis,
+                                      const uint32_t *bits, const double *r, const double *c, const double *d,
+                                      double *r_out) {
+  int64_t wpr = words_per_row(k);
+  const double *cb = c + (int64_t)basis * k;
+  double den = 0.0;
+  for (int64_t j = 0; j < k; ++j) den += (d ? d[j] : 1.0) * cb[j] * cb[j];
+#ifdef _OPENMP
+#pragma omp parallel for schedule(static)
+#endif
+  for (int64_t i = 0; i < n; ++i) {
+    const uint32_t *row = bits + ((int64_t)basis * n + i) * wpr;
+    double num = 0.0;
+    for (int64_t j = 0; j < k; ++j) {
+      double res = orc_half_to_double(w[i * k + j]) - approx_at(n, k, kb, bits, r, c, i, j, basis);
+      num += (d ? d[j] : 1.0) * res * sign_at(row, j) * cb[j];
+    }
+    r_out[i] = den > 0.0 ? num / den : 0.0;
+  }
+}
+
+/* Column step of basis `basis`: c_out[j] for every column. */
+ORC_EXPORT void orc_decomp_col_scales(const uint16_t *w, int64_t n, int64_t k, int32_t kb, int32_t basis,
+                                      const uint32_t *bits, const double *r, const double *c, double *c_out) {
+  int64_t wpr = words_per_row(k);
+  const double *rb = r + (int64_t)basis * n;
+  double den = 0.0;
+  for (int64_t i = 0; i < n; ++i) den += rb[i] * rb[i];
+#ifdef _OPENMP
+#pragma omp parallel for schedule(static)
+#endif
+  for (int64_t j = 0; j < k; ++j) {
+    double num = 0.0;
+    for (int64_t i = 0; i < n; ++i) {
+      const uint32_t *row = bits + ((int64_t)basis * n + i) * wpr;
+      double res = orc_half_to_double(w[i * k + j]) - approx_at(n, k, kb, bits, r, c, i, j, basis);
+      num += res * sign_at(row, j) * rb[i];
+    }
+    c_out[j] = den > 0.0 ? num / den : 0.0;
+  }
+}
+
+/* Sign step: joint exhaustive search of every element; writes all kb bases. */
+ORC_EXPORT void orc_decomp_signs(const uint16_t *w, int64_t n, int64_t k, int32_t kb, const double *r,
+                                 const double *c, uint32_t *bits_out) {
+  int64_t wpr = words_per_row(k);
+  for (int64_t t = 0; t < (int64_t)kb * n * wpr; ++t) bits_out[t] = 0;
+#ifdef _OPENMP
+#pragma omp parallel for schedule(static)
+#endif
+  for (int64_t i = 0; i < n; ++i) {
+    for (int64_t j = 0; j < k; ++j) {
+      double wv = orc_half_to_double(w[i * k + j]);
+      double best = INFINITY;
+      int32_t best_m = 0;
+      for (int32_t m = 0; m < (1 << kb); ++m) {
+        double sum = 0.0;
+        for (int32_t b = 0; b < kb; ++b) {
+          double p = r[(int64_t)b * n + i] * c[(int64_t)b * k + j];
+          sum = ((m >> b) & 1) ? sum + p : sum - p;
+        }
+        double e = fabs(wv - sum);
+        if (e < best) {
+          best = e;
+          best_m = m;
+        }
+      }
+      for (int32_t b = 0; b < kb; ++b)
+        if ((best_m >> b) & 1) bits_out[((int64_t)b * n + i) * wpr + j / 32] |= 1u << (j % 32);
+    }
+  }
+}
+
+/* Initial signs of basis `basis`: +1 where the residual of the other bases is >= 0. */
+ORC_EXPORT void orc_decomp_residual_signs(const uint16_t *w, int64_t n, int64_t k, int32_t kb, int32_t basis,
+                                          const uint32_t *bits, const double *r, const double *c,
+                                          uint32_t *basis_bits_out) {
+  int64_t wpr = words_per_row(k);
+  for (int64_t t = 0; t < n * wpr; ++t) basis_bits_out[t] = 0;
+  for (int64_t i = 0; i < n; ++i)
+    for (int64_t j = 0; j < k; ++j) {
+      double res = orc_half_to_double(w[i * k + j]) - approx_at(n, k, kb, bits, r, c, i, j, basis);
+      if (res >= 0.0) basis_bits_out[i * wpr + j / 32] |= 1u << (j % 32);
+    }
+}
+
+/* E = sum_ij d_j (W_ij - W_hat_ij)^2. */
+ORC_EXPORT double orc_decomp_error(const uint16_t *w, int64_t n, int64_t k, int32_t kb, const uint32_t *bits,
+                                   const double *r, const double *c, const double *d) {
+  double e = 0.0;
+  for (int64_t i = 0; i < n; ++i)
+    for (int64_t j = 0; j < k; ++j) {
+      double res = orc_half_to_double(w[i * k + j]) - approx_at(n, k, kb, bits, r, c, i, j, -1);
+      e += (d ? d[j] : 1.0) * res * res;
+    }
+  return e;
+}
+
+/* The whole decomposition.  bits [kb][n][ceil(k/32)]; r16 [kb][n], c16 [kb][k]
+ * fp16; r64, c64 (may be NULL) receive the fp64 scales before rounding.
+ * trace (may be NULL) receives 2 + iters * (2 kb + 1) errors: after the
+ * initialisation, after every row, column and sign step of every iteration,
+ * and after the output rounding and its sign step. */
+ORC_EXPORT int orc_decompose(const uint16_t *w, int64_t n, int64_t k, int32_t kb, int32_t iters, const double *d,
+                             uint32_t *bits, uint16_t *r16, uint16_t *c16, double *r64, double *c64,
+                             double *trace) {
+  if (kb < 1 || kb > 4 || n < 1 || k < 1 || iters < 0) return 1;
+  int64_t wpr = words_per_row(k);
+  double *r = (double *)calloc((size_t)kb * n, sizeof(double));
+  double *c = (double *)calloc((size_t)kb * k, sizeof(double));
+  double *tmp = (double *)malloc((size_t)(n > k ? n : k) * sizeof(double));
+  int64_t tr = 0;
+  for (int64_t t = 0; t < (int64_t)kb * n * wpr; ++t) bits[t] = 0;
+  for (int32_t b = 0; b < kb; ++b) {
+    for (int64_t j = 0; j < k; ++j) c[(int64_t)b * k + j] = 1.0;
+    orc_decomp_residual_signs(w, n, k, kb, b, bits, r, c, bits + (int64_t)b * n * wpr);
+    orc_decomp_row_scales(w, n, k, kb, b, bits, r, c, d, tmp);
+    memcpy(r + (int64_t)b * n, tmp, (size_t)n * sizeof(double));
+    orc_decomp_col_scales(w, n, k, kb, b, bits, r, c, tmp);
+    memcpy(c + (int64_t)b * k, tmp, (size_t)k * sizeof(double));
+  }
+  if (trace) trace[tr++] = orc_decomp_error(w, n, k, kb, bits, r, c, d);
+  for (int32_t it = 0; it < iters; ++it) {
+    for (int32_t b = 0; b < kb; ++b) {
+      orc_decomp_row_scales(w, n, k, kb, b, bits, r, c, d, tmp);
+      memcpy(r + (int64_t)b * n, tmp, (size_t)n * sizeof(double));
+      if (trace) trace[tr++] = orc_decomp_error(w, n, k, kb, bits, r, c, d);
+      orc_decomp_col_scales(w, n, k, kb, b, bits, r, c, tmp);
+      memcpy(c + (int64_t)b * k, tmp, (size_t)k * sizeof(double));
+      if (trace) trace[tr++] = orc_decomp_error(w, n, k, kb, bits, r, c, d);
+    }
+    orc_decomp_signs(w, n, k, kb, r, c, bits);
+    if (trace) trace[tr++] = orc_decomp_error(w, n, k, kb, bits, r, c, d);
+  }
+  if (r64) memcpy(r64, r, (size_t)kb * n * sizeof(double));
+  if (c64) memcpy(c64, c, (size_t)kb * k * sizeof(double));
+  for (int64_t t = 0; t < (int64_t)kb * n; ++t) {
+    r16[t] = orc_double_to_half(r[t]);
+    r[t] = orc_half_to_double(r16[t]);
+  }
+  for (int64_t t = 0; t < (int64_t)kb * k; ++t) {
+    c16[t] = orc_double_to_half(c[t]);
+    c[t] = orc_half_to_double(c16[t]);
+  }
+  orc_decomp_signs(w, n, k, kb, r, c, bits);
+  if (trace) trace[tr++] = orc_decomp_error(w, n, k, kb, bits, r, c, d);
+  free(r);
+  free(c);
+  free(tmp);
+  return 0;
 }
 
 ORC_EXPORT int orc_max_threads(void) {

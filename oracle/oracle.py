@@ -77,6 +77,14 @@ def _declare(L):
     L.orc_half_luts.argtypes = [I64, I64, I32, I32, I32, P, P, P, P, I64, P, P]
     L.orc_dense_f16_gemv.argtypes = [P, I64, I64, P, I64, P, P]
     L.orc_max_threads.restype = ctypes.c_int
+    L.orc_decomp_row_scales.argtypes = [P, I64, I64, I32, I32, P, P, P, P, P]
+    L.orc_decomp_col_scales.argtypes = [P, I64, I64, I32, I32, P, P, P, P]
+    L.orc_decomp_signs.argtypes = [P, I64, I64, I32, P, P, P]
+    L.orc_decomp_residual_signs.argtypes = [P, I64, I64, I32, I32, P, P, P, P]
+    L.orc_decomp_error.restype = ctypes.c_double
+    L.orc_decomp_error.argtypes = [P, I64, I64, I32, P, P, P, P]
+    L.orc_decompose.restype = ctypes.c_int
+    L.orc_decompose.argtypes = [P, I64, I64, I32, I32, P, P, P, P, P, P, P]
 
 
 def _p(a):
@@ -257,3 +265,72 @@ def contract_bound(mag) -> np.ndarray:
 def tight_bound(y_ref, mag) -> np.ndarray:
     """Diagnostic bound: fp16 output rounding plus fp32 accumulation, 2^-11 |y| + 2^-20 sum|W x|."""
     return np.abs(y_ref) * 2.0 ** -11 + np.asarray(mag) * 2.0 ** -20
+
+
+# ---------------------------------------------------------------- offline decomposition
+# W fp16 [n][k] (uint16 bits); bits canonical [kb][n][ceil(k/32)]; r fp64 [kb][n]; c fp64 [kb][k];
+# d fp64 [k] column weights or None (all 1).
+
+def _opt(a, dtype):
+    return None if a is None else _c(a, dtype)
+
+
+def decomp_row_scales(w, kb, basis, bits, r, c, d=None) -> np.ndarray:
+    w = _c(w, np.uint16)
+    n, k = w.shape
+    out = np.empty(n, np.float64)
+    bits, r, c, d = _c(bits, np.uint32), _c(r, np.float64), _c(c, np.float64), _opt(d, np.float64)
+    lib().orc_decomp_row_scales(_p(w), n, k, kb, basis, _p(bits), _p(r), _p(c), _p(d), _p(out))
+    return out
+
+
+def decomp_col_scales(w, kb, basis, bits, r, c) -> np.ndarray:
+    w = _c(w, np.uint16)
+    n, k = w.shape
+    out = np.empty(k, np.float64)
+    bits, r, c = _c(bits, np.uint32), _c(r, np.float64), _c(c, np.float64)
+    lib().orc_decomp_col_scales(_p(w), n, k, kb, basis, _p(bits), _p(r), _p(c), _p(out))
+    return out
+
+
+def decomp_signs(w, kb, r, c) -> np.ndarray:
+    w = _c(w, np.uint16)
+    n, k = w.shape
+    out = np.empty((kb, n, (k + 31) // 32), np.uint32)
+    r, c = _c(r, np.float64), _c(c, np.float64)
+    lib().orc_decomp_signs(_p(w), n, k, kb, _p(r), _p(c), _p(out))
+    return out
+
+
+def decomp_residual_signs(w, kb, basis, bits, r, c) -> np.ndarray:
+    w = _c(w, np.uint16)
+    n, k = w.shape
+    out = np.empty((n, (k + 31) // 32), np.uint32)
+    bits, r, c = _c(bits, np.uint32), _c(r, np.float64), _c(c, np.float64)
+    lib().orc_decomp_residual_signs(_p(w), n, k, kb, basis, _p(bits), _p(r), _p(c), _p(out))
+    return out
+
+
+def decomp_error(w, kb, bits, r, c, d=None) -> float:
+    w = _c(w, np.uint16)
+    n, k = w.shape
+    bits, r, c, d = _c(bits, np.uint32), _c(r, np.float64), _c(c, np.float64), _opt(d, np.float64)
+    return float(lib().orc_decomp_error(_p(w), n, k, kb, _p(bits), _p(r), _p(c), _p(d)))
+
+
+def decompose(w, kb: int, iters: int, d=None) -> dict:
+    """The whole decomposition: bits, fp16 r/c, the fp64 scales before rounding, the error trace."""
+    w = _c(w, np.uint16)
+    n, k = w.shape
+    d = _opt(d, np.float64)
+    bits = np.empty((kb, n, (k + 31) // 32), np.uint32)
+    r16 = np.empty((kb, n), np.uint16)
+    c16 = np.empty((kb, k), np.uint16)
+    r64 = np.empty((kb, n), np.float64)
+    c64 = np.empty((kb, k), np.float64)
+    trace = np.empty(2 + iters * (2 * kb + 1), np.float64)
+    err = lib().orc_decompose(_p(w), n, k, kb, iters, _p(d), _p(bits), _p(r16), _p(c16), _p(r64), _p(c64),
+                              _p(trace))
+    if err:
+        raise ValueError("unsupported decomposition arguments")
+    return {"bits": bits, "r16": r16, "c16": c16, "r64": r64, "c64": c64, "trace": trace}

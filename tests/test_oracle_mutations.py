@@ -15,6 +15,7 @@ import pytest
 
 from binary_basis_lut_amd import inputs as I
 
+from . import test_oracle_decomp as D
 from .test_oracle_grouped import exact_y_grouped
 from .test_oracle_pins import bits_of, exact_y, f16, layer_from
 
@@ -48,6 +49,18 @@ MUTANTS = {
                                       "const uint16_t *rrow = L->r_g + ((int64_t)0 * L->n + i) * L->ngroups;"),
     "grouped_group_boundary_off_by_one": ("{ return row_group ? j / row_group : 0; }",
                                           "{ return row_group ? (j > 0 ? (j - 1) / row_group : 0) : 0; }"),
+    "decomp_row_denominator_not_squared": ("den += (d ? d[j] : 1.0) * cb[j] * cb[j];",
+                                           "den += (d ? d[j] : 1.0) * cb[j];"),
+    "decomp_row_residual_keeps_own_basis": (
+        "approx_at(n, k, kb, bits, r, c, i, j, basis);\n      num += (d ? d[j] : 1.0)",
+        "approx_at(n, k, kb, bits, r, c, i, j, -1);\n      num += (d ? d[j] : 1.0)"),
+    "decomp_col_denominator_not_squared": ("den += rb[i] * rb[i];", "den += rb[i];"),
+    "decomp_col_ignores_row_scale": ("num += res * sign_at(row, j) * rb[i];", "num += res * sign_at(row, j);"),
+    "decomp_sign_ties_to_largest": ("if (e < best) {", "if (e <= best) {"),
+    "decomp_sign_skips_last_basis": ("for (int32_t b = 0; b < kb; ++b) {\n          double p",
+                                     "for (int32_t b = 0; b + 1 < kb; ++b) {\n          double p"),
+    "decomp_weights_ignored": ("num += (d ? d[j] : 1.0) * res * sign_at(row, j) * cb[j];",
+                               "num += res * sign_at(row, j) * cb[j];"),
 }
 
 
@@ -137,7 +150,45 @@ def chk_grouped_bruteforce(O):
     return np.array_equal(O.gemv_dense(lay, x)[0], exact_y_grouped(lay, x))
 
 
-CHECKS = [chk_popcount, chk_one_hot, chk_bruteforce, chk_half_numpy, chk_grouped_one_hot, chk_grouped_bruteforce]
+def chk_decomp_steps(O):
+    """Row and column steps at their least-squares vertex (weighted rows), the sign step at the exhaustive
+    optimum with smallest-index ties, and a never-increasing error trace."""
+    w, bits, r, c = D.random_state(9, 70, 3, 1)
+    d = I.calibration_weights(70, 0.05, seed=(81, 70))
+    rn = O.decomp_row_scales(w, 3, 1, bits, r, c, d)
+    cn = O.decomp_col_scales(w, 3, 2, bits, r, c)
+    for i in (0, 8):
+        def f(t):
+            rr = r.copy()
+            rr[1] = rn
+            rr[1, i] = t
+            return D.err(w, bits, rr, c, d)
+        if not abs(D.vertex_offset(f, rn[i], 0.05)) < 1e-7:
+            return False
+    for j in (0, 69):
+        def g(t):
+            cc = c.copy()
+            cc[2] = cn
+            cc[2, j] = t
+            return D.err(w, bits, r, cc)
+        if not abs(D.vertex_offset(g, cn[j], 0.2)) < 1e-7:
+            return False
+    rng = I.stream(83, 3)
+    rd, cd = D.dyadic_scales(rng, 3, 6, 40)
+    wd = (rng.integers(-16, 17, size=(6, 40)) * 0.0625).astype(np.float16).view(np.uint16)
+    s = D.signs_of(O.decomp_signs(wd, 3, rd, cd), 40)
+    for i in range(6):
+        for j in range(40):
+            errs = [abs(D.wf(wd)[i, j] - sum((1.0 if (m >> b) & 1 else -1.0) * rd[b, i] * cd[b, j]
+                                             for b in range(3))) for m in range(8)]
+            if sum(1 << b for b in range(3) if s[b, i, j] > 0) != errs.index(min(errs)):
+                return False
+    t = O.decompose(I.decomp_matrix(20, 129, seed=(85, 20, 129)), 3, 2, d=None)["trace"]
+    return bool(np.all(np.diff(t[:-1]) <= 1e-12 * t[0]))
+
+
+CHECKS = [chk_popcount, chk_one_hot, chk_bruteforce, chk_half_numpy, chk_grouped_one_hot, chk_grouped_bruteforce,
+          chk_decomp_steps]
 
 
 def test_unmutated_oracle_passes_every_check(orc):
