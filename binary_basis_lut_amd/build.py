@@ -16,7 +16,8 @@ PKG = Path(__file__).resolve().parent
 ROOT = PKG.parent
 CSRC = PKG / "csrc"
 SOURCES = [CSRC / "fluxbin.hip"] + [CSRC / f"gemv_g{g}_rs{rs}.hip" for g in (4, 8) for rs in (0, 1)]
-HEADERS = [CSRC / "common.hpp", CSRC / "gemv_kernel.hpp", CSRC / "aux_kernels.hpp", ROOT / "include" / "fluxbin.h"]
+HEADERS = [CSRC / "common.hpp", CSRC / "gemv_kernel.hpp", CSRC / "aux_kernels.hpp", CSRC / "decomp_kernels.hpp",
+           ROOT / "include" / "fluxbin.h"]
 DEPS = SOURCES + HEADERS
 BUILD = PKG / "_build"
 LIB = BUILD / "libfluxbin.so"

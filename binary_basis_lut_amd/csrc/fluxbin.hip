@@ -17,6 +17,7 @@
 #include <vector>
 
 #include "aux_kernels.hpp"
+#include "decomp_kernels.hpp"
 
 using namespace fluxbin;
 
@@ -246,6 +247,89 @@ int grid_for(int64_t items, int per_thread_block = 256) {
   if (g < 1) g = 1;
   if (g > 65536) g = 65536;
   return (int)g;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// offline decomposition: argument checks and launches
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr int64_t kDecompMaxRows = (int64_t)1 << 22;  // column-step grid.y = rows / 64 <= 65535
+
+fluxbin_status decomp_shape(int64_t n, int64_t k, int32_t kb) {
+  if (n < 1 || k < 1) return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "n = %lld, k = %lld (must be >= 1)", (long long)n,
+                                  (long long)k);
+  if (n > kDecompMaxRows || k > ((int64_t)1 << 30))
+    return fail(FLUXBIN_ERR_UNSUPPORTED, "n above 2^22 or k above 2^30");
+  if (kb < 1 || kb > 4) return fail(FLUXBIN_ERR_UNSUPPORTED, "kb = %d (supported: 1..4)", kb);
+  return FLUXBIN_OK;
+}
+
+size_t decomp_ws_bytes(int64_t n, int64_t k) {
+  return sizeof(double) * (size_t)(cdiv(n, kDecompRowChunk) * k + kDecompErrBlocks + 16 + 4 * (n + k));
+}
+
+// Workspace: [chunks][k] column partials, kDecompErrBlocks error partials,
+// 16 scalars, then room for fp64 copies of the rounded scales (up to 4 bases).
+struct DecompWs {
+  double *partial, *errp, *scal, *rounded;
+};
+
+fluxbin_status decomp_ws(void *ws, size_t bytes, int64_t n, int64_t k, DecompWs *out) {
+  const size_t need = decomp_ws_bytes(n, k);
+  if (!ws || bytes < need)
+    return fail(FLUXBIN_ERR_WORKSPACE, "decomposition workspace of %zu bytes needed, %zu given", need,
+                ws ? bytes : (size_t)0);
+  if (!aligned(ws, 256)) return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "workspace not 256-byte aligned");
+  out->partial = static_cast<double *>(ws);
+  out->errp = out->partial + cdiv(n, kDecompRowChunk) * k;
+  out->scal = out->errp + kDecompErrBlocks;
+  out->rounded = out->scal + 16;
+  return FLUXBIN_OK;
+}
+
+dim3 grid1(int64_t items, int per = 256) { return dim3((unsigned)cdiv(items, per)); }
+
+void run_row(hipStream_t st, const uint16_t *w, int64_t n, int64_t k, int kb, int basis, const uint32_t *bits,
+             const double *r, const double *c, const double *d, double *r_out, const DecompWs &ws) {
+  hipLaunchKernelGGL(decomp_sumsq_kernel, dim3(1), dim3(256), 0, st, c + (int64_t)basis * k, d, k, ws.scal);
+  hipLaunchKernelGGL(decomp_row_kernel, grid1(n, 4), dim3(256), 0, st, w, n, k, kb, basis, bits, r, c, d, ws.scal,
+                     r_out);
+}
+
+void run_col(hipStream_t st, const uint16_t *w, int64_t n, int64_t k, int kb, int basis, const uint32_t *bits,
+             const double *r, const double *c, double *c_out, const DecompWs &ws) {
+  const int64_t chunks = cdiv(n, kDecompRowChunk);
+  hipLaunchKernelGGL(decomp_sumsq_kernel, dim3(1), dim3(256), 0, st, r + (int64_t)basis * n, nullptr, n, ws.scal);
+  hipLaunchKernelGGL(decomp_col_partial_kernel, dim3((unsigned)cdiv(k, 256), (unsigned)chunks), dim3(256), 0, st, w,
+                     n, k, kb, basis, bits, r, c, ws.partial);
+  hipLaunchKernelGGL(decomp_col_finish_kernel, grid1(k), dim3(256), 0, st, ws.partial, chunks, k, ws.scal, c_out);
+}
+
+void run_signs(hipStream_t st, const uint16_t *w, int64_t n, int64_t k, int kb, const double *r, const double *c,
+               uint32_t *bits) {
+  const dim3 g = grid1(n * cdiv(k, 64), 4);
+  switch (kb) {
+    case 1: hipLaunchKernelGGL(decomp_sign_kernel<1>, g, dim3(256), 0, st, w, n, k, r, c, bits); break;
+    case 2: hipLaunchKernelGGL(decomp_sign_kernel<2>, g, dim3(256), 0, st, w, n, k, r, c, bits); break;
+    case 3: hipLaunchKernelGGL(decomp_sign_kernel<3>, g, dim3(256), 0, st, w, n, k, r, c, bits); break;
+    default: hipLaunchKernelGGL(decomp_sign_kernel<4>, g, dim3(256), 0, st, w, n, k, r, c, bits); break;
+  }
+}
+
+void run_residual_signs(hipStream_t st, const uint16_t *w, int64_t n, int64_t k, int kb, int basis,
+                        const uint32_t *bits, const double *r, const double *c, uint32_t *out) {
+  hipLaunchKernelGGL(decomp_residual_sign_kernel, grid1(n * cdiv(k, 64), 4), dim3(256), 0, st, w, n, k, kb, basis,
+                     bits, r, c, out);
+}
+
+void run_error(hipStream_t st, const uint16_t *w, int64_t n, int64_t k, int kb, const uint32_t *bits,
+               const double *r, const double *c, const double *d, double *out, const DecompWs &ws) {
+  hipLaunchKernelGGL(decomp_error_partial_kernel, dim3(kDecompErrBlocks), dim3(256), 0, st, w, n, k, kb, bits, r, c,
+                     d, ws.errp);
+  hipLaunchKernelGGL(decomp_error_finish_kernel, dim3(1), dim3(64), 0, st, ws.errp, kDecompErrBlocks, out);
 }
 
 }  // namespace
@@ -554,6 +638,130 @@ fluxbin_status fluxbin_dense_gemv_f16(const uint16_t *w, int64_t n, int64_t k, c
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "dense gemv launch");
   return ok();
+}
+
+// ---------------------------------------------------------------------------
+// offline decomposition
+// ---------------------------------------------------------------------------
+
+fluxbin_status fluxbin_decomp_workspace_size(int64_t n, int64_t k, int32_t kb, size_t *bytes) {
+  fluxbin_status st = decomp_shape(n, k, kb);
+  if (st) return st;
+  if (!bytes) return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  *bytes = decomp_ws_bytes(n, k);
+  return ok();
+}
+
+fluxbin_status fluxbin_decomp_row_scales(const uint16_t *w, int64_t n, int64_t k, int32_t kb, int32_t basis,
+                                         const uint32_t *bits, const double *r, const double *c,
+                                         const double *col_weight, double *r_out, void *workspace,
+                                         size_t workspace_bytes, void *stream) {
+  fluxbin_status st = decomp_shape(n, k, kb);
+  if (st) return st;
+  if (basis < 0 || basis >= kb) return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "basis = %d outside [0, %d)", basis, kb);
+  if (!w || !bits || !r || !c || !r_out) return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "NULL pointer");
+  DecompWs ws;
+  st = decomp_ws(workspace, workspace_bytes, n, k, &ws);
+  if (st) return st;
+  run_row((hipStream_t)stream, w, n, k, kb, basis, bits, r, c, col_weight, r_out, ws);
+  hipError_t e = hipGetLastError();
+  return e != hipSuccess ? hip_fail(e, "decomposition row step launch") : ok();
+}
+
+fluxbin_status fluxbin_decomp_col_scales(const uint16_t *w, int64_t n, int64_t k, int32_t kb, int32_t basis,
+                                         const uint32_t *bits, const double *r, const double *c, double *c_out,
+                                         void *workspace, size_t workspace_bytes, void *stream) {
+  fluxbin_status st = decomp_shape(n, k, kb);
+  if (st) return st;
+  if (basis < 0 || basis >= kb) return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "basis = %d outside [0, %d)", basis, kb);
+  if (!w || !bits || !r || !c || !c_out) return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "NULL pointer");
+  DecompWs ws;
+  st = decomp_ws(workspace, workspace_bytes, n, k, &ws);
+  if (st) return st;
+  run_col((hipStream_t)stream, w, n, k, kb, basis, bits, r, c, c_out, ws);
+  hipError_t e = hipGetLastError();
+  return e != hipSuccess ? hip_fail(e, "decomposition column step launch") : ok();
+}
+
+fluxbin_status fluxbin_decomp_signs(const uint16_t *w, int64_t n, int64_t k, int32_t kb, const double *r,
+                                    const double *c, uint32_t *bits_out, void *stream) {
+  fluxbin_status st = decomp_shape(n, k, kb);
+  if (st) return st;
+  if (!w || !r || !c || !bits_out) return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "NULL pointer");
+  run_signs((hipStream_t)stream, w, n, k, kb, r, c, bits_out);
+  hipError_t e = hipGetLastError();
+  return e != hipSuccess ? hip_fail(e, "decomposition sign step launch") : ok();
+}
+
+fluxbin_status fluxbin_decomp_residual_signs(const uint16_t *w, int64_t n, int64_t k, int32_t kb, int32_t basis,
+                                             const uint32_t *bits, const double *r, const double *c,
+                                             uint32_t *basis_bits_out, void *stream) {
+  fluxbin_status st = decomp_shape(n, k, kb);
+  if (st) return st;
+  if (basis < 0 || basis >= kb) return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "basis = %d outside [0, %d)", basis, kb);
+  if (!w || !bits || !r || !c || !basis_bits_out) return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "NULL pointer");
+  run_residual_signs((hipStream_t)stream, w, n, k, kb, basis, bits, r, c, basis_bits_out);
+  hipError_t e = hipGetLastError();
+  return e != hipSuccess ? hip_fail(e, "decomposition residual-sign launch") : ok();
+}
+
+fluxbin_status fluxbin_decomp_error(const uint16_t *w, int64_t n, int64_t k, int32_t kb, const uint32_t *bits,
+                                    const double *r, const double *c, const double *col_weight, double *err_out,
+                                    void *workspace, size_t workspace_bytes, void *stream) {
+  fluxbin_status st = decomp_shape(n, k, kb);
+  if (st) return st;
+  if (!w || !bits || !r || !c || !err_out) return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "NULL pointer");
+  DecompWs ws;
+  st = decomp_ws(workspace, workspace_bytes, n, k, &ws);
+  if (st) return st;
+  run_error((hipStream_t)stream, w, n, k, kb, bits, r, c, col_weight, err_out, ws);
+  hipError_t e = hipGetLastError();
+  return e != hipSuccess ? hip_fail(e, "decomposition error launch") : ok();
+}
+
+fluxbin_status fluxbin_decompose(const uint16_t *w, int64_t n, int64_t k, int32_t kb, int32_t iters,
+                                 const double *col_weight, uint32_t *bits, uint16_t *r16, uint16_t *c16, double *r64,
+                                 double *c64, double *trace, void *workspace, size_t workspace_bytes, void *stream) {
+  fluxbin_status st = decomp_shape(n, k, kb);
+  if (st) return st;
+  if (iters < 0 || iters > 10000) return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "iters = %d (0..10000)", iters);
+  if (!w || !bits || !r16 || !c16 || !r64 || !c64) return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "NULL pointer");
+  DecompWs ws;
+  st = decomp_ws(workspace, workspace_bytes, n, k, &ws);
+  if (st) return st;
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t wpr = cdiv(k, 32);
+  int64_t tr = 0;
+  hipLaunchKernelGGL(decomp_zero_words_kernel, grid1(kb * n * wpr), dim3(256), 0, s, bits, kb * n * wpr);
+  hipLaunchKernelGGL(decomp_fill_kernel, grid1(kb * n), dim3(256), 0, s, r64, kb * n, 0.0);
+  hipLaunchKernelGGL(decomp_fill_kernel, grid1(kb * k), dim3(256), 0, s, c64, kb * k, 0.0);
+  // initialisation: basis b from the signs of the residual of bases 0..b-1
+  for (int b = 0; b < kb; ++b) {
+    double *rb = r64 + (int64_t)b * n, *cb = c64 + (int64_t)b * k;
+    hipLaunchKernelGGL(decomp_fill_kernel, grid1(k), dim3(256), 0, s, cb, k, 1.0);
+    run_residual_signs(s, w, n, k, kb, b, bits, r64, c64, bits + (int64_t)b * n * wpr);
+    run_row(s, w, n, k, kb, b, bits, r64, c64, col_weight, rb, ws);
+    run_col(s, w, n, k, kb, b, bits, r64, c64, cb, ws);
+  }
+  if (trace) run_error(s, w, n, k, kb, bits, r64, c64, col_weight, trace + tr++, ws);
+  for (int it = 0; it < iters; ++it) {
+    for (int b = 0; b < kb; ++b) {
+      run_row(s, w, n, k, kb, b, bits, r64, c64, col_weight, r64 + (int64_t)b * n, ws);
+      if (trace) run_error(s, w, n, k, kb, bits, r64, c64, col_weight, trace + tr++, ws);
+      run_col(s, w, n, k, kb, b, bits, r64, c64, c64 + (int64_t)b * k, ws);
+      if (trace) run_error(s, w, n, k, kb, bits, r64, c64, col_weight, trace + tr++, ws);
+    }
+    run_signs(s, w, n, k, kb, r64, c64, bits);
+    if (trace) run_error(s, w, n, k, kb, bits, r64, c64, col_weight, trace + tr++, ws);
+  }
+  // output: fp16 scales and a last sign step against them
+  double *rr = ws.rounded, *cr = ws.rounded + kb * n;
+  hipLaunchKernelGGL(decomp_round_kernel, grid1(kb * n), dim3(256), 0, s, r64, kb * n, r16, rr);
+  hipLaunchKernelGGL(decomp_round_kernel, grid1(kb * k), dim3(256), 0, s, c64, kb * k, c16, cr);
+  run_signs(s, w, n, k, kb, rr, cr, bits);
+  if (trace) run_error(s, w, n, k, kb, bits, rr, cr, col_weight, trace + tr++, ws);
+  hipError_t e = hipGetLastError();
+  return e != hipSuccess ? hip_fail(e, "decomposition launch") : ok();
 }
 
 }  // extern "C"

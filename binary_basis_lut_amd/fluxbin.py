@@ -84,12 +84,21 @@ _decl("fluxbin_lut_size", ctypes.c_int, [P, I64, ctypes.POINTER(ctypes.c_size_t)
 _decl("fluxbin_build_lut", ctypes.c_int, [P, P, I64, P, P])
 _decl("fluxbin_gemv", ctypes.c_int, [P, P, P, I64, P])
 _decl("fluxbin_dense_gemv_f16", ctypes.c_int, [P, I64, I64, P, P, I64, P])
+_decl("fluxbin_decomp_workspace_size", ctypes.c_int, [I64, I64, I32, ctypes.POINTER(ctypes.c_size_t)])
+_decl("fluxbin_decompose", ctypes.c_int, [P, I64, I64, I32, I32, P, P, P, P, P, P, P, P, ctypes.c_size_t, P])
+_decl("fluxbin_decomp_row_scales", ctypes.c_int, [P, I64, I64, I32, I32, P, P, P, P, P, P, ctypes.c_size_t, P])
+_decl("fluxbin_decomp_col_scales", ctypes.c_int, [P, I64, I64, I32, I32, P, P, P, P, P, ctypes.c_size_t, P])
+_decl("fluxbin_decomp_signs", ctypes.c_int, [P, I64, I64, I32, P, P, P, P])
+_decl("fluxbin_decomp_residual_signs", ctypes.c_int, [P, I64, I64, I32, I32, P, P, P, P, P])
+_decl("fluxbin_decomp_error", ctypes.c_int, [P, I64, I64, I32, P, P, P, P, P, P, ctypes.c_size_t, P])
 
 SYMBOLS = [
     "fluxbin_abi_version", "fluxbin_status_string", "fluxbin_last_error", "fluxbin_tiled_words", "fluxbin_pack",
     "fluxbin_relayout", "fluxbin_tiled_scale_elems", "fluxbin_relayout_scales", "fluxbin_vcm_gather",
     "fluxbin_workspace_size", "fluxbin_create", "fluxbin_destroy", "fluxbin_get_plan", "fluxbin_lut_size",
-    "fluxbin_build_lut", "fluxbin_gemv", "fluxbin_dense_gemv_f16",
+    "fluxbin_build_lut", "fluxbin_gemv", "fluxbin_dense_gemv_f16", "fluxbin_decomp_workspace_size",
+    "fluxbin_decompose", "fluxbin_decomp_row_scales", "fluxbin_decomp_col_scales", "fluxbin_decomp_signs",
+    "fluxbin_decomp_residual_signs", "fluxbin_decomp_error",
 ]
 
 
@@ -196,6 +205,48 @@ def fluxbin_gemv(handle, x, y, batch, stream=None):
 def fluxbin_dense_gemv_f16(w, n, k, x, y, batch, stream=None):
     _check(_lib.fluxbin_dense_gemv_f16(_ptr(w), n, k, _ptr(x), _ptr(y), batch, _stream(stream)),
            "fluxbin_dense_gemv_f16")
+
+
+def fluxbin_decomp_workspace_size(n, k, kb) -> int:
+    out = ctypes.c_size_t(0)
+    _check(_lib.fluxbin_decomp_workspace_size(n, k, kb, ctypes.byref(out)), "fluxbin_decomp_workspace_size")
+    return int(out.value)
+
+
+def fluxbin_decompose(w, n, k, kb, iters, col_weight, bits, r16, c16, r64, c64, trace, workspace, workspace_bytes,
+                      stream=None):
+    _check(_lib.fluxbin_decompose(_ptr(w), n, k, kb, iters, _ptr(col_weight), _ptr(bits), _ptr(r16), _ptr(c16),
+                                  _ptr(r64), _ptr(c64), _ptr(trace), _ptr(workspace), workspace_bytes,
+                                  _stream(stream)), "fluxbin_decompose")
+
+
+def fluxbin_decomp_row_scales(w, n, k, kb, basis, bits, r, c, col_weight, r_out, workspace, workspace_bytes,
+                              stream=None):
+    _check(_lib.fluxbin_decomp_row_scales(_ptr(w), n, k, kb, basis, _ptr(bits), _ptr(r), _ptr(c), _ptr(col_weight),
+                                          _ptr(r_out), _ptr(workspace), workspace_bytes, _stream(stream)),
+           "fluxbin_decomp_row_scales")
+
+
+def fluxbin_decomp_col_scales(w, n, k, kb, basis, bits, r, c, c_out, workspace, workspace_bytes, stream=None):
+    _check(_lib.fluxbin_decomp_col_scales(_ptr(w), n, k, kb, basis, _ptr(bits), _ptr(r), _ptr(c), _ptr(c_out),
+                                          _ptr(workspace), workspace_bytes, _stream(stream)),
+           "fluxbin_decomp_col_scales")
+
+
+def fluxbin_decomp_signs(w, n, k, kb, r, c, bits_out, stream=None):
+    _check(_lib.fluxbin_decomp_signs(_ptr(w), n, k, kb, _ptr(r), _ptr(c), _ptr(bits_out), _stream(stream)),
+           "fluxbin_decomp_signs")
+
+
+def fluxbin_decomp_residual_signs(w, n, k, kb, basis, bits, r, c, basis_bits_out, stream=None):
+    _check(_lib.fluxbin_decomp_residual_signs(_ptr(w), n, k, kb, basis, _ptr(bits), _ptr(r), _ptr(c),
+                                              _ptr(basis_bits_out), _stream(stream)), "fluxbin_decomp_residual_signs")
+
+
+def fluxbin_decomp_error(w, n, k, kb, bits, r, c, col_weight, err_out, workspace, workspace_bytes, stream=None):
+    _check(_lib.fluxbin_decomp_error(_ptr(w), n, k, kb, _ptr(bits), _ptr(r), _ptr(c), _ptr(col_weight),
+                                     _ptr(err_out), _ptr(workspace), workspace_bytes, _stream(stream)),
+           "fluxbin_decomp_error")
 
 
 def raw_status(name: str, *args) -> int:

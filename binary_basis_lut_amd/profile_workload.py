@@ -11,6 +11,11 @@ profiles/ (each summary names the exact command).  Two modes:
       shape in the block-wise row-scale storage instead (--kb global and --ks
       salient bases, --sal-group salient columns per 128-column group);
 
+  python3 -m binary_basis_lut_amd.profile_workload decompose --n 4096 --k 4096 --kb 2 --iters 5 --reps 3
+      the offline decomposition of one synthetic fp16 matrix (HIP events
+      around fluxbin_decompose; no error trace), time per call and per
+      iteration;
+
   python3 -m binary_basis_lut_amd.profile_workload copy --bytes 1073741824 --reps 4
       a plain device-to-device copy of known size (torch's copy kernel): the
       reference that scales the FETCH_SIZE / WRITE_SIZE counters to bytes.
@@ -80,6 +85,44 @@ def run_gemv(args) -> None:
         d.close()
 
 
+def run_decompose(args) -> None:
+    import numpy as np
+    import torch
+
+    from binary_basis_lut_amd import fluxbin as F
+    from binary_basis_lut_amd import inputs as I
+
+    n, k, kb, iters = args.n, args.k, args.kb, args.iters
+    w = torch.from_numpy(I.decomp_matrix(n, k, seed=(7, n, k)).view(np.int16)).cuda()
+    nbytes = F.fluxbin_decomp_workspace_size(n, k, kb)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    wpr = (k + 31) // 32
+    bits = torch.empty(kb * n * wpr, dtype=torch.int32, device="cuda")
+    r16 = torch.empty(kb * n, dtype=torch.int16, device="cuda")
+    c16 = torch.empty(kb * k, dtype=torch.int16, device="cuda")
+    r64 = torch.empty(kb * n, dtype=torch.float64, device="cuda")
+    c64 = torch.empty(kb * k, dtype=torch.float64, device="cuda")
+    trace = torch.empty(2 + iters * (2 * kb + 1), dtype=torch.float64, device="cuda")
+
+    def call(with_trace):
+        F.fluxbin_decompose(w, n, k, kb, iters, None, bits, r16, c16, r64, c64, trace if with_trace else None, ws,
+                            nbytes)
+
+    call(True)  # warm-up, and the error trace of this matrix
+    torch.cuda.synchronize()
+    tr = trace.cpu().numpy()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.reps):
+        call(False)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.reps
+    norm = float((w.view(torch.float16).double() ** 2).sum())
+    print(f"decompose {n}x{k} kb={kb} iters={iters}: {ms:.3f} ms per call ({n * k / (ms * 1e-3) / 1e9:.2f} G "
+          f"weights/s); relative error init {tr[0] / norm:.5f} -> final {tr[-1] / norm:.5f}", flush=True)
+
+
 def run_copy(args) -> None:
     import torch
 
@@ -107,11 +150,17 @@ def main() -> int:
     g.add_argument("--kb", type=int, default=2, help="blockwise: global bases")
     g.add_argument("--ks", type=int, default=2, help="blockwise: salient bases")
     g.add_argument("--sal-group", type=int, default=8, choices=[8, 16])
+    dp = sub.add_parser("decompose")
+    dp.add_argument("--n", type=int, default=4096)
+    dp.add_argument("--k", type=int, default=4096)
+    dp.add_argument("--kb", type=int, default=2)
+    dp.add_argument("--iters", type=int, default=5)
+    dp.add_argument("--reps", type=int, default=3)
     c = sub.add_parser("copy")
     c.add_argument("--bytes", type=int, default=1 << 30)
     c.add_argument("--reps", type=int, default=4)
     args = ap.parse_args()
-    (run_gemv if args.mode == "gemv" else run_copy)(args)
+    {"gemv": run_gemv, "decompose": run_decompose, "copy": run_copy}[args.mode](args)
     return 0
 
 

@@ -244,6 +244,70 @@ fluxbin_status fluxbin_gemv(fluxbin_handle h, const uint16_t *x, uint16_t *y, in
 fluxbin_status fluxbin_dense_gemv_f16(const uint16_t *w, int64_t n, int64_t k, const uint16_t *x, uint16_t *y,
                                       int64_t batch, void *stream);
 
+/* ------------------------------------------------------------------------
+ * Offline decomposition W ~ sum_{b<kb} diag(r_b) B_b diag(c_b), the step that
+ * produces the bases the GEMV streams (FluxBin summary, section 3 bullets
+ * "Quantization" and "Parameter Optimization", appendices A.1 and A.2).
+ *
+ * Minimises E = sum_ij d_j (W_ij - W_hat_ij)^2 (weighted least squares with
+ * per-column weights d, NULL = all 1) by alternating exact minimisations:
+ *   row step (basis b):    r_b,i = sum_j d_j R_ij B_b,ij c_b,j / sum_j d_j c_b,j^2
+ *   column step (basis b): c_b,j = sum_i R_ij B_b,ij r_b,i / sum_i r_b,i^2
+ *     with R = W - sum_{l != b} diag(r_l) B_l diag(c_l); a zero denominator
+ *     gives 0;
+ *   sign step: every element takes the sign combination m in [0, 2^kb) (bit b
+ *     of m set = +1 on basis b) minimising |W_ij - sum_b (+-) r_b,i c_b,j|,
+ *     the sum taken in basis order in fp64 with each product rounded once;
+ *     ties go to the smallest m (an exhaustive search, globally optimal for
+ *     fixed scales).
+ * fluxbin_decompose: initialise basis b = 0..kb-1 in order (signs of the
+ * residual of the bases before it, R >= 0 -> +1; c_b = 1; one row step, one
+ * column step), run `iters` iterations (row then column step of every basis,
+ * then the sign step), round the scales to fp16 (nearest even), and end with
+ * a sign step against the rounded scales.  The Hessian-guided parts of the
+ * pages' pipeline (error compensation, saliency search) are not here.
+ *
+ * Layouts (all device memory): W fp16 [n][k] row-major; bits canonical sign
+ * words [kb][n][ceil(k/32)] (FLUXBIN_LAYOUT_ROWMAJOR per basis); r fp64
+ * [kb][n]; c fp64 [kb][k]; col_weight fp64 [k] or NULL.  1 <= kb <= 4,
+ * 1 <= n <= 2^22, 1 <= k <= 2^30.  Working scales are fp64; sums over a row
+ * or a column are split over lanes and workgroups in a fixed order (repeated
+ * calls give identical results).  workspace: 256-B aligned,
+ * fluxbin_decomp_workspace_size() bytes; one call at a time per workspace.
+ * ------------------------------------------------------------------------ */
+fluxbin_status fluxbin_decomp_workspace_size(int64_t n, int64_t k, int32_t kb, size_t *bytes);
+
+/* The whole decomposition.  Outputs bits [kb][n][ceil(k/32)], r16 [kb][n],
+ * c16 [kb][k] (fp16), r64/c64 (the fp64 scales before rounding), and, if
+ * trace != NULL, 2 + iters * (2 kb + 1) fp64 errors E: after the
+ * initialisation, after every row, column and sign step of every iteration,
+ * and after the rounding and its sign step. */
+fluxbin_status fluxbin_decompose(const uint16_t *w, int64_t n, int64_t k, int32_t kb, int32_t iters,
+                                 const double *col_weight, uint32_t *bits, uint16_t *r16, uint16_t *c16, double *r64,
+                                 double *c64, double *trace, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Single steps (the same kernels fluxbin_decompose runs).  The row step
+ * writes r_out [n] for basis `basis` (it reads the other bases' row scales
+ * only, so r_out may be r + basis * n); the column step writes c_out [k]
+ * likewise; the sign step writes all kb bases of bits_out; the residual-sign
+ * step writes basis_bits_out [n][ceil(k/32)] (+1 where W minus the other bases
+ * is >= 0); the error step writes E to err_out[0]. */
+fluxbin_status fluxbin_decomp_row_scales(const uint16_t *w, int64_t n, int64_t k, int32_t kb, int32_t basis,
+                                         const uint32_t *bits, const double *r, const double *c,
+                                         const double *col_weight, double *r_out, void *workspace,
+                                         size_t workspace_bytes, void *stream);
+fluxbin_status fluxbin_decomp_col_scales(const uint16_t *w, int64_t n, int64_t k, int32_t kb, int32_t basis,
+                                         const uint32_t *bits, const double *r, const double *c, double *c_out,
+                                         void *workspace, size_t workspace_bytes, void *stream);
+fluxbin_status fluxbin_decomp_signs(const uint16_t *w, int64_t n, int64_t k, int32_t kb, const double *r,
+                                    const double *c, uint32_t *bits_out, void *stream);
+fluxbin_status fluxbin_decomp_residual_signs(const uint16_t *w, int64_t n, int64_t k, int32_t kb, int32_t basis,
+                                             const uint32_t *bits, const double *r, const double *c,
+                                             uint32_t *basis_bits_out, void *stream);
+fluxbin_status fluxbin_decomp_error(const uint16_t *w, int64_t n, int64_t k, int32_t kb, const uint32_t *bits,
+                                    const double *r, const double *c, const double *col_weight, double *err_out,
+                                    void *workspace, size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -203,3 +203,32 @@ def test_block_wise_create_checks_salient_scale_alignment(fb):
     d.r_sal = 0x2002
     assert fb.raw_status("fluxbin_create", ctypes.byref(d), ctypes.byref(h)) == fb.ERR_INVALID_ARGUMENT
     assert "r_sal" in fb.fluxbin_last_error()
+
+
+def test_decomposition_host_validation(fb):
+    s = fb.raw_status
+    out = ctypes.c_size_t(0)
+    assert s("fluxbin_decomp_workspace_size", 4096, 4096, 2, ctypes.byref(out)) == fb.OK
+    assert out.value == 8 * (64 * 4096 + 1024 + 16 + 4 * 8192)
+    assert s("fluxbin_decomp_workspace_size", 4096, 4096, 5, ctypes.byref(out)) == fb.ERR_UNSUPPORTED
+    assert s("fluxbin_decomp_workspace_size", 0, 4096, 2, ctypes.byref(out)) == fb.ERR_INVALID_ARGUMENT
+    assert s("fluxbin_decomp_workspace_size", (1 << 22) + 1, 8, 2, ctypes.byref(out)) == fb.ERR_UNSUPPORTED
+    assert s("fluxbin_decomp_workspace_size", 8, 8, 2, None) == fb.ERR_INVALID_ARGUMENT
+    P = 0x1000
+    # basis out of range, NULL pointers, missing workspace
+    assert s("fluxbin_decomp_row_scales", P, 8, 8, 2, 2, P, P, P, None, P, P, 1 << 20, None) == fb.ERR_INVALID_ARGUMENT
+    assert s("fluxbin_decomp_row_scales", None, 8, 8, 2, 0, P, P, P, None, P, P, 1 << 20, None) == fb.ERR_INVALID_ARGUMENT
+    assert s("fluxbin_decomp_row_scales", P, 8, 8, 2, 0, P, P, P, None, P, None, 0, None) == fb.ERR_WORKSPACE
+    assert s("fluxbin_decomp_row_scales", P, 8, 8, 2, 0, P, P, P, None, P, P, 16, None) == fb.ERR_WORKSPACE
+    assert s("fluxbin_decomp_row_scales", P, 8, 8, 2, 0, P, P, P, None, P, P + 8, 1 << 20, None) == \
+        fb.ERR_INVALID_ARGUMENT  # misaligned workspace
+    assert s("fluxbin_decomp_col_scales", P, 8, 8, 2, -1, P, P, P, P, P, 1 << 20, None) == fb.ERR_INVALID_ARGUMENT
+    assert s("fluxbin_decomp_signs", P, 8, 8, 0, P, P, P, None) == fb.ERR_UNSUPPORTED
+    assert s("fluxbin_decomp_signs", P, 8, 8, 2, None, P, P, None) == fb.ERR_INVALID_ARGUMENT
+    assert s("fluxbin_decomp_residual_signs", P, 8, 8, 2, 3, P, P, P, P, None) == fb.ERR_INVALID_ARGUMENT
+    assert s("fluxbin_decomp_error", P, 8, 8, 2, P, P, P, None, None, P, 1 << 20, None) == fb.ERR_INVALID_ARGUMENT
+    assert s("fluxbin_decompose", P, 8, 8, 2, -1, None, P, P, P, P, P, None, P, 1 << 20, None) == \
+        fb.ERR_INVALID_ARGUMENT
+    assert s("fluxbin_decompose", P, 8, 8, 2, 3, None, P, P, None, P, P, None, P, 1 << 20, None) == \
+        fb.ERR_INVALID_ARGUMENT
+    assert s("fluxbin_decompose", P, 8, 8, 2, 3, None, P, P, P, P, P, None, P, 100, None) == fb.ERR_WORKSPACE
