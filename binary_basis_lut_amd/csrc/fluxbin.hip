@@ -50,7 +50,7 @@ constexpr int kTargetBlocks = 1024;  // about four workgroups per CU
 
 struct Plan {
   int32_t waves;       // waves per workgroup (64 rows each)
-  int32_t nb;          // compiled batch width (power of two >= max_batch)
+  int32_t nb;          // compiled batch width = batch rows per group (see batch_group)
   int32_t cpb;         // chunks per workgroup
   int32_t pf;          // chunks of weights in flight per wave (2 or 8)
   int32_t row_tiles;
@@ -62,6 +62,8 @@ struct Plan {
   int64_t n_pad;
   size_t acc_bytes;    // packed split-reduction words (splits > 1)
 };
+
+constexpr int kMaxBatch = 128;
 
 int32_t pow2_at_least(int64_t v) {
   int32_t p = 1;
@@ -85,10 +87,8 @@ fluxbin_status validate_shape(const fluxbin_layer_desc *d) {
   if (d->ks == 0 && d->s != 0) return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "s = %lld with ks = 0", (long long)d->s);
   if (d->ks > 0 && (d->s < 1 || d->s > d->k))
     return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "s = %lld must be in [1, k] when ks > 0", (long long)d->s);
-  const int64_t maxb = d->g == 4 ? 16 : 4;
-  if (d->max_batch < 1 || d->max_batch > maxb)
-    return fail(FLUXBIN_ERR_UNSUPPORTED, "max_batch = %lld (supported for g = %d: 1..%lld)",
-                (long long)d->max_batch, d->g, (long long)maxb);
+  if (d->max_batch < 1 || d->max_batch > kMaxBatch)
+    return fail(FLUXBIN_ERR_UNSUPPORTED, "max_batch = %lld (supported: 1..%d)", (long long)d->max_batch, kMaxBatch);
   if (d->chunks_per_block < 0 || d->chunks_per_block > kMaxCpb)
     return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "chunks_per_block = %d (0 = automatic, else 1..%d)", d->chunks_per_block,
                 kMaxCpb);
@@ -133,8 +133,16 @@ int32_t auto_cpb(int32_t cmax, int32_t waves, int64_t row_tiles, int32_t total_c
   return (int32_t)std::max<int64_t>(1, std::min<int64_t>(c, cmax));
 }
 
+// Batch rows one workgroup serves (the kernel's compiled width): the next
+// power of two of max_batch, at most 16 (g = 4) or 4 (g = 8); wider batches
+// run as several groups.
+int32_t batch_group(int32_t g, int64_t max_batch) {
+  const int64_t cap = g == 4 ? 16 : 4;
+  return pow2_at_least(max_batch < cap ? max_batch : cap);
+}
+
 fluxbin_status make_plan(const fluxbin_layer_desc *d, Plan *p) {
-  p->nb = pow2_at_least(d->max_batch);
+  p->nb = batch_group(d->g, d->max_batch);
   p->row_tiles = (int32_t)cdiv(d->n, kTileRows);
   p->n_pad = (int64_t)p->row_tiles * kTileRows;
   p->total_chunks = (int32_t)(d->kb * cdiv(d->k, kChunkCols) + d->ks * cdiv(d->s, kChunkCols));
@@ -606,15 +614,20 @@ fluxbin_status fluxbin_gemv(fluxbin_handle h, const uint16_t *x, uint16_t *y, in
   a.row_tiles = p.row_tiles;
   a.row_blocks = p.row_blocks;
   a.splits = p.splits;
-  a.batch = (int32_t)batch;
   a.n_pad = p.n_pad;
-  a.x = x;
-  a.y = y;
-  a.acc = p.splits > 1 ? reinterpret_cast<uint64_t *>(d.workspace) : nullptr;
+  uint64_t *acc = p.splits > 1 ? reinterpret_cast<uint64_t *>(d.workspace) : nullptr;
   const int64_t grid = (int64_t)p.row_blocks * p.splits;
-  hipLaunchKernelGGL(h->fn, dim3((unsigned)grid), dim3(p.waves * 64), h->lds, (hipStream_t)stream, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return hip_fail(e, "gemv launch");
+  // one launch per group of p.nb batch rows (a prefill batch runs as several groups,
+  // each building its own tables and streaming the weights again)
+  for (int64_t b0 = 0; b0 < batch; b0 += p.nb) {
+    a.batch = (int32_t)std::min<int64_t>(p.nb, batch - b0);
+    a.x = x + b0 * d.k;
+    a.y = y + b0 * d.n;
+    a.acc = acc ? acc + b0 * p.n_pad : nullptr;
+    hipLaunchKernelGGL(h->fn, dim3((unsigned)grid), dim3(p.waves * 64), h->lds, (hipStream_t)stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "gemv launch");
+  }
   return ok();
 }
 

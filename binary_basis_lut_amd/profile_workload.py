@@ -16,6 +16,11 @@ profiles/ (each summary names the exact command).  Two modes:
       around fluxbin_decompose; no error trace), time per call and per
       iteration;
 
+  python3 -m binary_basis_lut_amd.profile_workload dense --n 11008 --k 4096 --batch 128 --sets 8 --reps 20
+      the dense fp16 product y = x W^T of the same shape with torch.matmul
+      (the platform GEMM library) over `sets` distinct resident matrices, and,
+      for batch <= 16, the library's own dense fp16 GEMV kernel: time per call;
+
   python3 -m binary_basis_lut_amd.profile_workload copy --bytes 1073741824 --reps 4
       a plain device-to-device copy of known size (torch's copy kernel): the
       reference that scales the FETCH_SIZE / WRITE_SIZE counters to bytes.
@@ -123,6 +128,39 @@ def run_decompose(args) -> None:
           f"weights/s); relative error init {tr[0] / norm:.5f} -> final {tr[-1] / norm:.5f}", flush=True)
 
 
+def run_dense(args) -> None:
+    import torch
+
+    from binary_basis_lut_amd import fluxbin as F
+
+    n, k, b = args.n, args.k, args.batch
+    ws = [torch.randn(n, k, device="cuda").mul_(0.02).half() for _ in range(args.sets)]
+    x = torch.randn(b, k, device="cuda").half()
+    y = torch.empty(b, n, device="cuda", dtype=torch.float16)
+
+    def time_it(fn):
+        for i in range(args.sets):
+            fn(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.reps):
+            for i in range(args.sets):
+                fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / (args.reps * args.sets)
+
+    us_lib = time_it(lambda i: torch.matmul(x, ws[i].t(), out=y))
+    line = (f"dense {k}->{n} batch {b}: torch matmul {us_lib:.3f} us per call "
+            f"({2 * n * k * b / us_lib / 1e6:.1f} TFLOP/s, {2 * n * k / us_lib / 1e3:.0f} GB/s of weights)")
+    if b <= 16:
+        xi, yi = x.view(torch.int16), y.view(torch.int16)
+        us_own = time_it(lambda i: F.fluxbin_dense_gemv_f16(ws[i].view(torch.int16), n, k, xi, yi, b))
+        line += f"; fluxbin_dense_gemv_f16 {us_own:.3f} us per call"
+    print(line, flush=True)
+
+
 def run_copy(args) -> None:
     import torch
 
@@ -156,11 +194,17 @@ def main() -> int:
     dp.add_argument("--kb", type=int, default=2)
     dp.add_argument("--iters", type=int, default=5)
     dp.add_argument("--reps", type=int, default=3)
+    dn = sub.add_parser("dense")
+    dn.add_argument("--n", type=int, default=11008)
+    dn.add_argument("--k", type=int, default=4096)
+    dn.add_argument("--batch", type=int, default=1)
+    dn.add_argument("--sets", type=int, default=8)
+    dn.add_argument("--reps", type=int, default=20)
     c = sub.add_parser("copy")
     c.add_argument("--bytes", type=int, default=1 << 30)
     c.add_argument("--reps", type=int, default=4)
     args = ap.parse_args()
-    {"gemv": run_gemv, "decompose": run_decompose, "copy": run_copy}[args.mode](args)
+    {"gemv": run_gemv, "decompose": run_decompose, "dense": run_dense, "copy": run_copy}[args.mode](args)
     return 0
 
 

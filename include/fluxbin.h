@@ -41,9 +41,10 @@
  *     outputs are left untouched and fluxbin_last_error() holds a
  *     thread-local message.  Device faults surface at the caller's next
  *     synchronisation.  No C++ exception crosses this boundary.
- *   - fluxbin_gemv and fluxbin_build_lut launch exactly one kernel each and
- *     never allocate, copy, set memory or synchronise, so they may be
- *     captured in a HIP graph.  fluxbin_create does synchronise.
+ *   - fluxbin_build_lut launches one kernel and fluxbin_gemv one kernel per
+ *     group of batch rows (16 at g = 4, 4 at g = 8; one launch up to that
+ *     batch); neither ever allocates, copies, sets memory or synchronises, so
+ *     they may be captured in a HIP graph.  fluxbin_create does synchronise.
  */
 #ifndef FLUXBIN_H
 #define FLUXBIN_H
@@ -104,7 +105,9 @@ typedef struct {
   int64_t n;             /* output rows, >= 1 */
   int64_t k;             /* input columns, >= 1 */
   int64_t s;             /* salient columns |S|: 0 when ks == 0, else 1..k */
-  int64_t max_batch;     /* largest batch a call may pass: 1..16 (g = 8: 1..4) */
+  int64_t max_batch;     /* largest batch a call may pass: 1..128.  A workgroup serves up to 16 batch
+                            rows (g = 8: 4); wider batches run as groups of that many rows, each
+                            building its own tables and streaming the weights again */
   const uint32_t *bits_global; /* TILED words, kb blocks of fluxbin_tiled_words(n, k), 16-B aligned */
   const uint16_t *r_global;    /* fp16 row scales: [kb][n], or block-wise (see row_group) */
   const uint16_t *c_global;    /* fp16 [kb][k] column scales */

@@ -87,7 +87,7 @@ def test_too_many_splits_is_unsupported(fb):
 
 @pytest.mark.parametrize("field,value,status", [
     ("abi_version", 1, 1), ("g", 3, 2), ("g", 16, 2), ("kb", 0, 2), ("kb", 5, 2), ("ks", 3, 2), ("ks", -1, 2),
-    ("n", 0, 1), ("k", 0, 1), ("s", 0, 1), ("s", 5000, 1), ("max_batch", 0, 2), ("max_batch", 17, 2),
+    ("n", 0, 1), ("k", 0, 1), ("s", 0, 1), ("s", 5000, 1), ("max_batch", 0, 2), ("max_batch", 129, 2),
     ("chunks_per_block", 33, 1), ("chunks_per_block", -1, 1), ("waves_per_block", 2, 1), ("waves_per_block", 16, 1),
     ("row_group", 64, 2), ("row_group", -1, 2), ("sal_group", 8, 1),
 ])
@@ -99,7 +99,11 @@ def test_workspace_size_rejects(fb, field, value, status):
 
 def test_g8_batch_limit_and_salient_flags(fb):
     assert ws_status(fb, good_desc(fb, g=8, max_batch=4))[0] == fb.OK
-    assert ws_status(fb, good_desc(fb, g=8, max_batch=5))[0] == fb.ERR_UNSUPPORTED
+    assert ws_status(fb, good_desc(fb, g=8, max_batch=128))[0] == fb.OK  # 32 groups of 4 rows
+    assert ws_status(fb, good_desc(fb, g=8, max_batch=129))[0] == fb.ERR_UNSUPPORTED
+    # a prefill batch keeps one reduction word per (batch row, padded output row)
+    st, ws = ws_status(fb, good_desc(fb, max_batch=128))
+    assert st == fb.OK and ws == 128 * 4096 * 8
     assert ws_status(fb, good_desc(fb, ks=0, s=0))[0] == fb.OK
     assert ws_status(fb, good_desc(fb, ks=0, s=8))[0] == fb.ERR_INVALID_ARGUMENT
     assert ws_status(fb, good_desc(fb, chunks_per_block=8, max_batch=8))[0] == fb.ERR_UNSUPPORTED
