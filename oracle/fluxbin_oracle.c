@@ -360,12 +360,60 @@ static inline uint32_t pattern_at(const uint32_t *row_words, int32_t g, int64_t 
  * y is [batch][nrows] like orc_gemv_dense, scales laid out as there.
  * Returns 1 for an unsupported g, 2 when a sub-vector's columns fall in two
  * row-scale groups (the block-wise format then has no per-group sum). */
+/* Quantised tables (LUT Tensor Core notes, section 3.1.3: the precomputed
+ * table entries stored in a lower, uniform precision).  table_fmt 0: exact
+ * fp64 entries (the plain LUT route).  table_fmt 1: fp16 entries taken in
+ * the precision the GPU kernel takes them -- the half-table entry
+ * v_{g-1} + sum_{t<g-1} (+-v_t) summed in fp32 in that order (each v_t =
+ * c_t x_t is exact in fp32), rounded to fp16 (nearest even); the other half
+ * is its negation.  Returns 0 and writes lut (2^g entries). */
+static void quantised_table(int32_t g, const double *v, int32_t table_fmt, double *lut) {
+  int64_t tsize = (int64_t)1 << g, half = tsize / 2;
+  if (table_fmt == 0) {
+    orc_lut_explicit(g, v, lut);
+    return;
+  }
+  for (int64_t q = 0; q < half; ++q) {
+    float t = (float)v[g - 1];
+    for (int32_t i = 0; i < g - 1; ++i) {
+      float vi = (float)v[i];
+      t = ((q >> i) & 1) ? t + vi : t - vi;
+    }
+    double h = orc_half_to_double(orc_double_to_half((double)t));
+    lut[q | half] = h;
+    lut[(half - 1) ^ q] = -h;
+  }
+}
+
+ORC_EXPORT int orc_gemv_lut_tables(int64_t n, int64_t k, int64_t s, int32_t kb, int32_t ks, int64_t row_group,
+                                   int32_t g, int32_t table_fmt, const uint32_t *bits_g, const uint16_t *r_g,
+                                   const uint16_t *c_g, const uint32_t *bits_s, const uint16_t *r_s,
+                                   const uint16_t *c_s, const int32_t *idx, const uint16_t *x, int64_t batch,
+                                   const int64_t *rows, int64_t nrows, double *y);
+
+/* The full 2^g table of one sub-vector in format table_fmt (exported for the pins). */
+ORC_EXPORT void orc_quantised_table(int32_t g, const double *v, int32_t table_fmt, double *lut) {
+  quantised_table(g, v, table_fmt, lut);
+}
+
 ORC_EXPORT int orc_gemv_lut(int64_t n, int64_t k, int64_t s, int32_t kb, int32_t ks, int64_t row_group, int32_t g,
                             const uint32_t *bits_g, const uint16_t *r_g, const uint16_t *c_g,
                             const uint32_t *bits_s, const uint16_t *r_s, const uint16_t *c_s,
                             const int32_t *idx, const uint16_t *x, int64_t batch,
                             const int64_t *rows, int64_t nrows, double *y) {
+  return orc_gemv_lut_tables(n, k, s, kb, ks, row_group, g, 0, bits_g, r_g, c_g, bits_s, r_s, c_s, idx, x, batch,
+                             rows, nrows, y);
+}
+
+/* The LUT route with tables in format table_fmt (see quantised_table); y as
+ * orc_gemv_lut.  Returns 1 for an unsupported g or format. */
+ORC_EXPORT int orc_gemv_lut_tables(int64_t n, int64_t k, int64_t s, int32_t kb, int32_t ks, int64_t row_group,
+                                   int32_t g, int32_t table_fmt, const uint32_t *bits_g, const uint16_t *r_g,
+                                   const uint16_t *c_g, const uint32_t *bits_s, const uint16_t *r_s,
+                                   const uint16_t *c_s, const int32_t *idx, const uint16_t *x, int64_t batch,
+                                   const int64_t *rows, int64_t nrows, double *y) {
   if (g <= 0 || g > 16 || 32 % g) return 1;
+  if (table_fmt != 0 && table_fmt != 1) return 1;
   if (row_group < 0) return 2;
   const int64_t ng = group_count(row_group, k);
   int err = 0;
@@ -401,7 +449,7 @@ ORC_EXPORT int orc_gemv_lut(int64_t n, int64_t k, int64_t s, int32_t kb, int32_t
       const double *xb = xd + b * k;
       for (int64_t j = 0; j < nsub; ++j) {
         fused_inputs(g, j, len, c, xb, salient ? idx : NULL, v);
-        orc_lut_explicit(g, v, tables + j * tsize);
+        quantised_table(g, v, table_fmt, tables + j * tsize);
       }
       for (int64_t t = 0; t < nrows; ++t) {
         int64_t i = rows ? rows[t] : t;

@@ -69,6 +69,9 @@ def _declare(L):
     L.orc_gemv_dense.argtypes = [I64, I64, I64, I32, I32, I64, P, P, P, P, P, P, P, P, I64, P, I64, P, P, I32]
     L.orc_gemv_lut.restype = ctypes.c_int
     L.orc_gemv_lut.argtypes = [I64, I64, I64, I32, I32, I64, I32, P, P, P, P, P, P, P, P, I64, P, I64, P]
+    L.orc_gemv_lut_tables.restype = ctypes.c_int
+    L.orc_gemv_lut_tables.argtypes = [I64, I64, I64, I32, I32, I64, I32, I32, P, P, P, P, P, P, P, P, I64, P, I64, P]
+    L.orc_quantised_table.argtypes = [I32, P, I32, P]
     L.orc_tiled_scale_elems.restype = I64
     L.orc_tiled_scale_elems.argtypes = [I64, I64, I64]
     L.orc_tile_scales.argtypes = [P, I64, I64, I64, P]
@@ -215,6 +218,28 @@ def gemv_lut(layer, x, g: int | None = None, rows=None):
     if err:
         raise ValueError("unsupported g" if err == 1 else "a sub-vector spans two row-scale groups")
     return y
+
+
+def gemv_lut_fp16_tables(layer, x, rows=None):
+    """fp64 LUT route with fp16 table entries built in fp32 as the kernel builds them (quantised tables)."""
+    x = _c(x, np.uint16)
+    batch = x.shape[0]
+    arrs = _layer_arrays(layer)
+    rows_a = None if rows is None else _c(rows, np.int64)
+    nrows = layer.n if rows is None else rows_a.size
+    y = np.empty((batch, nrows), np.float64)
+    err = lib().orc_gemv_lut_tables(layer.n, layer.k, layer.s, layer.kb, layer.ks, _row_group(layer), layer.g, 1,
+                                    *[_p(a) for a in arrs], _p(x), batch, _p(rows_a), nrows, _p(y))
+    if err:
+        raise ValueError("unsupported g or a sub-vector spans two row-scale groups")
+    return y
+
+
+def quantised_table(g: int, v, table_fmt: int = 1) -> np.ndarray:
+    v = _c(v, np.float64)
+    out = np.empty(1 << g, np.float64)
+    lib().orc_quantised_table(g, _p(v), table_fmt, _p(out))
+    return out
 
 
 def lut_explicit(g: int, v) -> np.ndarray:

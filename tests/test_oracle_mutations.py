@@ -16,6 +16,7 @@ import pytest
 from binary_basis_lut_amd import inputs as I
 
 from . import test_oracle_decomp as D
+from . import test_oracle_tables as T
 from .test_oracle_grouped import exact_y_grouped
 from .test_oracle_pins import bits_of, exact_y, f16, layer_from
 
@@ -61,6 +62,10 @@ MUTANTS = {
                                      "for (int32_t b = 0; b + 1 < kb; ++b) {\n          double p"),
     "decomp_weights_ignored": ("num += (d ? d[j] : 1.0) * res * sign_at(row, j) * cb[j];",
                                "num += res * sign_at(row, j) * cb[j];"),
+    "table_fp16_rounding_skipped": ("double h = orc_half_to_double(orc_double_to_half((double)t));",
+                                    "double h = (double)t;"),
+    "table_summed_in_fp64": ("float t = (float)v[g - 1];", "double t = v[g - 1];"),
+    "table_negated_half_misplaced": ("lut[(half - 1) ^ q] = -h;", "lut[q] = -h;"),
 }
 
 
@@ -187,8 +192,22 @@ def chk_decomp_steps(O):
     return bool(np.all(np.diff(t[:-1]) <= 1e-12 * t[0]))
 
 
+def chk_fp16_tables(O):
+    """Quantised (fp16) tables equal numpy's float32 sums cast to float16, with the negated half in place."""
+    rng = I.stream(100, 8)
+    for g in (4, 8):
+        for _ in range(20):
+            c = np.abs(rng.normal(0, 0.02, g)) + 1e-3
+            x = rng.normal(0, 1, g) * rng.choice([1.0, 20.0], g)
+            v = c.astype(np.float16).astype(np.float64) * x.astype(np.float16).astype(np.float64)
+            if not np.array_equal(O.quantised_table(g, v, 1), T.numpy_table(g, v)):
+                return False
+    v = T.crafted_double_rounding_case()
+    return bool(np.array_equal(O.quantised_table(4, v, 1), T.numpy_table(4, v)))
+
+
 CHECKS = [chk_popcount, chk_one_hot, chk_bruteforce, chk_half_numpy, chk_grouped_one_hot, chk_grouped_bruteforce,
-          chk_decomp_steps]
+          chk_decomp_steps, chk_fp16_tables]
 
 
 def test_unmutated_oracle_passes_every_check(orc):
