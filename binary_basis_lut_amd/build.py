@@ -15,7 +15,8 @@ from pathlib import Path
 PKG = Path(__file__).resolve().parent
 ROOT = PKG.parent
 CSRC = PKG / "csrc"
-SOURCES = [CSRC / "fluxbin.hip"] + [CSRC / f"gemv_g{g}_rs{rs}.hip" for g in (4, 8) for rs in (0, 1)]
+SOURCES = [CSRC / "fluxbin.hip"] + [CSRC / f"gemv_g{g}_rs{rs}_t{t}.hip" for g in (4, 8) for rs in (0, 1)
+                                   for t in (32, 16)]
 HEADERS = [CSRC / "common.hpp", CSRC / "gemv_kernel.hpp", CSRC / "aux_kernels.hpp", CSRC / "decomp_kernels.hpp",
            ROOT / "include" / "fluxbin.h"]
 DEPS = SOURCES + HEADERS

@@ -212,13 +212,18 @@ struct GemvArgs {
 
 typedef void (*gemv_fn)(const GemvArgs);
 
-// GEMV kernel instances, one translation unit per table width g and
-// row-scale format (rs 0: per row, 1: block-wise): the instance for batch
-// width nb, waves per workgroup and prefetch depth pf, or nullptr.
-gemv_fn gemv_pick_g4_rs0(int nb, int waves, int pf);
-gemv_fn gemv_pick_g4_rs1(int nb, int waves, int pf);
-gemv_fn gemv_pick_g8_rs0(int nb, int waves, int pf);
-gemv_fn gemv_pick_g8_rs1(int nb, int waves, int pf);
+// GEMV kernel instances, one translation unit per table width g, row-scale
+// format (rs 0: per row, 1: block-wise) and table entry type (t32: fp32,
+// t16: fp16): the instance for batch width nb, waves per workgroup and
+// prefetch depth pf, or nullptr.
+gemv_fn gemv_pick_g4_rs0_t32(int nb, int waves, int pf);
+gemv_fn gemv_pick_g4_rs1_t32(int nb, int waves, int pf);
+gemv_fn gemv_pick_g8_rs0_t32(int nb, int waves, int pf);
+gemv_fn gemv_pick_g8_rs1_t32(int nb, int waves, int pf);
+gemv_fn gemv_pick_g4_rs0_t16(int nb, int waves, int pf);
+gemv_fn gemv_pick_g4_rs1_t16(int nb, int waves, int pf);
+gemv_fn gemv_pick_g8_rs0_t16(int nb, int waves, int pf);
+gemv_fn gemv_pick_g8_rs1_t16(int nb, int waves, int pf);
 
 __device__ __forceinline__ float h2f(uint16_t h) { return __half2float(__ushort_as_half(h)); }
 __device__ __forceinline__ uint16_t f2h(float f) { return __half_as_ushort(__float2half_rn(f)); }
@@ -263,46 +268,96 @@ __device__ __forceinline__ uint32_t addr_of(uint32_t v, uint32_t base) {
   return __builtin_amdgcn_perm(base, v, 0x0c060500u | kk);
 }
 
+// fp16 at LDS byte address `addr` (raw bits, zero-extended).
+__device__ __forceinline__ uint32_t lds_u16(uint32_t addr) {
+  return *reinterpret_cast<const FB_LDS uint16_t *>((uintptr_t)addr);
+}
+
+// acc + (the fp16 value in the low half of h), one rounding: v_fma_mix_f32
+// computes acc + h * 1.0 with h read as fp16, the same single instruction and
+// rounding as a fp32 add of the converted value.
+__device__ __forceinline__ float add_f16_bits(float acc, uint32_t h) {
+  float r;
+  asm("v_fma_mix_f32 %0, %1, 1.0, %2 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(h), "v"(acc));
+  return r;
+}
+
+// Table entries of EB bytes: 4 = fp32, 2 = fp16 (quantised tables).
+template <int EB>
+__device__ __forceinline__ float add_entry(float acc, uint32_t addr) {
+  if constexpr (EB == 4) {
+    return acc + lds_f32(addr);
+  } else {
+    return add_f16_bits(acc, lds_u16(addr));
+  }
+}
+
+template <int EB>
+__device__ __forceinline__ float entry_value(uint32_t addr) {
+  if constexpr (EB == 4) {
+    return lds_f32(addr);
+  } else {
+    return add_f16_bits(0.0f, lds_u16(addr));  // exact conversion
+  }
+}
+
+// Byte offsets (pattern * EB) of the 4-bit patterns of a word: A holds
+// nibbles 0, 2, 4, 6 and B nibbles 1, 3, 5, 7, one per byte.
+template <int EB>
+__device__ __forceinline__ uint32_t nibbles_even(uint32_t w) {
+  return EB == 4 ? (w << 2) & 0x3c3c3c3cu : (w << 1) & 0x1e1e1e1eu;
+}
+template <int EB>
+__device__ __forceinline__ uint32_t nibbles_odd(uint32_t w) {
+  return EB == 4 ? (w >> 2) & 0x3c3c3c3cu : (w >> 3) & 0x1e1e1e1eu;
+}
+// Byte offset (pattern * EB) of byte kk of a word (an 8-bit pattern).
+template <int EB, int kk>
+__device__ __forceinline__ uint32_t byte_pattern(uint32_t w) {
+  constexpr int SH = EB == 4 ? 2 : 1;
+  if constexpr (kk == 0) {
+    return (w << SH) & (0xffu << SH);
+  } else {
+    return (w >> (8 * kk - SH)) & (0xffu << SH);
+  }
+}
+
 // Accumulate the lookups of one 32-bit word (32 columns) of one row.  `base`
-// is the LDS byte address of the chunk's table block (a multiple of 256
-// below 2^24); j0 is the first sub-vector of the word.  Sub-vector j of batch
-// row b has its TAB-entry table at base + ((b * SUB + j) * TAB) * 4.
-template <int G, int NB>
+// is the LDS byte address of the chunk's table block (a multiple of 256, or of
+// 512 for 256-entry tables, below 2^24); j0 is the first sub-vector of the
+// word.  Sub-vector j of batch row b has its TAB-entry table at
+// base + ((b * SUB + j) * TAB) * EB.
+template <int G, int NB, int EB>
 __device__ __forceinline__ void lookup_word(uint32_t w, uint32_t base, float (&acc)[NB], int j0) {
   constexpr int SUB = kChunkCols / G;
   constexpr int TAB = 1 << G;
   if constexpr (G == 4) {
-    // nibble m of w at bits [4m, 4m+4); A holds nibbles 0,2,4,6 and B nibbles
-    // 1,3,5,7, each as a byte offset (index * 4) into a 16-entry fp32 table.
-    const uint32_t A = (w << 2) & 0x3c3c3c3cu;
-    const uint32_t B = (w >> 2) & 0x3c3c3c3cu;
+    const uint32_t A = nibbles_even<EB>(w);
+    const uint32_t B = nibbles_odd<EB>(w);
     const uint32_t ia[4] = {addr_of<0>(A, base), addr_of<1>(A, base), addr_of<2>(A, base), addr_of<3>(A, base)};
     const uint32_t ib[4] = {addr_of<0>(B, base), addr_of<1>(B, base), addr_of<2>(B, base), addr_of<3>(B, base)};
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
-        const int off0 = ((b * SUB + j0 + 2 * kk) * TAB) * 4;
-        acc[b] += lds_f32(ia[kk] + off0);
-        acc[b] += lds_f32(ib[kk] + off0 + TAB * 4);
+        const int off0 = ((b * SUB + j0 + 2 * kk) * TAB) * EB;
+        acc[b] = add_entry<EB>(acc[b], ia[kk] + off0);
+        acc[b] = add_entry<EB>(acc[b], ib[kk] + off0 + TAB * EB);
       }
       // wide batches: at most 2 * NB table reads in flight per step, or the
       // scheduler hoists all of them and runs out of registers
       if constexpr (NB >= 8) asm volatile("" ::: "memory");
     }
   } else {
-    // byte kk of w is the 8-bit pattern of sub-vector j0 + kk; table offset = pattern * 4
-    uint32_t ix[4];
-    ix[0] = ((w << 2) & 0x3fcu) | base;
-    ix[1] = ((w >> 6) & 0x3fcu) | base;
-    ix[2] = ((w >> 14) & 0x3fcu) | base;
-    ix[3] = ((w >> 22) & 0x3fcu) | base;
+    // byte kk of w is the 8-bit pattern of sub-vector j0 + kk
+    const uint32_t ix[4] = {byte_pattern<EB, 0>(w) | base, byte_pattern<EB, 1>(w) | base,
+                            byte_pattern<EB, 2>(w) | base, byte_pattern<EB, 3>(w) | base};
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
-        const int off0 = ((b * SUB + j0 + kk) * TAB) * 4;
-        acc[b] += lds_f32(ix[kk] + off0);
+        const int off0 = ((b * SUB + j0 + kk) * TAB) * EB;
+        acc[b] = add_entry<EB>(acc[b], ix[kk] + off0);
       }
       if constexpr (NB >= 8) asm volatile("" ::: "memory");
     }
@@ -312,39 +367,36 @@ __device__ __forceinline__ void lookup_word(uint32_t w, uint32_t base, float (&a
 // Block-wise variant: the lookups of each byte of w (8 columns: two
 // sub-vectors at g = 4, one at g = 8) are summed and added into `part`
 // scaled by that byte's row scale s0..s3.
-template <int G, int NB>
+template <int G, int NB, int EB>
 __device__ __forceinline__ void lookup_word_scaled(uint32_t w, uint32_t base, float (&part)[NB], int j0, float s0,
                                                    float s1, float s2, float s3) {
   constexpr int SUB = kChunkCols / G;
   constexpr int TAB = 1 << G;
   const float sc[4] = {s0, s1, s2, s3};
   if constexpr (G == 4) {
-    const uint32_t A = (w << 2) & 0x3c3c3c3cu;  // nibbles 0, 2, 4, 6 as byte offsets
-    const uint32_t B = (w >> 2) & 0x3c3c3c3cu;  // nibbles 1, 3, 5, 7
+    const uint32_t A = nibbles_even<EB>(w);
+    const uint32_t B = nibbles_odd<EB>(w);
     const uint32_t ia[4] = {addr_of<0>(A, base), addr_of<1>(A, base), addr_of<2>(A, base), addr_of<3>(A, base)};
     const uint32_t ib[4] = {addr_of<0>(B, base), addr_of<1>(B, base), addr_of<2>(B, base), addr_of<3>(B, base)};
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
-        const int off0 = ((b * SUB + j0 + 2 * kk) * TAB) * 4;
-        const float t = lds_f32(ia[kk] + off0) + lds_f32(ib[kk] + off0 + TAB * 4);
+        const int off0 = ((b * SUB + j0 + 2 * kk) * TAB) * EB;
+        const float t = add_entry<EB>(entry_value<EB>(ia[kk] + off0), ib[kk] + off0 + TAB * EB);
         part[b] = fmaf(sc[kk], t, part[b]);
       }
       if constexpr (NB >= 8) asm volatile("" ::: "memory");
     }
   } else {
-    uint32_t ix[4];
-    ix[0] = ((w << 2) & 0x3fcu) | base;
-    ix[1] = ((w >> 6) & 0x3fcu) | base;
-    ix[2] = ((w >> 14) & 0x3fcu) | base;
-    ix[3] = ((w >> 22) & 0x3fcu) | base;
+    const uint32_t ix[4] = {byte_pattern<EB, 0>(w) | base, byte_pattern<EB, 1>(w) | base,
+                            byte_pattern<EB, 2>(w) | base, byte_pattern<EB, 3>(w) | base};
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
-        const int off0 = ((b * SUB + j0 + kk) * TAB) * 4;
-        part[b] = fmaf(sc[kk], lds_f32(ix[kk] + off0), part[b]);
+        const int off0 = ((b * SUB + j0 + kk) * TAB) * EB;
+        part[b] = fmaf(sc[kk], entry_value<EB>(ix[kk] + off0), part[b]);
       }
       if constexpr (NB >= 8) asm volatile("" ::: "memory");
     }
@@ -360,30 +412,35 @@ __device__ __forceinline__ void next_chunk(const ULayer &L, int &sg, int &cis, b
   sg = step ? sg + (int)wrap : sg;
 }
 
-// Dynamic LDS of the GEMV kernel: [cpb][NB][SUB][TAB] fp32 tables, then
-// [cpb][NB][128] fp32 scale-fused inputs, then a 64-float sink for the
-// stores of unused input slots.
+// Dynamic LDS of the GEMV kernel: [cpb][NB][SUB][TAB] tables of eb-byte
+// entries (fp32, or fp16 when quantised), then [cpb][NB][128] fp32
+// scale-fused inputs, then a 64-float sink for the stores of unused input
+// slots.
 constexpr int kLdsBudget = 80 * 1024;  // per workgroup: two workgroups per CU
 constexpr int kMaxCpb = 32;            // chunks per workgroup
 constexpr int kLdsSink = 64 * 4;
 
-__host__ __device__ constexpr int lds_per_chunk(int g, int nb) {
-  return nb * (kChunkCols / g) * (1 << g) * 4 + nb * kChunkCols * 4;
+__host__ __device__ constexpr int lds_per_chunk(int g, int nb, int eb) {
+  return nb * (kChunkCols / g) * (1 << g) * eb + nb * kChunkCols * 4;
 }
 
-__host__ __device__ constexpr int lds_bytes(int g, int nb, int cpb) { return cpb * lds_per_chunk(g, nb) + kLdsSink; }
+__host__ __device__ constexpr int lds_bytes(int g, int nb, int cpb, int eb) {
+  return cpb * lds_per_chunk(g, nb, eb) + kLdsSink;
+}
 
 constexpr int kMaxItems = 8;  // table-build inputs per thread (registers)
 
 __host__ __device__ constexpr int cmin(int a, int b) { return a < b ? a : b; }
 
-// Most chunks one workgroup may take for table width g, batch width nb and
-// `waves` waves: its tables must fit the LDS budget, and its table-build
-// inputs (nb * 128 per chunk) at most kMaxItems per thread.
-__host__ __device__ constexpr int cpb_cap(int g, int nb, int waves) {
-  return cmin(cmin(kMaxCpb, (kLdsBudget - kLdsSink) / lds_per_chunk(g, nb)), kMaxItems * waves * 64 / (nb * kChunkCols)) < 1
+// Most chunks one workgroup may take for table width g, batch width nb,
+// `waves` waves and eb-byte entries: its tables must fit the LDS budget, and
+// its table-build inputs (nb * 128 per chunk) at most kMaxItems per thread.
+__host__ __device__ constexpr int cpb_cap(int g, int nb, int waves, int eb) {
+  return cmin(cmin(kMaxCpb, (kLdsBudget - kLdsSink) / lds_per_chunk(g, nb, eb)),
+              kMaxItems * waves * 64 / (nb * kChunkCols)) < 1
              ? 1
-             : cmin(cmin(kMaxCpb, (kLdsBudget - kLdsSink) / lds_per_chunk(g, nb)), kMaxItems * waves * 64 / (nb * kChunkCols));
+             : cmin(cmin(kMaxCpb, (kLdsBudget - kLdsSink) / lds_per_chunk(g, nb, eb)),
+                    kMaxItems * waves * 64 / (nb * kChunkCols));
 }
 
 // Prefetch depth for a workgroup range of cpb chunks: the deepest of 8, 4, 2

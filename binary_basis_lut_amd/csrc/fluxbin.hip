@@ -2,7 +2,7 @@
 //
 // Host side: argument validation (pure host work, before any HIP call),
 // work planning, kernel launches.  The GEMV kernel instances live in the
-// gemv_g*_rs*.hip translation units (gemv_kernel.hpp), the other kernels in
+// gemv_g*_rs*_t*.hip translation units (gemv_kernel.hpp), the other kernels in
 // aux_kernels.hpp.
 #include "fluxbin.h"
 
@@ -94,6 +94,8 @@ fluxbin_status validate_shape(const fluxbin_layer_desc *d) {
                 kMaxCpb);
   if (d->waves_per_block != 0 && d->waves_per_block != 4 && d->waves_per_block != 8)
     return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "waves_per_block = %d (0, 4 or 8)", d->waves_per_block);
+  if (d->table_precision != FLUXBIN_TABLE_F32 && d->table_precision != FLUXBIN_TABLE_F16)
+    return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "table_precision = %d (0 = fp32, 1 = fp16)", d->table_precision);
   if (d->row_group != 0 && d->row_group != kChunkCols)
     return fail(FLUXBIN_ERR_UNSUPPORTED, "row_group = %d (supported: 0 = per row, 128 = block-wise)", d->row_group);
   if (d->row_group == 0 || d->ks == 0) {
@@ -141,6 +143,8 @@ int32_t batch_group(int32_t g, int64_t max_batch) {
   return pow2_at_least(max_batch < cap ? max_batch : cap);
 }
 
+int entry_bytes(const fluxbin_layer_desc *d) { return d->table_precision == FLUXBIN_TABLE_F16 ? 2 : 4; }
+
 fluxbin_status make_plan(const fluxbin_layer_desc *d, Plan *p) {
   p->nb = batch_group(d->g, d->max_batch);
   p->row_tiles = (int32_t)cdiv(d->n, kTileRows);
@@ -153,7 +157,7 @@ fluxbin_status make_plan(const fluxbin_layer_desc *d, Plan *p) {
     // the large g = 8 tables, and for very tall layers (measured on MI355X)
     p->waves = (d->g == 8 || p->row_tiles >= 512) ? 8 : 4;
   }
-  const int32_t cmax = cpb_cap(d->g, p->nb, p->waves);
+  const int32_t cmax = cpb_cap(d->g, p->nb, p->waves, entry_bytes(d));
   if (d->chunks_per_block > cmax)
     return fail(FLUXBIN_ERR_UNSUPPORTED, "chunks_per_block = %d exceeds %d for g = %d, max_batch = %lld, %d waves",
                 d->chunks_per_block, cmax, d->g, (long long)d->max_batch, p->waves);
@@ -196,9 +200,11 @@ __device__ int32_t g_zero_index[4];
 // ---------------------------------------------------------------------------
 namespace {
 
-gemv_fn pick_gemv(int g, int rs, int nb, int waves, int pf) {
-  if (g == 4) return rs ? gemv_pick_g4_rs1(nb, waves, pf) : gemv_pick_g4_rs0(nb, waves, pf);
-  if (g == 8) return rs ? gemv_pick_g8_rs1(nb, waves, pf) : gemv_pick_g8_rs0(nb, waves, pf);
+gemv_fn pick_gemv(int g, int rs, int tq, int nb, int waves, int pf) {
+  if (g == 4 && tq == 0) return rs ? gemv_pick_g4_rs1_t32(nb, waves, pf) : gemv_pick_g4_rs0_t32(nb, waves, pf);
+  if (g == 8 && tq == 0) return rs ? gemv_pick_g8_rs1_t32(nb, waves, pf) : gemv_pick_g8_rs0_t32(nb, waves, pf);
+  if (g == 4 && tq == 1) return rs ? gemv_pick_g4_rs1_t16(nb, waves, pf) : gemv_pick_g4_rs0_t16(nb, waves, pf);
+  if (g == 8 && tq == 1) return rs ? gemv_pick_g8_rs1_t16(nb, waves, pf) : gemv_pick_g8_rs0_t16(nb, waves, pf);
   return nullptr;
 }
 
@@ -509,9 +515,9 @@ fluxbin_status fluxbin_create(const fluxbin_layer_desc *d, fluxbin_handle *out) 
     e = hipDeviceSynchronize();
     if (e != hipSuccess) return hip_fail(e, "synchronising after create");
   }
-  gemv_fn fn = pick_gemv(d->g, d->row_group ? 1 : 0, p.nb, p.waves, p.pf);
+  gemv_fn fn = pick_gemv(d->g, d->row_group ? 1 : 0, d->table_precision, p.nb, p.waves, p.pf);
   if (!fn) return fail(FLUXBIN_ERR_UNSUPPORTED, "no kernel for g = %d, batch width %d, %d waves", d->g, p.nb, p.waves);
-  const size_t lds = (size_t)lds_bytes(d->g, p.nb, p.cpb);
+  const size_t lds = (size_t)lds_bytes(d->g, p.nb, p.cpb, entry_bytes(d));
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)lds);
   if (e != hipSuccess) return hip_fail(e, "setting the kernel's dynamic LDS size");
@@ -549,7 +555,7 @@ fluxbin_status fluxbin_get_plan(fluxbin_handle h, fluxbin_plan *plan) {
   plan->row_blocks = p.row_blocks;
   plan->splits = p.splits;
   plan->total_chunks = p.total_chunks;
-  plan->lds_bytes = lds_bytes(h->d.g, p.nb, p.cpb);
+  plan->lds_bytes = lds_bytes(h->d.g, p.nb, p.cpb, entry_bytes(&h->d));
   plan->grid = (int64_t)p.row_blocks * p.splits;
   return ok();
 }

@@ -1,0 +1,9 @@
+// gemv_g4_rs0_t32.hip -- LUT GEMV kernel instances for g = 4, per-row row scales,
+// fp32 table entries.
+#include "gemv_kernel.hpp"
+
+namespace fluxbin {
+
+gemv_fn gemv_pick_g4_rs0_t32(int nb, int waves, int pf) { return gemv_pick<4, 0, 0>(nb, waves, pf); }
+
+}  // namespace fluxbin

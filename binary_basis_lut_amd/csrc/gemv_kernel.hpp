@@ -14,15 +14,21 @@ namespace fluxbin {
 // chunk is one group, scaled once its lookups are summed; a salient chunk
 // holds 16 groups of 8 or 8 groups of 16 compact columns, each sum of 8
 // columns (one byte of a sign word) is scaled as it is formed.
-template <int G, int NB, int WAVES, int PF, int RS>
+//
+// TQ selects the table entries: 0 = fp32; 1 = fp16 (quantised tables, LUT
+// Tensor Core notes, section 3.1.3): each entry is summed in fp32 as before
+// and rounded to fp16 once, halving the tables' LDS; lookups add the fp16
+// entry into the fp32 accumulator with one v_fma_mix_f32.
+template <int G, int NB, int WAVES, int PF, int RS, int TQ>
 __global__ __launch_bounds__(WAVES * 64) void lut_gemv_kernel(const GemvArgs a) {
   constexpr int NT = WAVES * 64;
   constexpr int SUB = kChunkCols / G;      // sub-vectors per chunk
   constexpr int TAB = 1 << G;              // full table entries
   constexpr int HALF = TAB / 2;
   constexpr int WPL = kChunkCols / 32;     // words per lane per chunk (4)
-  constexpr int CTB = NB * SUB * TAB * 4;  // table bytes of one chunk (all batch rows)
-  static_assert(CTB % 256 == 0, "chunk table blocks must be 256-byte aligned");
+  constexpr int EB = TQ ? 2 : 4;           // bytes per table entry
+  constexpr int CTB = NB * SUB * TAB * EB; // table bytes of one chunk (all batch rows)
+  static_assert(CTB % 256 == 0 && (G == 4 || CTB % 512 == 0), "chunk table blocks must stay aligned");
   static_assert(NT % HALF == 0, "thread count must be a multiple of the half-table size");
   static_assert(PF >= 1 && PF <= 8, "prefetch depth");
   extern __shared__ __align__(1024) float smem[];
@@ -124,7 +130,7 @@ __global__ __launch_bounds__(WAVES * 64) void lut_gemv_kernel(const GemvArgs a) 
     // handled by thread e % NT; a wave's 64 items share chunk and batch row.
     // Every item slot loads (items past the range re-read the last chunk's
     // inputs and are dropped).
-    constexpr int CMAX = cpb_for_depth(PF, cpb_cap(G, NB, WAVES));  // chunks, at most
+    constexpr int CMAX = cpb_for_depth(PF, cpb_cap(G, NB, WAVES, EB));  // chunks, at most
     constexpr int VPT = (CMAX * NB * kChunkCols + NT - 1) / NT;  // items per thread, at most
     static_assert(VPT <= kMaxItems, "table-build inputs per thread");
     static_assert(kChunkCols % 64 == 0 && NT % 64 == 0, "a wave's items must share chunk and batch row");
@@ -210,9 +216,16 @@ __global__ __launch_bounds__(WAVES * 64) void lut_gemv_kernel(const GemvArgs a) 
         float t = v[G - 1];
 #pragma unroll
         for (int i = 0; i < G - 1; ++i) t = fmaf(sgn[i], v[i], t);
-        float *tb = &s_tab[(cb * SUB + j) * TAB];
-        tb[q | HALF] = t;
-        tb[(HALF - 1) ^ q] = -t;
+        if constexpr (TQ == 0) {
+          float *tb = &s_tab[(cb * SUB + j) * TAB];
+          tb[q | HALF] = t;
+          tb[(HALF - 1) ^ q] = -t;
+        } else {
+          uint16_t *tb = reinterpret_cast<uint16_t *>(s_tab) + (cb * SUB + j) * TAB;
+          const uint16_t h = f2h(t);  // nearest even; the negation is exact
+          tb[q | HALF] = h;
+          tb[(HALF - 1) ^ q] = h ^ 0x8000u;
+        }
       }
     }
     __syncthreads();
@@ -248,14 +261,14 @@ __global__ __launch_bounds__(WAVES * 64) void lut_gemv_kernel(const GemvArgs a) 
         }
 #pragma unroll
         for (int q = 0; q < WPL; ++q) {
-          lookup_word_scaled<G, NB>(w[q], base, part, q * (32 / G), sc[4 * q], sc[4 * q + 1], sc[4 * q + 2],
+          lookup_word_scaled<G, NB, EB>(w[q], base, part, q * (32 / G), sc[4 * q], sc[4 * q + 1], sc[4 * q + 2],
                                     sc[4 * q + 3]);
           if constexpr (NB >= 4) asm volatile("" ::: "memory");
         }
       } else {
 #pragma unroll
         for (int q = 0; q < WPL; ++q) {
-          lookup_word<G, NB>(w[q], base, acc, q * (32 / G));
+          lookup_word<G, NB, EB>(w[q], base, acc, q * (32 / G));
           // wider batches: one word's table reads at a time
           if constexpr (NB >= 4) asm volatile("" ::: "memory");
         }
@@ -353,32 +366,32 @@ __global__ __launch_bounds__(WAVES * 64) void lut_gemv_kernel(const GemvArgs a) 
   }
 }
 
-// Instance for (batch width, waves, prefetch depth) at table width G and
-// row-scale format RS, or nullptr.
-template <int G, int NB, int W, int RS>
+// Instance for (batch width, waves, prefetch depth) at table width G,
+// row-scale format RS and table entry type TQ, or nullptr.
+template <int G, int NB, int W, int RS, int TQ>
 gemv_fn gemv_pick_pf(int pf) {
-  return pf == 8 ? lut_gemv_kernel<G, NB, W, 8, RS>
-         : pf == 4 ? lut_gemv_kernel<G, NB, W, 4, RS>
-         : pf == 2 ? lut_gemv_kernel<G, NB, W, 2, RS>
+  return pf == 8 ? lut_gemv_kernel<G, NB, W, 8, RS, TQ>
+         : pf == 4 ? lut_gemv_kernel<G, NB, W, 4, RS, TQ>
+         : pf == 2 ? lut_gemv_kernel<G, NB, W, 2, RS, TQ>
                    : nullptr;
 }
 
-template <int G, int NB, int RS>
+template <int G, int NB, int RS, int TQ>
 gemv_fn gemv_pick_waves(int waves, int pf) {
-  return waves == 8 ? gemv_pick_pf<G, NB, 8, RS>(pf) : waves == 4 ? gemv_pick_pf<G, NB, 4, RS>(pf) : nullptr;
+  return waves == 8 ? gemv_pick_pf<G, NB, 8, RS, TQ>(pf) : waves == 4 ? gemv_pick_pf<G, NB, 4, RS, TQ>(pf) : nullptr;
 }
 
-template <int G, int RS>
+template <int G, int RS, int TQ>
 gemv_fn gemv_pick(int nb, int waves, int pf) {
   switch (nb) {
-    case 1: return gemv_pick_waves<G, 1, RS>(waves, pf);
-    case 2: return gemv_pick_waves<G, 2, RS>(waves, pf);
-    case 4: return gemv_pick_waves<G, 4, RS>(waves, pf);
+    case 1: return gemv_pick_waves<G, 1, RS, TQ>(waves, pf);
+    case 2: return gemv_pick_waves<G, 2, RS, TQ>(waves, pf);
+    case 4: return gemv_pick_waves<G, 4, RS, TQ>(waves, pf);
   }
   if constexpr (G == 4) {
     switch (nb) {
-      case 8: return gemv_pick_waves<G, 8, RS>(waves, pf);
-      case 16: return gemv_pick_waves<G, 16, RS>(waves, pf);
+      case 8: return gemv_pick_waves<G, 8, RS, TQ>(waves, pf);
+      case 16: return gemv_pick_waves<G, 16, RS, TQ>(waves, pf);
     }
   }
   return nullptr;

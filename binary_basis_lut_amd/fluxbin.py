@@ -20,10 +20,11 @@ if not LIB_PATH.exists():
 
 _lib = ctypes.CDLL(str(LIB_PATH))
 
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
 LAYOUT_ROWMAJOR, LAYOUT_TILED = 0, 1
+TABLE_F32, TABLE_F16 = 0, 1
 DT_I8, DT_F16, DT_BITS = 0, 1, 2
 
 P = ctypes.c_void_p
@@ -39,7 +40,7 @@ class LayerDesc(ctypes.Structure):
         ("bits_sal", P), ("r_sal", P), ("c_sal", P), ("sal_idx", P),
         ("workspace", P), ("workspace_bytes", ctypes.c_size_t),
         ("chunks_per_block", I32), ("waves_per_block", I32),
-        ("row_group", I32), ("sal_group", I32),
+        ("row_group", I32), ("sal_group", I32), ("table_precision", I32),
     ]
 
 
@@ -267,12 +268,13 @@ class DeviceLayer:
     """
 
     def __init__(self, layer, max_batch: int = 1, chunks_per_block: int = 0, waves_per_block: int = 0,
-                 device="cuda"):
+                 device="cuda", table_precision: int = TABLE_F32):
         import numpy as np
         import torch
 
         self.layer = layer
         self.max_batch = max_batch
+        self.table_precision = table_precision
         dev = torch.device(device)
 
         def up(a, dtype):
@@ -339,6 +341,7 @@ class DeviceLayer:
         d.waves_per_block = waves_per_block
         d.row_group = self.row_group
         d.sal_group = self.sal_group
+        d.table_precision = self.table_precision
         return d
 
     def gemv(self, x, y, batch=None, stream=None):

@@ -57,7 +57,8 @@ def run_gemv(args) -> None:
         else:
             lay = I.workload_layer(args.workload, args.shape, i)
             x = I.workload_x(args.workload, lay, args.batch, args.shape, i)
-        dls.append(F.DeviceLayer(lay, max_batch=args.batch, chunks_per_block=args.chunks_per_block))
+        dls.append(F.DeviceLayer(lay, max_batch=args.batch, chunks_per_block=args.chunks_per_block,
+                                 waves_per_block=args.waves_per_block, table_precision=args.table_precision))
         xs.append(torch.from_numpy(x.view(np.int16)).cuda())
         ys.append(torch.empty((args.batch, lay.n), dtype=torch.int16, device="cuda"))
     stream = torch.cuda.Stream()
@@ -83,7 +84,9 @@ def run_gemv(args) -> None:
     lay = dls[0].layer
     wb = (A.grouped_weight_bytes(lay.n, lay.k, lay.kb, lay.ks, 128, args.sal_group) if blockwise
           else A.weight_bytes(lay.n, lay.k, lay.s, lay.kb, lay.ks))
-    print(f"gemv workload {args.workload} shape {args.shape} ({sh.name} {sh.k}->{sh.n}, {args.format}): "
+    tables = "fp16 tables" if args.table_precision else "fp32 tables"
+    print(f"gemv workload {args.workload} shape {args.shape} ({sh.name} {sh.k}->{sh.n}, {args.format}, {tables}, "
+          f"batch {args.batch}): "
           f"{args.sets} sets x {args.reps} replays, {us:.3f} us per call, {wb / us / 1e3:.1f} GB/s of "
           f"{wb} weight-side bytes, plan {dls[0].plan}", flush=True)
     for d in dls:
@@ -184,6 +187,8 @@ def main() -> int:
     g.add_argument("--reps", type=int, default=2)
     g.add_argument("--batch", type=int, default=1)
     g.add_argument("--chunks-per-block", type=int, default=0)
+    g.add_argument("--waves-per-block", type=int, default=0)
+    g.add_argument("--table-precision", type=int, default=0, choices=[0, 1], help="0: fp32 tables, 1: fp16")
     g.add_argument("--format", choices=["per-row", "blockwise"], default="per-row")
     g.add_argument("--kb", type=int, default=2, help="blockwise: global bases")
     g.add_argument("--ks", type=int, default=2, help="blockwise: salient bases")

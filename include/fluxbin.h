@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define FLUXBIN_ABI_VERSION 2
+#define FLUXBIN_ABI_VERSION 3
 
 typedef enum {
   FLUXBIN_OK = 0,
@@ -83,6 +83,12 @@ typedef enum {
  *   contiguous memory in which lane l of a wave finds the 16 bytes of row l.
  *   Size in words: fluxbin_tiled_words(rows, cols). */
 typedef enum { FLUXBIN_LAYOUT_ROWMAJOR = 0, FLUXBIN_LAYOUT_TILED = 1 } fluxbin_layout;
+
+/* Table entry types of the GEMV (fluxbin_layer_desc.table_precision). */
+typedef enum {
+  FLUXBIN_TABLE_F32 = 0, /* fp32 entries (the default) */
+  FLUXBIN_TABLE_F16 = 1  /* fp16 entries: each entry summed in fp32, rounded to fp16 (nearest even) */
+} fluxbin_table_precision;
 
 /* Element kinds for fluxbin_vcm_gather. */
 typedef enum {
@@ -133,6 +139,10 @@ typedef struct {
                                   multiple of g).  S must take exactly sal_group columns from every group:
                                   s == sal_group * G and sal_idx[c] / 128 == c / sal_group (checked by
                                   fluxbin_create).  Must be 0 otherwise. */
+  int32_t table_precision;     /* fluxbin_table_precision of the GEMV's tables.  FLUXBIN_TABLE_F16 stores
+                                  the scale-fused tables in fp16 (quantised tables, LUT Tensor Core notes,
+                                  section 3.1.3): half the LDS per table; each entry adds one fp16
+                                  rounding, |error| <= 2^-11 |entry| (accumulation stays fp32) */
 } fluxbin_layer_desc;
 
 /* How a handle splits the work (read-only introspection). */

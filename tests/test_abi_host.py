@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported(fb):
 
 
 def test_abi_version_and_strings(fb):
-    assert fb.fluxbin_abi_version() == fb.ABI_VERSION == 2
+    assert fb.fluxbin_abi_version() == fb.ABI_VERSION == 3
     assert fb.fluxbin_status_string(fb.OK) == "ok"
     assert "invalid" in fb.fluxbin_status_string(fb.ERR_INVALID_ARGUMENT)
     assert fb.fluxbin_status_string(99) == "unknown status"
@@ -86,10 +86,11 @@ def test_too_many_splits_is_unsupported(fb):
 
 
 @pytest.mark.parametrize("field,value,status", [
-    ("abi_version", 1, 1), ("g", 3, 2), ("g", 16, 2), ("kb", 0, 2), ("kb", 5, 2), ("ks", 3, 2), ("ks", -1, 2),
+    ("abi_version", 2, 1), ("g", 3, 2), ("g", 16, 2), ("kb", 0, 2), ("kb", 5, 2), ("ks", 3, 2), ("ks", -1, 2),
     ("n", 0, 1), ("k", 0, 1), ("s", 0, 1), ("s", 5000, 1), ("max_batch", 0, 2), ("max_batch", 129, 2),
     ("chunks_per_block", 33, 1), ("chunks_per_block", -1, 1), ("waves_per_block", 2, 1), ("waves_per_block", 16, 1),
-    ("row_group", 64, 2), ("row_group", -1, 2), ("sal_group", 8, 1),
+    ("row_group", 64, 2), ("row_group", -1, 2), ("sal_group", 8, 1), ("table_precision", 2, 1),
+    ("table_precision", -1, 1),
 ])
 def test_workspace_size_rejects(fb, field, value, status):
     st, _ = ws_status(fb, good_desc(fb, **{field: value}))
