@@ -281,12 +281,18 @@ fluxbin_status decomp_shape(int64_t n, int64_t k, int32_t kb) {
   return FLUXBIN_OK;
 }
 
-size_t decomp_ws_bytes(int64_t n, int64_t k) {
-  return sizeof(double) * (size_t)(cdiv(n, kDecompRowChunk) * k + kDecompErrBlocks + 16 + 4 * (n + k));
+// Partials of the row and column steps: [ceil(n/64)][k] for the columns,
+// [ceil(k/512)][n] for the rows (tiled form); the larger of the two.
+int64_t decomp_partial_elems(int64_t n, int64_t k) {
+  return std::max(cdiv(n, kDecompRowChunk) * k, cdiv(k, kDecompTileCols) * n);
 }
 
-// Workspace: [chunks][k] column partials, kDecompErrBlocks error partials,
-// 16 scalars, then room for fp64 copies of the rounded scales (up to 4 bases).
+size_t decomp_ws_bytes(int64_t n, int64_t k) {
+  return sizeof(double) * (size_t)(decomp_partial_elems(n, k) + kDecompErrBlocks + 16 + 4 * (n + k));
+}
+
+// Workspace: the step partials, kDecompErrBlocks error partials, 16 scalars,
+// then room for fp64 copies of the rounded scales (up to 4 bases).
 struct DecompWs {
   double *partial, *errp, *scal, *rounded;
 };
@@ -298,7 +304,7 @@ fluxbin_status decomp_ws(void *ws, size_t bytes, int64_t n, int64_t k, DecompWs 
                 ws ? bytes : (size_t)0);
   if (!aligned(ws, 256)) return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "workspace not 256-byte aligned");
   out->partial = static_cast<double *>(ws);
-  out->errp = out->partial + cdiv(n, kDecompRowChunk) * k;
+  out->errp = out->partial + decomp_partial_elems(n, k);
   out->scal = out->errp + kDecompErrBlocks;
   out->rounded = out->scal + 16;
   return FLUXBIN_OK;
@@ -306,24 +312,65 @@ fluxbin_status decomp_ws(void *ws, size_t bytes, int64_t n, int64_t k, DecompWs 
 
 dim3 grid1(int64_t items, int per = 256) { return dim3((unsigned)cdiv(items, per)); }
 
+// The tiled kernels read W with 16-byte loads: rows must start 16-byte aligned.
+bool decomp_tiled(const uint16_t *w, int64_t k) { return k % 8 == 0 && aligned(w, 16); }
+
+dim3 decomp_tiles(int64_t n, int64_t k) {
+  return dim3((unsigned)cdiv(k, kDecompTileCols), (unsigned)cdiv(n, kDecompTileRows));
+}
+
+// kernel<KB> for a run-time kb in 1..4
+#define FB_KB_SWITCH(kb, KERNEL, ...)                                   \
+  switch (kb) {                                                         \
+    case 1: hipLaunchKernelGGL(KERNEL<1>, __VA_ARGS__); break;          \
+    case 2: hipLaunchKernelGGL(KERNEL<2>, __VA_ARGS__); break;          \
+    case 3: hipLaunchKernelGGL(KERNEL<3>, __VA_ARGS__); break;          \
+    default: hipLaunchKernelGGL(KERNEL<4>, __VA_ARGS__); break;         \
+  }
+
 void run_row(hipStream_t st, const uint16_t *w, int64_t n, int64_t k, int kb, int basis, const uint32_t *bits,
              const double *r, const double *c, const double *d, double *r_out, const DecompWs &ws) {
-  hipLaunchKernelGGL(decomp_sumsq_kernel, dim3(1), dim3(256), 0, st, c + (int64_t)basis * k, d, k, ws.scal);
-  hipLaunchKernelGGL(decomp_row_kernel, grid1(n, 4), dim3(256), 0, st, w, n, k, kb, basis, bits, r, c, d, ws.scal,
-                     r_out);
+  hipLaunchKernelGGL(decomp_sumsq_kernel, dim3(1), dim3(kSumsqThreads), 0, st, c + (int64_t)basis * k, d, k, ws.scal);
+  if (decomp_tiled(w, k)) {
+    FB_KB_SWITCH(kb, decomp_row_tiled_kernel, decomp_tiles(n, k), dim3(256), 0, st, w, n, k, basis, bits, r, c, d,
+                 ws.partial)
+    hipLaunchKernelGGL(decomp_row_finish_kernel, grid1(n), dim3(256), 0, st, ws.partial, cdiv(k, kDecompTileCols), n,
+                       ws.scal, r_out);
+  } else {
+    hipLaunchKernelGGL(decomp_row_kernel, grid1(n, 4), dim3(256), 0, st, w, n, k, kb, basis, bits, r, c, d, ws.scal,
+                       r_out);
+  }
 }
 
 void run_col(hipStream_t st, const uint16_t *w, int64_t n, int64_t k, int kb, int basis, const uint32_t *bits,
              const double *r, const double *c, double *c_out, const DecompWs &ws) {
   const int64_t chunks = cdiv(n, kDecompRowChunk);
-  hipLaunchKernelGGL(decomp_sumsq_kernel, dim3(1), dim3(256), 0, st, r + (int64_t)basis * n, nullptr, n, ws.scal);
-  hipLaunchKernelGGL(decomp_col_partial_kernel, dim3((unsigned)cdiv(k, 256), (unsigned)chunks), dim3(256), 0, st, w,
-                     n, k, kb, basis, bits, r, c, ws.partial);
+  hipLaunchKernelGGL(decomp_sumsq_kernel, dim3(1), dim3(kSumsqThreads), 0, st, r + (int64_t)basis * n, nullptr, n, ws.scal);
+  if (decomp_tiled(w, k)) {
+    FB_KB_SWITCH(kb, decomp_col_tiled_kernel, decomp_tiles(n, k), dim3(256), 0, st, w, n, k, basis, bits, r, c,
+                 ws.partial)
+  } else {
+    hipLaunchKernelGGL(decomp_col_partial_kernel, dim3((unsigned)cdiv(k, 256), (unsigned)chunks), dim3(256), 0, st,
+                       w, n, k, kb, basis, bits, r, c, ws.partial);
+  }
   hipLaunchKernelGGL(decomp_col_finish_kernel, grid1(k), dim3(256), 0, st, ws.partial, chunks, k, ws.scal, c_out);
 }
 
 void run_signs(hipStream_t st, const uint16_t *w, int64_t n, int64_t k, int kb, const double *r, const double *c,
                uint32_t *bits) {
+  if (decomp_tiled(w, k)) {
+    switch (kb) {
+      case 1: hipLaunchKernelGGL((decomp_sign_tiled_kernel<1, false>), decomp_tiles(n, k), dim3(256), 0, st, w, n, k,
+                                 0, nullptr, r, c, bits); break;
+      case 2: hipLaunchKernelGGL((decomp_sign_tiled_kernel<2, false>), decomp_tiles(n, k), dim3(256), 0, st, w, n, k,
+                                 0, nullptr, r, c, bits); break;
+      case 3: hipLaunchKernelGGL((decomp_sign_tiled_kernel<3, false>), decomp_tiles(n, k), dim3(256), 0, st, w, n, k,
+                                 0, nullptr, r, c, bits); break;
+      default: hipLaunchKernelGGL((decomp_sign_tiled_kernel<4, false>), decomp_tiles(n, k), dim3(256), 0, st, w, n,
+                                  k, 0, nullptr, r, c, bits); break;
+    }
+    return;
+  }
   const dim3 g = grid1(n * cdiv(k, 64), 4);
   switch (kb) {
     case 1: hipLaunchKernelGGL(decomp_sign_kernel<1>, g, dim3(256), 0, st, w, n, k, r, c, bits); break;
@@ -335,6 +382,19 @@ void run_signs(hipStream_t st, const uint16_t *w, int64_t n, int64_t k, int kb, 
 
 void run_residual_signs(hipStream_t st, const uint16_t *w, int64_t n, int64_t k, int kb, int basis,
                         const uint32_t *bits, const double *r, const double *c, uint32_t *out) {
+  if (decomp_tiled(w, k)) {
+    switch (kb) {
+      case 1: hipLaunchKernelGGL((decomp_sign_tiled_kernel<1, true>), decomp_tiles(n, k), dim3(256), 0, st, w, n, k,
+                                 basis, bits, r, c, out); break;
+      case 2: hipLaunchKernelGGL((decomp_sign_tiled_kernel<2, true>), decomp_tiles(n, k), dim3(256), 0, st, w, n, k,
+                                 basis, bits, r, c, out); break;
+      case 3: hipLaunchKernelGGL((decomp_sign_tiled_kernel<3, true>), decomp_tiles(n, k), dim3(256), 0, st, w, n, k,
+                                 basis, bits, r, c, out); break;
+      default: hipLaunchKernelGGL((decomp_sign_tiled_kernel<4, true>), decomp_tiles(n, k), dim3(256), 0, st, w, n,
+                                  k, basis, bits, r, c, out); break;
+    }
+    return;
+  }
   hipLaunchKernelGGL(decomp_residual_sign_kernel, grid1(n * cdiv(k, 64), 4), dim3(256), 0, st, w, n, k, kb, basis,
                      bits, r, c, out);
 }
