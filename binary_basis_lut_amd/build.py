@@ -16,9 +16,9 @@ PKG = Path(__file__).resolve().parent
 ROOT = PKG.parent
 CSRC = PKG / "csrc"
 SOURCES = [CSRC / "fluxbin.hip"] + [CSRC / f"gemv_g{g}_rs{rs}_t{t}.hip" for g in (4, 8) for rs in (0, 1)
-                                   for t in (32, 16)]
+                                   for t in (32, 16)] + [CSRC / "gemm_mfma.hip"]
 HEADERS = [CSRC / "common.hpp", CSRC / "gemv_kernel.hpp", CSRC / "aux_kernels.hpp", CSRC / "decomp_kernels.hpp",
-           ROOT / "include" / "fluxbin.h"]
+           CSRC / "gemm_mfma.hpp", ROOT / "include" / "fluxbin.h"]
 DEPS = SOURCES + HEADERS
 BUILD = PKG / "_build"
 LIB = BUILD / "libfluxbin.so"

@@ -17,6 +17,7 @@
 #include <vector>
 
 #include "aux_kernels.hpp"
+#include "gemm_mfma.hpp"
 #include "decomp_kernels.hpp"
 
 using namespace fluxbin;
@@ -60,7 +61,10 @@ struct Plan {
   int32_t gsplits;     // workgroup ranges over the first part
   int32_t splits;
   int64_t n_pad;
-  size_t acc_bytes;    // packed split-reduction words (splits > 1)
+  size_t acc_bytes;    // workspace (splits > 1): packed reduction words (LUT) or fp32 partials (MFMA)
+  bool mfma;           // matrix-core route: ranges of one segment each
+  int32_t ranges_g;    // matrix-core ranges per global / salient segment
+  int32_t ranges_s;
 };
 
 constexpr int kMaxBatch = 128;
@@ -94,6 +98,11 @@ fluxbin_status validate_shape(const fluxbin_layer_desc *d) {
                 kMaxCpb);
   if (d->waves_per_block != 0 && d->waves_per_block != 4 && d->waves_per_block != 8)
     return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "waves_per_block = %d (0, 4 or 8)", d->waves_per_block);
+  if (d->compute != FLUXBIN_COMPUTE_LUT && d->compute != FLUXBIN_COMPUTE_MFMA)
+    return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "compute = %d (0 = LUT, 1 = MFMA)", d->compute);
+  if (d->compute == FLUXBIN_COMPUTE_MFMA && d->waves_per_block != 0 && d->waves_per_block != kMfmaWaves)
+    return fail(FLUXBIN_ERR_UNSUPPORTED, "waves_per_block = %d with compute MFMA (0 or %d)", d->waves_per_block,
+                kMfmaWaves);
   if (d->table_precision != FLUXBIN_TABLE_F32 && d->table_precision != FLUXBIN_TABLE_F16)
     return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "table_precision = %d (0 = fp32, 1 = fp16)", d->table_precision);
   if (d->row_group != 0 && d->row_group != kChunkCols)
@@ -145,11 +154,54 @@ int32_t batch_group(int32_t g, int64_t max_batch) {
 
 int entry_bytes(const fluxbin_layer_desc *d) { return d->table_precision == FLUXBIN_TABLE_F16 ? 2 : 4; }
 
+// Matrix-core route: ranges of cpb chunks inside one segment, 128 rows per
+// workgroup at the widest batch.  Automatic cpb: the most chunks per range
+// that still give kMfmaTargetBlocks workgroups, about one and a half per CU
+// (fewer, longer ranges mean fewer partial sums to store and add; measured on
+// MI355X over the 7B MLP shapes at batches 32 and 128).
+constexpr int64_t kMfmaTargetBlocks = 384;
+
+fluxbin_status make_mfma_plan(const fluxbin_layer_desc *d, Plan *p) {
+  // x is addressed with 32-bit element offsets: batch row * k + column
+  if (d->max_batch * d->k > (int64_t)INT32_MAX - kChunkCols)
+    return fail(FLUXBIN_ERR_UNSUPPORTED, "max_batch * k = %lld too large for compute MFMA (below 2^31)",
+                (long long)(d->max_batch * d->k));
+  p->mfma = true;
+  p->nb = 0;
+  p->pf = 0;
+  p->waves = kMfmaWaves;
+  p->row_blocks = (int32_t)cdiv(d->n, 2 * kTileRows);  // at the widest batch: 128 rows per workgroup
+  const int32_t nc_g = (int32_t)cdiv(d->k, kChunkCols), nc_s = d->ks > 0 ? (int32_t)cdiv(d->s, kChunkCols) : 0;
+  auto splits_for = [&](int32_t c) { return d->kb * (int32_t)cdiv(nc_g, c) + d->ks * (int32_t)cdiv(nc_s, c); };
+  int32_t cpb = d->chunks_per_block;
+  if (!cpb) {
+    cpb = 1;
+    while (cpb < kMaxCpb && splits_for(cpb) > 1 &&
+           (int64_t)p->row_blocks * splits_for(cpb * 2) >= kMfmaTargetBlocks)
+      cpb *= 2;
+    while (splits_for(cpb) > kMaxSplits && cpb < kMaxCpb) ++cpb;
+  }
+  p->cpb = cpb;
+  p->ranges_g = (int32_t)cdiv(nc_g, cpb);
+  p->ranges_s = d->ks > 0 ? (int32_t)cdiv(nc_s, cpb) : 0;
+  p->splits = splits_for(cpb);
+  p->gsplits = d->kb * p->ranges_g;
+  p->gchunks = d->kb * nc_g;
+  if (p->splits > kMaxSplits)
+    return fail(FLUXBIN_ERR_UNSUPPORTED, "%d column ranges exceed %d (chunks_per_block %d)", p->splits, kMaxSplits,
+                cpb);
+  p->acc_bytes = p->splits > 1 ? (size_t)p->splits * d->max_batch * p->n_pad * sizeof(float) : 0;
+  return FLUXBIN_OK;
+}
+
 fluxbin_status make_plan(const fluxbin_layer_desc *d, Plan *p) {
-  p->nb = batch_group(d->g, d->max_batch);
   p->row_tiles = (int32_t)cdiv(d->n, kTileRows);
   p->n_pad = (int64_t)p->row_tiles * kTileRows;
   p->total_chunks = (int32_t)(d->kb * cdiv(d->k, kChunkCols) + d->ks * cdiv(d->s, kChunkCols));
+  p->mfma = false;
+  p->ranges_g = p->ranges_s = 0;
+  if (d->compute == FLUXBIN_COMPUTE_MFMA) return make_mfma_plan(d, p);
+  p->nb = batch_group(d->g, d->max_batch);
   if (d->waves_per_block) {
     p->waves = d->waves_per_block;
   } else {
@@ -575,12 +627,16 @@ fluxbin_status fluxbin_create(const fluxbin_layer_desc *d, fluxbin_handle *out) 
     e = hipDeviceSynchronize();
     if (e != hipSuccess) return hip_fail(e, "synchronising after create");
   }
-  gemv_fn fn = pick_gemv(d->g, d->row_group ? 1 : 0, d->table_precision, p.nb, p.waves, p.pf);
-  if (!fn) return fail(FLUXBIN_ERR_UNSUPPORTED, "no kernel for g = %d, batch width %d, %d waves", d->g, p.nb, p.waves);
-  const size_t lds = (size_t)lds_bytes(d->g, p.nb, p.cpb, entry_bytes(d));
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     (int)lds);
-  if (e != hipSuccess) return hip_fail(e, "setting the kernel's dynamic LDS size");
+  gemv_fn fn = nullptr;
+  size_t lds = 0;
+  hipError_t e = hipSuccess;
+  if (!p.mfma) {
+    fn = pick_gemv(d->g, d->row_group ? 1 : 0, d->table_precision, p.nb, p.waves, p.pf);
+    if (!fn) return fail(FLUXBIN_ERR_UNSUPPORTED, "no kernel for g = %d, batch width %d, %d waves", d->g, p.nb, p.waves);
+    lds = (size_t)lds_bytes(d->g, p.nb, p.cpb, entry_bytes(d));
+    e = hipFuncSetAttribute(reinterpret_cast<const void *>(fn), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return hip_fail(e, "setting the kernel's dynamic LDS size");
+  }
   const int32_t *idx = d->sal_idx;
   if (d->ks == 0) {
     void *z = nullptr;
@@ -610,12 +666,13 @@ fluxbin_status fluxbin_destroy(fluxbin_handle h) {
 fluxbin_status fluxbin_get_plan(fluxbin_handle h, fluxbin_plan *plan) {
   if (!h || !plan) return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "NULL argument");
   const Plan &p = h->plan;
-  plan->rows_per_block = p.waves * kTileRows;
+  plan->rows_per_block = p.mfma ? 2 * kTileRows : p.waves * kTileRows;  // matrix cores: at batches above 64
   plan->chunks_per_block = p.cpb;
   plan->row_blocks = p.row_blocks;
   plan->splits = p.splits;
   plan->total_chunks = p.total_chunks;
-  plan->lds_bytes = lds_bytes(h->d.g, p.nb, p.cpb, entry_bytes(&h->d));
+  plan->lds_bytes = p.mfma ? (int32_t)((kMfmaMaxBlocks * 32 * kMfmaXStride + kChunkCols) * sizeof(uint16_t))
+                           : lds_bytes(h->d.g, p.nb, p.cpb, entry_bytes(&h->d));
   plan->grid = (int64_t)p.row_blocks * p.splits;
   return ok();
 }
@@ -658,6 +715,53 @@ fluxbin_status fluxbin_build_lut(fluxbin_handle h, const uint16_t *x, int64_t ba
   return ok();
 }
 
+namespace {
+
+// The matrix-core route: the narrowest instance that covers the batch in one
+// workgroup along y (32, 64 or 128 rows: waves of 64 weight rows x 32 or 64
+// batch rows, four along the weight rows, or two x two).  The per-element
+// arithmetic does not depend on the instance.
+fluxbin_status mfma_gemv(fluxbin_handle h, const uint16_t *x, uint16_t *y, int64_t batch, hipStream_t stream) {
+  const fluxbin_layer_desc &d = h->d;
+  const Plan &p = h->plan;
+  const int nbt = batch <= 32 ? 1 : 2, wb = batch <= 64 ? 1 : 2;
+  mfma_fn fn = mfma_pick(nbt, wb, d.row_group ? 1 : 0);
+  if (!fn) return fail(FLUXBIN_ERR_UNSUPPORTED, "no matrix-core kernel for %d x %d batch blocks", nbt, wb);
+  const int64_t rows_per_block = (int64_t)(kMfmaWaves / wb) * kTileRows;
+  MfmaArgs a;
+  a.L = layer_args(d);
+  a.idx_or_dummy = h->idx_or_dummy;
+  a.x = x;
+  a.y = y;
+  a.part = p.splits > 1 ? reinterpret_cast<float *>(d.workspace) : nullptr;
+  a.n_pad = p.n_pad;
+  const int64_t groups = d.row_group ? cdiv(d.k, d.row_group) : 0;
+  a.rstride_g = d.row_group ? fluxbin_tiled_scale_elems(d.n, groups, 1) : d.n;
+  a.rstride_s = d.row_group && d.ks > 0 ? fluxbin_tiled_scale_elems(d.n, groups, kChunkCols / d.sal_group) : d.n;
+  a.cpb = p.cpb;
+  a.ranges_g = p.ranges_g;
+  a.ranges_s = p.ranges_s;
+  a.row_tiles = p.row_tiles;
+  a.row_blocks = (int32_t)cdiv(d.n, rows_per_block);
+  a.splits = p.splits;
+  a.batch = (int32_t)batch;
+  a.xvec = d.k % 8 == 0 && aligned(x, 16) && aligned(d.c_global, 16) ? 1 : 0;
+  a.sal_group = d.row_group && d.ks > 0 ? d.sal_group : kChunkCols;
+  const dim3 grid((unsigned)((int64_t)a.row_blocks * p.splits), (unsigned)cdiv(batch, 32 * nbt * wb));
+  hipLaunchKernelGGL(fn, grid, dim3(kMfmaWaves * 64), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "matrix-core gemv launch");
+  if (p.splits > 1) {
+    hipLaunchKernelGGL(mfma_finalize_kernel, dim3(grid_for(batch * d.n)), dim3(256), 0, stream, a.part, p.splits,
+                       (int32_t)batch, d.n, p.n_pad, y);
+    e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "matrix-core finalize launch");
+  }
+  return ok();
+}
+
+}  // namespace
+
 fluxbin_status fluxbin_gemv(fluxbin_handle h, const uint16_t *x, uint16_t *y, int64_t batch, void *stream) {
   if (!h) return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "handle is NULL");
   if (batch < 0 || batch > h->d.max_batch)
@@ -668,6 +772,7 @@ fluxbin_status fluxbin_gemv(fluxbin_handle h, const uint16_t *x, uint16_t *y, in
   if (h->fault_launch) return fail(FLUXBIN_ERR_HIP, "injected launch fault (FLUXBIN_FAULT=launch)");
   const fluxbin_layer_desc &d = h->d;
   const Plan &p = h->plan;
+  if (p.mfma) return mfma_gemv(h, x, y, batch, (hipStream_t)stream);
   GemvArgs a;
   a.L = layer_args(d);
   gemv_segments(d, a.seg);

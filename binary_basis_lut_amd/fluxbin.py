@@ -20,11 +20,12 @@ if not LIB_PATH.exists():
 
 _lib = ctypes.CDLL(str(LIB_PATH))
 
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
 LAYOUT_ROWMAJOR, LAYOUT_TILED = 0, 1
 TABLE_F32, TABLE_F16 = 0, 1
+COMPUTE_LUT, COMPUTE_MFMA = 0, 1
 DT_I8, DT_F16, DT_BITS = 0, 1, 2
 
 P = ctypes.c_void_p
@@ -40,7 +41,7 @@ class LayerDesc(ctypes.Structure):
         ("bits_sal", P), ("r_sal", P), ("c_sal", P), ("sal_idx", P),
         ("workspace", P), ("workspace_bytes", ctypes.c_size_t),
         ("chunks_per_block", I32), ("waves_per_block", I32),
-        ("row_group", I32), ("sal_group", I32), ("table_precision", I32),
+        ("row_group", I32), ("sal_group", I32), ("table_precision", I32), ("compute", I32),
     ]
 
 
@@ -268,13 +269,14 @@ class DeviceLayer:
     """
 
     def __init__(self, layer, max_batch: int = 1, chunks_per_block: int = 0, waves_per_block: int = 0,
-                 device="cuda", table_precision: int = TABLE_F32):
+                 device="cuda", table_precision: int = TABLE_F32, compute: int = COMPUTE_LUT):
         import numpy as np
         import torch
 
         self.layer = layer
         self.max_batch = max_batch
         self.table_precision = table_precision
+        self.compute = compute
         dev = torch.device(device)
 
         def up(a, dtype):
@@ -342,6 +344,7 @@ class DeviceLayer:
         d.row_group = self.row_group
         d.sal_group = self.sal_group
         d.table_precision = self.table_precision
+        d.compute = self.compute
         return d
 
     def gemv(self, x, y, batch=None, stream=None):

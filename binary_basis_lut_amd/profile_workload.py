@@ -58,7 +58,8 @@ def run_gemv(args) -> None:
             lay = I.workload_layer(args.workload, args.shape, i)
             x = I.workload_x(args.workload, lay, args.batch, args.shape, i)
         dls.append(F.DeviceLayer(lay, max_batch=args.batch, chunks_per_block=args.chunks_per_block,
-                                 waves_per_block=args.waves_per_block, table_precision=args.table_precision))
+                                 waves_per_block=args.waves_per_block, table_precision=args.table_precision,
+                                 compute=F.COMPUTE_MFMA if args.compute == "mfma" else F.COMPUTE_LUT))
         xs.append(torch.from_numpy(x.view(np.int16)).cuda())
         ys.append(torch.empty((args.batch, lay.n), dtype=torch.int16, device="cuda"))
     stream = torch.cuda.Stream()
@@ -85,6 +86,8 @@ def run_gemv(args) -> None:
     wb = (A.grouped_weight_bytes(lay.n, lay.k, lay.kb, lay.ks, 128, args.sal_group) if blockwise
           else A.weight_bytes(lay.n, lay.k, lay.s, lay.kb, lay.ks))
     tables = "fp16 tables" if args.table_precision else "fp32 tables"
+    if args.compute == "mfma":
+        tables = "matrix cores"
     print(f"gemv workload {args.workload} shape {args.shape} ({sh.name} {sh.k}->{sh.n}, {args.format}, {tables}, "
           f"batch {args.batch}): "
           f"{args.sets} sets x {args.reps} replays, {us:.3f} us per call, {wb / us / 1e3:.1f} GB/s of "
@@ -193,6 +196,7 @@ def main() -> int:
     g.add_argument("--kb", type=int, default=2, help="blockwise: global bases")
     g.add_argument("--ks", type=int, default=2, help="blockwise: salient bases")
     g.add_argument("--sal-group", type=int, default=8, choices=[8, 16])
+    g.add_argument("--compute", choices=["lut", "mfma"], default="lut")
     dp = sub.add_parser("decompose")
     dp.add_argument("--n", type=int, default=4096)
     dp.add_argument("--k", type=int, default=4096)

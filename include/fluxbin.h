@@ -42,8 +42,9 @@
  *     thread-local message.  Device faults surface at the caller's next
  *     synchronisation.  No C++ exception crosses this boundary.
  *   - fluxbin_build_lut launches one kernel and fluxbin_gemv one kernel per
- *     group of batch rows (16 at g = 4, 4 at g = 8; one launch up to that
- *     batch); neither ever allocates, copies, sets memory or synchronises, so
+ *     group of batch rows (LUT route: 16 at g = 4, 4 at g = 8; one launch up
+ *     to that batch; matrix-core route: one, plus a summing launch when the plan
+ *     splits the columns); neither ever allocates, copies, sets memory or synchronises, so
  *     they may be captured in a HIP graph.  fluxbin_create does synchronise.
  */
 #ifndef FLUXBIN_H
@@ -56,7 +57,7 @@
 extern "C" {
 #endif
 
-#define FLUXBIN_ABI_VERSION 3
+#define FLUXBIN_ABI_VERSION 4
 
 typedef enum {
   FLUXBIN_OK = 0,
@@ -89,6 +90,16 @@ typedef enum {
   FLUXBIN_TABLE_F32 = 0, /* fp32 entries (the default) */
   FLUXBIN_TABLE_F16 = 1  /* fp16 entries: each entry summed in fp32, rounded to fp16 (nearest even) */
 } fluxbin_table_precision;
+
+/* How fluxbin_gemv evaluates a handle's product (fluxbin_layer_desc.compute).
+ * The choice is made per handle, not per call, so that the result of a batch
+ * row never depends on the batch it came with. */
+typedef enum {
+  FLUXBIN_COMPUTE_LUT = 0, /* table lookups in LDS (the GEMV of the FluxBin summary, section 3 bullet
+                              "LUT-Based GEMV Kernel"): decode, batches of a few rows */
+  FLUXBIN_COMPUTE_MFMA = 1 /* matrix cores: the sign bits expanded in registers to +-c (exact in fp16)
+                              against fp16 x, fp32 accumulation; prefill batches (tens of rows and up) */
+} fluxbin_compute;
 
 /* Element kinds for fluxbin_vcm_gather. */
 typedef enum {
@@ -142,12 +153,18 @@ typedef struct {
   int32_t table_precision;     /* fluxbin_table_precision of the GEMV's tables.  FLUXBIN_TABLE_F16 stores
                                   the scale-fused tables in fp16 (quantised tables, LUT Tensor Core notes,
                                   section 3.1.3): half the LDS per table; each entry adds one fp16
-                                  rounding, |error| <= 2^-11 |entry| (accumulation stays fp32) */
+                                  rounding, |error| <= 2^-11 |entry| (accumulation stays fp32).  Ignored by
+                                  FLUXBIN_COMPUTE_MFMA, which builds no tables */
+  int32_t compute;             /* fluxbin_compute.  FLUXBIN_COMPUTE_MFMA ignores g and table_precision,
+                                  takes chunks_per_block as the 128-column chunks of one segment per
+                                  workgroup (a workgroup never spans two segments) and needs
+                                  waves_per_block 0 or 4 (128 rows per workgroup) */
 } fluxbin_layer_desc;
 
 /* How a handle splits the work (read-only introspection). */
 typedef struct {
-  int32_t rows_per_block;   /* output rows per workgroup (64 per wave) */
+  int32_t rows_per_block;   /* output rows per workgroup (64 per wave; matrix cores: 128 at batches above 64,
+                               256 below, and row_blocks and grid likewise) */
   int32_t chunks_per_block; /* 128-column chunks per workgroup */
   int32_t row_blocks;       /* workgroups along the rows */
   int32_t splits;           /* workgroups along the concatenated columns of all segments */
@@ -209,7 +226,11 @@ fluxbin_status fluxbin_relayout_scales(const uint16_t *src, int64_t rows, int64_
 fluxbin_status fluxbin_vcm_gather(const int32_t *idx, int64_t s, const void *src, int64_t rows, int64_t cols,
                                   int32_t dtype, void *dst, void *stream);
 
-/* Workspace bytes a layer needs (host-side arithmetic, no device access). */
+/* Workspace bytes a layer needs (host-side arithmetic, no device access):
+ * 0 when the plan has one column range per row (fluxbin_plan.splits == 1);
+ * else LUT route: max_batch * ceil(n/64)*64 packed 64-bit reduction words
+ * (zeroed by fluxbin_create, left zero by every call); matrix-core route:
+ * splits * max_batch * ceil(n/64)*64 fp32 partial sums (no zeroing). */
 fluxbin_status fluxbin_workspace_size(const fluxbin_layer_desc *d, size_t *bytes);
 
 /* Validate the description (copies sal_idx to the host to check it), zero the
@@ -238,13 +259,20 @@ fluxbin_status fluxbin_build_lut(fluxbin_handle h, const uint16_t *x, int64_t ba
 
 /* y = the layer applied to x.  x: fp16 [batch][k], y: fp16 [batch][n]
  * (round to nearest even), 0 <= batch <= max_batch (0 launches nothing).
- * Tables and accumulation are fp32.  Per-row scales multiply a segment's
+ * FLUXBIN_COMPUTE_LUT: tables and accumulation are fp32.  Per-row scales multiply a segment's
  * accumulated sum; block-wise scales multiply the sum of each global chunk
  * (one group) and of each 8 salient columns (one group, or half of one when
  * sal_group = 16), before those sums are added.  When the handle's plan splits the
  * columns over several workgroups (fluxbin_plan.splits > 1), the partial
  * sums of a row are combined exactly as 2^-30 fixed-point integers: each
  * partial is rounded to 2^-31 (absolute) and partials beyond +-2^17 saturate.
+ * FLUXBIN_COMPUTE_MFMA (one launch, two with splits): each weight is used as +-c_j
+ * in fp16 against x in fp16, products exact, sums accumulated in fp32 by
+ * the matrix cores 16 columns at a time; a per-row scale multiplies the sum
+ * of a workgroup's range of one segment, a block-wise scale the sum of each
+ * global chunk and of each salient group (sal_group columns); when a row has
+ * several ranges (fluxbin_plan.splits, at least kb + ks then) their fp32
+ * partials are added in range order by a second launch.
  * Uses the handle's workspace: at most one call per handle may be in flight
  * at a time (use one handle per concurrent stream).  For a given handle the
  * result of row b does not depend on the other rows of the batch, and

@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported(fb):
 
 
 def test_abi_version_and_strings(fb):
-    assert fb.fluxbin_abi_version() == fb.ABI_VERSION == 3
+    assert fb.fluxbin_abi_version() == fb.ABI_VERSION == 4
     assert fb.fluxbin_status_string(fb.OK) == "ok"
     assert "invalid" in fb.fluxbin_status_string(fb.ERR_INVALID_ARGUMENT)
     assert fb.fluxbin_status_string(99) == "unknown status"
@@ -90,7 +90,7 @@ def test_too_many_splits_is_unsupported(fb):
     ("n", 0, 1), ("k", 0, 1), ("s", 0, 1), ("s", 5000, 1), ("max_batch", 0, 2), ("max_batch", 129, 2),
     ("chunks_per_block", 33, 1), ("chunks_per_block", -1, 1), ("waves_per_block", 2, 1), ("waves_per_block", 16, 1),
     ("row_group", 64, 2), ("row_group", -1, 2), ("sal_group", 8, 1), ("table_precision", 2, 1),
-    ("table_precision", -1, 1),
+    ("table_precision", -1, 1), ("compute", 2, 1), ("compute", -1, 1),
 ])
 def test_workspace_size_rejects(fb, field, value, status):
     st, _ = ws_status(fb, good_desc(fb, **{field: value}))
@@ -108,6 +108,25 @@ def test_g8_batch_limit_and_salient_flags(fb):
     assert ws_status(fb, good_desc(fb, ks=0, s=0))[0] == fb.OK
     assert ws_status(fb, good_desc(fb, ks=0, s=8))[0] == fb.ERR_INVALID_ARGUMENT
     assert ws_status(fb, good_desc(fb, chunks_per_block=8, max_batch=8))[0] == fb.ERR_UNSUPPORTED
+
+
+def test_mfma_plan_ranges_never_span_segments(fb):
+    # 4096 x 4096, kb = 2, ks = 1, s = 256: 32 global chunks per basis, 2 salient chunks
+    mf = fb.COMPUTE_MFMA
+    for cpb, splits in [(1, 66), (2, 33), (4, 17), (8, 9), (32, 3)]:
+        st, ws = ws_status(fb, good_desc(fb, compute=mf, chunks_per_block=cpb, max_batch=64))
+        assert st == fb.OK and ws == splits * 64 * 4096 * 4, fb.fluxbin_last_error()  # fp32 partials
+    # one segment in one range: no split, no workspace (kb = 1, k = 4096, 32 chunks)
+    st, ws = ws_status(fb, good_desc(fb, compute=mf, kb=1, ks=0, s=0, chunks_per_block=32))
+    assert st == fb.OK and ws == 0
+    # the matrix-core route ignores g and the table type, and runs 4 waves per workgroup
+    assert ws_status(fb, good_desc(fb, compute=mf, g=8, max_batch=128))[0] == fb.OK
+    assert ws_status(fb, good_desc(fb, compute=mf, waves_per_block=4))[0] == fb.OK
+    assert ws_status(fb, good_desc(fb, compute=mf, waves_per_block=8))[0] == fb.ERR_UNSUPPORTED
+    assert ws_status(fb, good_desc(fb, compute=mf, k=1 << 17, ks=0, s=0, chunks_per_block=1))[0] == \
+        fb.ERR_UNSUPPORTED  # 2 x 1024 ranges
+    assert ws_status(fb, good_desc(fb, compute=mf, k=1 << 25, ks=0, s=0, max_batch=64))[0] == \
+        fb.ERR_UNSUPPORTED  # batch row offsets of x beyond 32 bits
 
 
 def test_create_rejects_before_touching_the_device(fb):

@@ -73,15 +73,19 @@ def magnitude(layer, x_np, rows):
     return out
 
 
-def check_y(orc, layer, x_np, y16, plan, rows=None):
-    """Assert the contract and the rigorous bound on the listed rows; return the worst ratios."""
+def check_y(orc, layer, x_np, y16, plan, rows=None, steps=None):
+    """Assert the contract and the rigorous bound on the listed rows; return the worst ratios.
+
+    `steps` bounds the fp32 roundings any one product term goes through (default: the LUT route's
+    table build, one lookup add per g columns, the scale folds and the split partials)."""
     rows = np.arange(layer.n) if rows is None else np.asarray(rows)
     y_ref, mag = orc.gemv_dense(layer, x_np, rows=rows)
     y = orc.half_to_double(y16[:, rows])
     err = np.abs(y - y_ref)
     assert np.all(np.isfinite(y)), "non-finite output"
     contract = 1e-3 * mag
-    steps = layer.g + max(layer.k, layer.s) / layer.g + layer.kb + layer.ks + plan["splits"] + 3
+    if steps is None:
+        steps = layer.g + max(layer.k, layer.s) / layer.g + layer.kb + layer.ks + plan["splits"] + 3
     # fp32 table build and accumulation (first-order worst case), fixed-point combination of the
     # split partials (2^-31 per partial, exact sum), then fp16 output rounding (possibly via fp32)
     fp32 = 2.0 ** -24 * steps * magnitude(layer, x_np, rows) + plan["splits"] * 2.0 ** -31
