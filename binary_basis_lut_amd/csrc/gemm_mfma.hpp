@@ -172,6 +172,15 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void gemm_mfma_kernel(const MfmaAr
   const int tile = min(row0 / kTileRows, a.row_tiles - 1);
   const int wbat = b0 + wb * NBT * 32;          // first batch row of this wave
   const int64_t roff0 = ((int64_t)tile * nc * kTileRows + m) * gpc;  // block-wise scales of row m, chunk 0
+  // per-row scales of the lane's two rows, loaded now so the epilogue does not wait for them
+  float rrow[2] = {1.0f, 1.0f};
+  if constexpr (RS == 0) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int row = row0 + 32 * i + m;
+      rrow[i] = h2f(rbase[min(row, (int)L.n - 1)]);
+    }
+  }
 
   struct Stage {
     u32x4 x[kPieces];
@@ -353,7 +362,7 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void gemm_mfma_kernel(const MfmaAr
   for (int i = 0; i < 2; ++i) {
     const int row = row0 + 32 * i + m;
     if (row >= L.n) continue;
-    const float r = RS == 0 ? h2f(rbase[row]) : 1.0f;  // per-row scale of the range's sum
+    const float r = rrow[i];  // per-row scale of the range's sum (1 when block-wise)
 #pragma unroll
     for (int j = 0; j < NBT; ++j) {
 #pragma unroll
@@ -370,14 +379,25 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void gemm_mfma_kernel(const MfmaAr
   }
 }
 
-// Sum of the ranges' partials of every output, in range order, to fp16.
+// Sum of the ranges' partials of every output, in range order, to fp16.  The
+// loads of eight ranges are issued together; the additions keep their order.
 static __global__ __launch_bounds__(256) void mfma_finalize_kernel(const float *part, int32_t splits, int32_t batch,
-                                                            int64_t n, int64_t n_pad, uint16_t *y) {
+                                                                   int64_t n, int64_t n_pad, uint16_t *y) {
   const int64_t total = (int64_t)batch * n;
+  const int64_t stride = (int64_t)batch * n_pad;  // between ranges
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
     const int64_t b = i / n, row = i - b * n;
+    const float *p = part + b * n_pad + row;
     float s = 0.0f;
-    for (int r = 0; r < splits; ++r) s += part[((int64_t)r * batch + b) * n_pad + row];
+    int r = 0;
+    for (; r + 8 <= splits; r += 8) {
+      float v[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] = p[(int64_t)(r + q) * stride];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) s += v[q];
+    }
+    for (; r < splits; ++r) s += p[(int64_t)r * stride];
     y[i] = f2h(s);
   }
 }

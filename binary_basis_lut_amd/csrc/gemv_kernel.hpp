@@ -337,9 +337,28 @@ __global__ __launch_bounds__(WAVES * 64) void lut_gemv_kernel(const GemvArgs a) 
     // The fixed-point step quantises each partial to 2^-31 (absolute) and
     // saturates partials beyond +-2^17, twice the largest fp16 output.
     //
-    // All NB atomics are issued before any result is examined, so that their
-    // round trips overlap instead of queueing one behind the other.
-    if (row_ok) {
+    // With several batch rows, all NB atomics are issued before any result
+    // is examined, so that their round trips overlap instead of queueing one
+    // behind the other.
+    if constexpr (NB == 1) {
+      if (row_ok) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          if (b < a.batch) {
+            const float scaled = fminf(fmaxf(part[b] * kFixScale, -kFixClamp), kFixClamp);
+            const uint64_t contrib = (uint64_t)(__float2ll_rn(scaled) + kFixBias);
+            uint64_t *slot = a.acc + (int64_t)b * a.n_pad + row;
+            const uint64_t old =
+                __hip_atomic_fetch_add(slot, contrib + kOneArrival, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if ((int)(old >> kCountShift) == a.splits - 1) {
+              const int64_t total = (int64_t)((old & kValueMask) + contrib) - (int64_t)a.splits * kFixBias;
+              a.y[(int64_t)b * L.n + row] = f2h(__ll2float_rn(total) * kFixInv);
+              __hip_atomic_store(slot, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+          }
+        }
+      }
+    } else if (row_ok) {
       uint64_t contrib[NB], old[NB];
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
