@@ -133,3 +133,46 @@ def test_mfma_and_lut_routes_agree_within_the_contract(fb, orc):
     check_y(orc, layer, x, yb, b.plan)
     a.close()
     b.close()
+
+
+def test_mfma_graph_capture_replays_match_eager(fb):
+    """The route's two launches (multiply, then the sum of the ranges' partials) captured in a
+    HIP graph: every replay, with eager work in between, equals the eager result."""
+    n, k, batch = 2000, 4096, 48
+    note(f"mfma graph capture n={n} k={k} batch={batch}")
+    layer = I.make_layer(n, k, 2, 1, 4, s=128, outlier_frac=0.01, seed=(101, n, k))
+    x = torch.from_numpy(I.make_x(layer, batch, seed=(101, n, k)).view(np.int16)).cuda()
+    dl = mfma_layer(fb, layer, batch)
+    assert dl.plan["splits"] > 1
+    eager = torch.empty((batch, n), dtype=torch.int16, device="cuda")
+    dl.gemv(x, eager)
+    torch.cuda.synchronize()
+    out = torch.zeros((batch, n), dtype=torch.int16, device="cuda")
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            dl.gemv(x, out, stream=s)
+    torch.cuda.current_stream().wait_stream(s)
+    for rep in range(3):
+        out.zero_()
+        junk = torch.randn(1 << 20, device="cuda").sum()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {rep} differs"
+        del junk
+    dl.close()
+
+
+def test_mfma_rejects_on_the_host(fb):
+    layer = I.make_layer(256, 512, 1, 0, 4, seed=(102, 0, 0))
+    with pytest.raises(fb.FluxbinError):
+        fb.DeviceLayer(layer, max_batch=8, waves_per_block=8, compute=fb.COMPUTE_MFMA)
+    dl = mfma_layer(fb, layer, 8)
+    x = torch.zeros((9, 512), dtype=torch.int16, device="cuda")
+    y = torch.zeros((9, 256), dtype=torch.int16, device="cuda")
+    with pytest.raises(fb.FluxbinError):
+        dl.gemv(x, y)  # batch above max_batch
+    dl.close()
