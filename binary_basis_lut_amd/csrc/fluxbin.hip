@@ -154,13 +154,8 @@ int32_t batch_group(int32_t g, int64_t max_batch) {
 
 int entry_bytes(const fluxbin_layer_desc *d) { return d->table_precision == FLUXBIN_TABLE_F16 ? 2 : 4; }
 
-// Matrix-core route: ranges of cpb chunks inside one segment, 128 rows per
-// workgroup at the widest batch.  Automatic cpb: the most chunks per range
-// that still give kMfmaTargetBlocks workgroups, about one and a half per CU
-// (fewer, longer ranges mean fewer partial sums to store and add; measured on
-// MI355X over the 7B MLP shapes at batches 32 and 128).
-constexpr int64_t kMfmaTargetBlocks = 384;
-
+// Matrix-core route: ranges of cpb chunks inside one segment (automatic cpb:
+// mfma_auto_cpb, next to the kernel).
 fluxbin_status make_mfma_plan(const fluxbin_layer_desc *d, Plan *p) {
   // x is addressed with 32-bit element offsets: batch row * k + column
   if (d->max_batch * d->k > (int64_t)INT32_MAX - kChunkCols)
@@ -175,10 +170,7 @@ fluxbin_status make_mfma_plan(const fluxbin_layer_desc *d, Plan *p) {
   auto splits_for = [&](int32_t c) { return d->kb * (int32_t)cdiv(nc_g, c) + d->ks * (int32_t)cdiv(nc_s, c); };
   int32_t cpb = d->chunks_per_block;
   if (!cpb) {
-    cpb = 1;
-    while (cpb < kMaxCpb && splits_for(cpb) > 1 &&
-           (int64_t)p->row_blocks * splits_for(cpb * 2) >= kMfmaTargetBlocks)
-      cpb *= 2;
+    cpb = mfma_auto_cpb(p->row_blocks, d->kb, nc_g, d->ks, nc_s, d->max_batch);
     while (splits_for(cpb) > kMaxSplits && cpb < kMaxCpb) ++cpb;
   }
   p->cpb = cpb;
@@ -717,17 +709,14 @@ fluxbin_status fluxbin_build_lut(fluxbin_handle h, const uint16_t *x, int64_t ba
 
 namespace {
 
-// The matrix-core route: the narrowest instance that covers the batch in one
-// workgroup along y (32, 64 or 128 rows: waves of 64 weight rows x 32 or 64
-// batch rows, four along the weight rows, or two x two).  The per-element
-// arithmetic does not depend on the instance.
+// The matrix-core route (instance for the batch: mfma_instance, next to the
+// kernel; the per-element arithmetic does not depend on it).
 fluxbin_status mfma_gemv(fluxbin_handle h, const uint16_t *x, uint16_t *y, int64_t batch, hipStream_t stream) {
   const fluxbin_layer_desc &d = h->d;
   const Plan &p = h->plan;
-  const int nbt = batch <= 32 ? 1 : 2, wb = batch <= 64 ? 1 : 2;
-  mfma_fn fn = mfma_pick(nbt, wb, d.row_group ? 1 : 0);
-  if (!fn) return fail(FLUXBIN_ERR_UNSUPPORTED, "no matrix-core kernel for %d x %d batch blocks", nbt, wb);
-  const int64_t rows_per_block = (int64_t)(kMfmaWaves / wb) * kTileRows;
+  const MfmaInstance in = mfma_instance(batch, d.row_group ? 1 : 0);
+  if (!in.fn) return fail(FLUXBIN_ERR_UNSUPPORTED, "no matrix-core kernel for batch %lld", (long long)batch);
+  const int64_t rows_per_block = (int64_t)(kMfmaWaves / in.wb) * kTileRows;
   MfmaArgs a;
   a.L = layer_args(d);
   a.idx_or_dummy = h->idx_or_dummy;
@@ -747,8 +736,8 @@ fluxbin_status mfma_gemv(fluxbin_handle h, const uint16_t *x, uint16_t *y, int64
   a.batch = (int32_t)batch;
   a.xvec = d.k % 8 == 0 && aligned(x, 16) && aligned(d.c_global, 16) ? 1 : 0;
   a.sal_group = d.row_group && d.ks > 0 ? d.sal_group : kChunkCols;
-  const dim3 grid((unsigned)((int64_t)a.row_blocks * p.splits), (unsigned)cdiv(batch, 32 * nbt * wb));
-  hipLaunchKernelGGL(fn, grid, dim3(kMfmaWaves * 64), 0, stream, a);
+  const dim3 grid((unsigned)((int64_t)a.row_blocks * p.splits), (unsigned)cdiv(batch, 32 * in.nbt * in.wb));
+  hipLaunchKernelGGL(in.fn, grid, dim3(kMfmaWaves * 64), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "matrix-core gemv launch");
   if (p.splits > 1) {

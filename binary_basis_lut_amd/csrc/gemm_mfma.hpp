@@ -73,10 +73,21 @@ struct MfmaArgs {
 
 typedef void (*mfma_fn)(const MfmaArgs);
 
-// Kernel instance for NBT 32-row batch blocks per wave (1 or 2), WB waves
-// along the batch (1 or 2; the other 4 / WB waves along the rows, 64 rows
-// each) and row-scale format rs (0 per row, 1 block-wise), or nullptr.
-mfma_fn mfma_pick(int nbt, int wb, int rs);
+// A kernel instance: NBT 32-row batch blocks per wave, WB waves along the
+// batch (the other 4 / WB waves along the weight rows, 64 rows each).
+struct MfmaInstance {
+  mfma_fn fn;
+  int nbt, wb;
+};
+
+// The instance for a call of `batch` rows (1..128) with row-scale format rs
+// (0 per row, 1 block-wise); fn is nullptr outside that range.
+MfmaInstance mfma_instance(int64_t batch, int rs);
+
+// Automatic chunks per range for a layer of row_blocks 128-row blocks, kb / ks
+// segments of nc_g / nc_s chunks, and calls of at most max_batch rows.
+int32_t mfma_auto_cpb(int32_t row_blocks, int32_t kb, int32_t nc_g, int32_t ks, int32_t nc_s, int64_t max_batch);
+
 
 // B operand of one k-step: the 8 column scales c8 with the sign of each
 // flipped where its weight bit is clear.  `neg` holds the 8 inverted bits
