@@ -176,3 +176,31 @@ def test_mfma_rejects_on_the_host(fb):
     with pytest.raises(fb.FluxbinError):
         dl.gemv(x, y)  # batch above max_batch
     dl.close()
+
+
+@pytest.mark.parametrize("compute", ["lut", "mfma"])
+def test_unaligned_x_gives_the_same_result(fb, orc, compute):
+    """x starting 2 bytes past a 16-byte boundary: the matrix-core route stages it element by
+    element (no 16-byte loads); both routes give the bits of the aligned call."""
+    n, k, batch = 300, 1024, 20
+    note(f"unaligned x, {compute}: n={n} k={k} batch={batch}")
+    layer = I.make_layer(n, k, 2, 1, 4, s=64, outlier_frac=0.01, seed=(103, n, k))
+    x_np = I.make_x(layer, batch, seed=(103, n, k))
+    route = fb.COMPUTE_MFMA if compute == "mfma" else fb.COMPUTE_LUT
+    dl = fb.DeviceLayer(layer, max_batch=batch, compute=route)
+    base = torch.zeros(batch * k + 8, dtype=torch.int16, device="cuda")
+    xa = base[:batch * k].view(batch, k)
+    xu = base[1:1 + batch * k].view(batch, k)
+    assert xu.data_ptr() % 16 == 2
+    xa.copy_(torch.from_numpy(x_np.view(np.int16)))
+    ya = torch.zeros((batch, n), dtype=torch.int16, device="cuda")
+    dl.gemv(xa, ya)
+    torch.cuda.synchronize()
+    xu.copy_(torch.from_numpy(x_np.view(np.int16)))
+    yu = torch.zeros((batch, n), dtype=torch.int16, device="cuda")
+    dl.gemv(xu, yu)
+    torch.cuda.synchronize()
+    assert torch.equal(ya, yu)
+    check_y(orc, layer, x_np, yu.cpu().numpy().view(np.uint16), dl.plan,
+            steps=mfma_steps(layer, dl.plan) if compute == "mfma" else None)
+    dl.close()
