@@ -18,7 +18,7 @@ storage instead (one fp16 row scale per row per basis per 128-column group,
 two global and two salient bases, --sal-group salient columns per group:
 about 2.63 bits per weight at 8, 2.75 at 16; FluxBin summary, appendix C.2).
 
-Prints one JSON line.  Extra figures go to --out (default gpurun_out/bench_detail.json).
+Prints one JSON line.  --out FILE also writes the extra figures (per-call timings, plan) as JSON.
 """
 from __future__ import annotations
 
@@ -102,12 +102,12 @@ def main() -> int:
                     help="row-scale storage: per row per basis (default), or per row per 128-column group")
     ap.add_argument("--sal-group", type=int, default=8, choices=[8, 16],
                     help="blockwise: salient columns per 128-column group")
-    ap.add_argument("--out", default=str(ROOT / "gpurun_out" / "bench_detail.json"))
+    ap.add_argument("--out", default=None, help="also write the extra figures to this JSON file")
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported by this build "
-              "(the path would shard by output rows; see the design notes).", file=sys.stderr)
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(one GPU's share of a layer is measured; the path would shard by output rows).", file=sys.stderr)
         return 2
 
     import torch
@@ -274,11 +274,9 @@ def main() -> int:
         "traffic_note": traffic_note,
         "kernel_source_hash": kernel_source_hash(),
     })
-    try:
+    if args.out:
         Path(args.out).parent.mkdir(parents=True, exist_ok=True)
         Path(args.out).write_text(json.dumps(detail, indent=1))
-    except OSError:
-        pass
     for d in dls:
         d.close()
     return 0 if parity_ok else 3

@@ -663,8 +663,7 @@ fluxbin_status fluxbin_get_plan(fluxbin_handle h, fluxbin_plan *plan) {
   plan->row_blocks = p.row_blocks;
   plan->splits = p.splits;
   plan->total_chunks = p.total_chunks;
-  plan->lds_bytes = p.mfma ? (int32_t)((kMfmaMaxBlocks * 32 * kMfmaXStride + kChunkCols) * sizeof(uint16_t))
-                           : lds_bytes(h->d.g, p.nb, p.cpb, entry_bytes(&h->d));
+  plan->lds_bytes = p.mfma ? mfma_lds_bytes(2, 2) : lds_bytes(h->d.g, p.nb, p.cpb, entry_bytes(&h->d));
   plan->grid = (int64_t)p.row_blocks * p.splits;
   return ok();
 }

@@ -84,6 +84,12 @@ struct MfmaInstance {
 // (0 per row, 1 block-wise); fn is nullptr outside that range.
 MfmaInstance mfma_instance(int64_t batch, int rs);
 
+// Static LDS of an instance: two buffers of x ([32 * nbt * wb][kMfmaXStride]
+// fp16), c (128 fp16) and the sign words of its (4 / wb) * 64 rows.
+constexpr int mfma_lds_bytes(int nbt, int wb) {
+  return 2 * (32 * nbt * wb * kMfmaXStride * 2 + kChunkCols * 2 + (kMfmaWaves / wb) * kTileRows * 16);
+}
+
 // Automatic chunks per range for a layer of row_blocks 128-row blocks, kb / ks
 // segments of nc_g / nc_s chunks, and calls of at most max_batch rows.
 int32_t mfma_auto_cpb(int32_t row_blocks, int32_t kb, int32_t nc_g, int32_t ks, int32_t nc_s, int64_t max_batch);
@@ -121,6 +127,7 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void gemm_mfma_kernel(const MfmaAr
   constexpr int kPieces = kBatchRows / 16;      // 16-byte pieces of x per thread per chunk
   constexpr int kXHalfs = kBatchRows * kMfmaXStride;
   // Two LDS buffers of one chunk each: x [kBatchRows][kMfmaXStride], c [128], sign words [kRows]
+  static_assert(2 * (kXHalfs * 2 + kChunkCols * 2 + kRows * 16) == mfma_lds_bytes(NBT, WB), "LDS plan");
   __shared__ __attribute__((aligned(16))) uint16_t xs[2][kXHalfs];
   __shared__ __attribute__((aligned(16))) uint16_t cs[2][kChunkCols];
   __shared__ __attribute__((aligned(16))) u32x4 ws[2][kRows];

@@ -62,7 +62,7 @@ extern "C" {
 typedef enum {
   FLUXBIN_OK = 0,
   FLUXBIN_ERR_INVALID_ARGUMENT = 1, /* bad pointer, size, alignment or index list */
-  FLUXBIN_ERR_UNSUPPORTED = 2,      /* valid request this build does not implement */
+  FLUXBIN_ERR_UNSUPPORTED = 2,      /* valid request this library does not implement */
   FLUXBIN_ERR_WORKSPACE = 3,        /* workspace missing or too small */
   FLUXBIN_ERR_HIP = 4               /* a HIP runtime call failed */
 } fluxbin_status;
@@ -169,7 +169,7 @@ typedef struct {
   int32_t row_blocks;       /* workgroups along the rows */
   int32_t splits;           /* workgroups along the concatenated columns of all segments */
   int32_t total_chunks;     /* sum over segments of ceil(len/128) */
-  int32_t lds_bytes;        /* dynamic LDS per workgroup at max_batch */
+  int32_t lds_bytes;        /* LDS per workgroup at max_batch (matrix cores: of the widest instance) */
   int64_t grid;             /* workgroups per fluxbin_gemv launch */
 } fluxbin_plan;
 
