@@ -57,6 +57,8 @@ def run_gemv(args) -> None:
         else:
             lay = I.workload_layer(args.workload, args.shape, i)
             x = I.workload_x(args.workload, lay, args.batch, args.shape, i)
+        if args.g:
+            lay.g = args.g  # table width is a kernel choice: the packed sign bits do not depend on it
         dls.append(F.DeviceLayer(lay, max_batch=args.batch, chunks_per_block=args.chunks_per_block,
                                  waves_per_block=args.waves_per_block, table_precision=args.table_precision,
                                  compute=F.COMPUTE_MFMA if args.compute == "mfma" else F.COMPUTE_LUT))
@@ -197,6 +199,7 @@ def main() -> int:
     g.add_argument("--ks", type=int, default=2, help="blockwise: salient bases")
     g.add_argument("--sal-group", type=int, default=8, choices=[8, 16])
     g.add_argument("--compute", choices=["lut", "mfma"], default="lut")
+    g.add_argument("--g", type=int, default=0, choices=[0, 4, 8], help="table width (0: the workload's)")
     dp = sub.add_parser("decompose")
     dp.add_argument("--n", type=int, default=4096)
     dp.add_argument("--k", type=int, default=4096)
