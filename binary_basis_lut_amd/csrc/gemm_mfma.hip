@@ -25,10 +25,11 @@ MfmaInstance mfma_instance(int64_t batch, int rs) {
     if (batch <= 64) return {gemm_mfma_kernel<2, 1, 0>, 2, 1};
     return {gemm_mfma_kernel<2, 2, 0>, 2, 2};
   }
-  // block-wise scales fold per group into a second accumulator set: at most two blocks per wave
+  // block-wise scales fold per group into a second accumulator set: one batch block per wave, so
+  // that two waves per SIMD fit; wider batches take more waves along the batch
   if (batch <= 32) return {gemm_mfma_kernel<1, 1, 1>, 1, 1};
-  if (batch <= 64) return {gemm_mfma_kernel<2, 1, 1>, 2, 1};
-  return {gemm_mfma_kernel<2, 2, 1>, 2, 2};
+  if (batch <= 64) return {gemm_mfma_kernel<1, 2, 1>, 1, 2};
+  return {gemm_mfma_kernel<1, 4, 1>, 1, 4};
 }
 
 int32_t mfma_auto_cpb(int32_t row_blocks, int32_t kb, int32_t nc_g, int32_t ks, int32_t nc_s, int64_t max_batch) {

@@ -119,8 +119,17 @@ __device__ __forceinline__ half8_t signed_scales(uint32_t neg, u32x4 c8) {
   return __builtin_bit_cast(half8_t, v);
 }
 
+// Waves per SIMD the register allocation must leave room for: two for the
+// block-wise instances (one batch block per wave; their second accumulator
+// set would otherwise take them to one wave per SIMD), no constraint else.
 template <int NBT, int WB, int RS>
-__global__ __launch_bounds__(kMfmaWaves * 64) void gemm_mfma_kernel(const MfmaArgs a) {
+struct MfmaWavesPerEu {
+  static constexpr int value = RS == 1 ? 2 : 1;
+};
+
+template <int NBT, int WB, int RS>
+__global__ __launch_bounds__(kMfmaWaves * 64) __attribute__((amdgpu_waves_per_eu(MfmaWavesPerEu<NBT, WB, RS>::value)))
+void gemm_mfma_kernel(const MfmaArgs a) {
   constexpr int WR = kMfmaWaves / WB;           // waves along the rows
   constexpr int kRows = WR * kTileRows;         // weight rows of the workgroup
   constexpr int kBatchRows = 32 * NBT * WB;     // staged batch rows
@@ -262,8 +271,9 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void gemm_mfma_kernel(const MfmaAr
 #pragma unroll
     for (int d = 0; d < 4; ++d) st.c[d] = h[2 * d] | (h[2 * d + 1] << 16);
   };
-  // block-wise scales of the chunk being multiplied (fp16), per lane row
-  uint16_t rq[2][16];
+  // block-wise scales of the chunk being multiplied, per lane row: fp16 pairs,
+  // scale q in half (q & 1) of word (q / 2) of rqa (q < 8) or rqb
+  u32x4 rqa[2], rqb[2];
   auto publish = [&](const Stage &st, int buf) {
 #pragma unroll
     for (int i = 0; i < kPieces; ++i) *(u32x4 *)&xs[buf][((tid >> 4) + 16 * i) * kMfmaXStride + pcol] = st.x[i];
@@ -272,13 +282,8 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void gemm_mfma_kernel(const MfmaAr
     if constexpr (RS == 1) {
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          rq[i][2 * d] = (uint16_t)st.r0[i][d];
-          rq[i][2 * d + 1] = (uint16_t)(st.r0[i][d] >> 16);
-          rq[i][8 + 2 * d] = (uint16_t)st.r1[i][d];
-          rq[i][8 + 2 * d + 1] = (uint16_t)(st.r1[i][d] >> 16);
-        }
+        rqa[i] = st.r0[i];
+        rqb[i] = st.r1[i];
       }
     }
   };
@@ -309,13 +314,11 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void gemm_mfma_kernel(const MfmaAr
     u32x4 nw[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) nw[i] = ~ws[buf][wr * kTileRows + 32 * i + m];
-    uint16_t rc[2][16];
-    if constexpr (RS == 1) {
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int q = 0; q < 16; ++q) rc[i][q] = rq[i][q];
-    }
+    // block-wise scale q of lane row i (q a compile-time index after unrolling)
+    auto rscale = [&](int i, int q) {
+      const uint32_t w = q < 8 ? rqa[i][(q >> 1) & 3] : rqb[i][(q >> 1) & 3];
+      return h2f((uint16_t)(w >> (16 * (q & 1))));
+    };
 #pragma unroll
     for (int t = 0; t < kChunkCols / 16; ++t) {
       const int kc = 16 * t + 8 * kq;  // this lane's 8 columns of the k-step
@@ -336,20 +339,20 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void gemm_mfma_kernel(const MfmaAr
 #pragma unroll
             for (int j = 0; j < NBT; ++j)
               acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(aop[j], bh, acc[i][j], 0, 0, 0);
-            fold(i, cis * kChunkCols + 16 * t + 8 * h < len ? h2f(rc[i][2 * t + h]) : 0.0f);
+            fold(i, cis * kChunkCols + 16 * t + 8 * h < len ? rscale(i, 2 * t + h) : 0.0f);
           }
         } else {
 #pragma unroll
           for (int j = 0; j < NBT; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(aop[j], bop, acc[i][j], 0, 0, 0);
           // 16-column groups: one per k-step (groups past the segment's end may hold any scale)
-          if (RS == 1 && S.salient) fold(i, cis * kChunkCols + 16 * t < len ? h2f(rc[i][t]) : 0.0f);
+          if (RS == 1 && S.salient) fold(i, cis * kChunkCols + 16 * t < len ? rscale(i, t) : 0.0f);
         }
       }
     }
     if (RS == 1 && !S.salient) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i) fold(i, h2f(rc[i][0]));
+      for (int i = 0; i < 2; ++i) fold(i, rscale(i, 0));
     }
   };
 
