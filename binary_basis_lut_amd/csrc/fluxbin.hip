@@ -663,7 +663,7 @@ fluxbin_status fluxbin_get_plan(fluxbin_handle h, fluxbin_plan *plan) {
   plan->row_blocks = p.row_blocks;
   plan->splits = p.splits;
   plan->total_chunks = p.total_chunks;
-  plan->lds_bytes = p.mfma ? mfma_lds_bytes(2, 2) : lds_bytes(h->d.g, p.nb, p.cpb, entry_bytes(&h->d));
+  plan->lds_bytes = p.mfma ? mfma_lds_bytes(2, 2, 2) : lds_bytes(h->d.g, p.nb, p.cpb, entry_bytes(&h->d));
   plan->grid = (int64_t)p.row_blocks * p.splits;
   return ok();
 }
@@ -715,7 +715,7 @@ fluxbin_status mfma_gemv(fluxbin_handle h, const uint16_t *x, uint16_t *y, int64
   const Plan &p = h->plan;
   const MfmaInstance in = mfma_instance(batch, d.row_group ? 1 : 0);
   if (!in.fn) return fail(FLUXBIN_ERR_UNSUPPORTED, "no matrix-core kernel for batch %lld", (long long)batch);
-  const int64_t rows_per_block = (int64_t)(kMfmaWaves / in.wb) * kTileRows;
+  const int64_t rows_per_block = (int64_t)(kMfmaWaves / in.wb) * 32 * in.rb;
   MfmaArgs a;
   a.L = layer_args(d);
   a.idx_or_dummy = h->idx_or_dummy;

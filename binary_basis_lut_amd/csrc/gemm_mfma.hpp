@@ -21,16 +21,17 @@
 // and the 16 batch rows 8 * (v / 4) + 4 * (l / 32) + (v mod 4), v < 16, so
 // each lane scales its 16 sums by one row scale.
 //
-// Work division: a wave covers 64 weight rows (one tile of the sign-word
-// layout, two 32-row MFMA blocks) x 32 * NBT batch rows, so each x fragment
-// read from LDS feeds two MFMAs and each expanded sign operand NBT of them.
-// A workgroup of 4 waves (WB along the batch, 4 / WB along the rows) covers
-// 256 / WB rows x 32 * NBT * WB batch rows x a range of at most cpb
-// 128-column chunks of ONE segment.  Per chunk the workgroup stages the
-// chunk's columns of x (gathered through S for a salient segment) and of c in
-// LDS, zero past the segment's end.  Ranges that cover the same rows add
-// their scaled partials in fp32, summed in range order by a second kernel
-// (plain stores and loads: no atomics, a fixed order of addition).
+// Work division: a wave covers 32 * RB weight rows (RB = 2: one tile of the
+// sign-word layout, so each x fragment read from LDS feeds two MFMAs; RB = 1:
+// half a tile, twice the workgroups) x 32 * NBT batch rows, each expanded
+// sign operand feeding NBT MFMAs.  A workgroup of 4 waves (WB along the
+// batch, 4 / WB along the rows) covers (4 / WB) * 32 * RB rows x 32 * NBT * WB
+// batch rows x a range of at most cpb 128-column chunks of ONE segment.  Per
+// chunk the workgroup stages the chunk's columns of x (gathered through S for
+// a salient segment), its column scales and its sign words in LDS, zero past
+// the segment's end.  Ranges that cover the same rows add their scaled
+// partials in fp32, summed in range order by a second kernel (plain stores
+// and loads: no atomics, a fixed order of addition).
 //
 // Row scales: per row (RS = 0), applied once to the range's sum; block-wise
 // (RS = 1), per 128-column group for the global bases (after every chunk)
@@ -73,11 +74,11 @@ struct MfmaArgs {
 
 typedef void (*mfma_fn)(const MfmaArgs);
 
-// A kernel instance: NBT 32-row batch blocks per wave, WB waves along the
-// batch (the other 4 / WB waves along the weight rows, 64 rows each).
+// A kernel instance: NBT 32-row batch blocks and RB 32-row blocks of weight
+// rows per wave, WB waves along the batch (the other 4 / WB along the rows).
 struct MfmaInstance {
   mfma_fn fn;
-  int nbt, wb;
+  int nbt, wb, rb;
 };
 
 // The instance for a call of `batch` rows (1..128) with row-scale format rs
@@ -85,9 +86,9 @@ struct MfmaInstance {
 MfmaInstance mfma_instance(int64_t batch, int rs);
 
 // Static LDS of an instance: two buffers of x ([32 * nbt * wb][kMfmaXStride]
-// fp16), c (128 fp16) and the sign words of its (4 / wb) * 64 rows.
-constexpr int mfma_lds_bytes(int nbt, int wb) {
-  return 2 * (32 * nbt * wb * kMfmaXStride * 2 + kChunkCols * 2 + (kMfmaWaves / wb) * kTileRows * 16);
+// fp16), c (128 fp16) and the sign words of its (4 / wb) * 32 * rb rows.
+constexpr int mfma_lds_bytes(int nbt, int wb, int rb) {
+  return 2 * (32 * nbt * wb * kMfmaXStride * 2 + kChunkCols * 2 + (kMfmaWaves / wb) * 32 * rb * 16);
 }
 
 // Automatic chunks per range for a layer of row_blocks 128-row blocks, kb / ks
@@ -122,21 +123,23 @@ __device__ __forceinline__ half8_t signed_scales(uint32_t neg, u32x4 c8) {
 // Waves per SIMD the register allocation must leave room for: two for the
 // block-wise instances (one batch block per wave; their second accumulator
 // set would otherwise take them to one wave per SIMD), no constraint else.
-template <int NBT, int WB, int RS>
+template <int NBT, int WB, int RB, int RS>
 struct MfmaWavesPerEu {
   static constexpr int value = RS == 1 ? 2 : 1;
 };
 
-template <int NBT, int WB, int RS>
-__global__ __launch_bounds__(kMfmaWaves * 64) __attribute__((amdgpu_waves_per_eu(MfmaWavesPerEu<NBT, WB, RS>::value)))
-void gemm_mfma_kernel(const MfmaArgs a) {
+template <int NBT, int WB, int RB, int RS>
+__global__ __launch_bounds__(kMfmaWaves * 64)
+__attribute__((amdgpu_waves_per_eu(MfmaWavesPerEu<NBT, WB, RB, RS>::value))) void gemm_mfma_kernel(const MfmaArgs a) {
+  static_assert(RB == 1 || RB == 2, "a wave covers 32 or 64 weight rows");
   constexpr int WR = kMfmaWaves / WB;           // waves along the rows
-  constexpr int kRows = WR * kTileRows;         // weight rows of the workgroup
+  constexpr int kWaveRows = 32 * RB;            // weight rows per wave
+  constexpr int kRows = WR * kWaveRows;         // weight rows of the workgroup
   constexpr int kBatchRows = 32 * NBT * WB;     // staged batch rows
   constexpr int kPieces = kBatchRows / 16;      // 16-byte pieces of x per thread per chunk
   constexpr int kXHalfs = kBatchRows * kMfmaXStride;
   // Two LDS buffers of one chunk each: x [kBatchRows][kMfmaXStride], c [128], sign words [kRows]
-  static_assert(2 * (kXHalfs * 2 + kChunkCols * 2 + kRows * 16) == mfma_lds_bytes(NBT, WB), "LDS plan");
+  static_assert(2 * (kXHalfs * 2 + kChunkCols * 2 + kRows * 16) == mfma_lds_bytes(NBT, WB, RB), "LDS plan");
   __shared__ __attribute__((aligned(16))) uint16_t xs[2][kXHalfs];
   __shared__ __attribute__((aligned(16))) uint16_t cs[2][kChunkCols];
   __shared__ __attribute__((aligned(16))) u32x4 ws[2][kRows];
@@ -191,19 +194,24 @@ void gemm_mfma_kernel(const MfmaArgs a) {
 #pragma unroll
   for (int i = 0; i < kPieces; ++i) xoff[i] = min(b0 + (tid >> 4) + 16 * i, batch - 1) * (int)L.k + pcol;
   const int wrow = min(tid, kRows - 1);         // workgroup row whose sign words this thread stages
-  const int wtile = min((rb * kRows + wrow) / kTileRows, a.row_tiles - 1);
-  const int64_t woff = (int64_t)wtile * nc * kTileRows + (wrow % kTileRows);
+  const int wgrow = rb * kRows + wrow;          // its global row
+  const int wtile = min(wgrow / kTileRows, a.row_tiles - 1);
+  const int64_t woff = (int64_t)wtile * nc * kTileRows + (wgrow % kTileRows);
 
-  // This wave's 64 weight rows (one tile); the lane holds rows 32 i + m.
-  const int row0 = (rb * WR + wr) * kTileRows;
+  // This wave's 32 * RB weight rows (a tile of the sign-word layout, or half
+  // of one); the lane holds rows 32 i + m of them.
+  const int row0 = (rb * WR + wr) * kWaveRows;
   const int tile = min(row0 / kTileRows, a.row_tiles - 1);
+  const int trow0 = row0 % kTileRows;           // 0, or 32 for the second half of a tile
   const int wbat = b0 + wb * NBT * 32;          // first batch row of this wave
-  const int64_t roff0 = ((int64_t)tile * nc * kTileRows + m) * gpc;  // block-wise scales of row m, chunk 0
+  const int64_t roff0 = ((int64_t)tile * nc * kTileRows + trow0 + m) * gpc;  // block-wise scales, chunk 0
   // per-row scales of the lane's two rows, loaded now so the epilogue does not wait for them
-  float rrow[2] = {1.0f, 1.0f};
+  float rrow[RB];
+#pragma unroll
+  for (int i = 0; i < RB; ++i) rrow[i] = 1.0f;
   if constexpr (RS == 0) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < RB; ++i) {
       const int row = row0 + 32 * i + m;
       rrow[i] = h2f(rbase[min(row, (int)L.n - 1)]);
     }
@@ -211,7 +219,7 @@ void gemm_mfma_kernel(const MfmaArgs a) {
 
   struct Stage {
     u32x4 x[kPieces];
-    u32x4 c, w, r0[2], r1[2];
+    u32x4 c, w, r0[RB], r1[RB];
   };
   // Loads of chunk cis.  A full chunk of a global segment (the common case)
   // takes 16-byte loads and no branch; one that reaches past the segment's
@@ -223,7 +231,7 @@ void gemm_mfma_kernel(const MfmaArgs a) {
     if constexpr (RS == 1) {
       const FB_GLOBAL uint16_t *rp = rbase + roff0 + (int64_t)cis * kTileRows * gpc;
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
+      for (int i = 0; i < RB; ++i) {
         const FB_GLOBAL uint16_t *ri = rp + 32 * i * gpc;
         if (S.salient) {
           st.r0[i] = *(const FB_GLOBAL u32x4 *)ri;
@@ -273,7 +281,7 @@ void gemm_mfma_kernel(const MfmaArgs a) {
   };
   // block-wise scales of the chunk being multiplied, per lane row: fp16 pairs,
   // scale q in half (q & 1) of word (q / 2) of rqa (q < 8) or rqb
-  u32x4 rqa[2], rqb[2];
+  u32x4 rqa[RB], rqb[RB];
   auto publish = [&](const Stage &st, int buf) {
 #pragma unroll
     for (int i = 0; i < kPieces; ++i) *(u32x4 *)&xs[buf][((tid >> 4) + 16 * i) * kMfmaXStride + pcol] = st.x[i];
@@ -281,7 +289,7 @@ void gemm_mfma_kernel(const MfmaArgs a) {
     if (tid < kRows) ws[buf][tid] = st.w;
     if constexpr (RS == 1) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
+      for (int i = 0; i < RB; ++i) {
         rqa[i] = st.r0[i];
         rqb[i] = st.r1[i];
       }
@@ -290,10 +298,10 @@ void gemm_mfma_kernel(const MfmaArgs a) {
 
   // acc[i][j]: rows (32 i + .) of the wave, batch block j.  Block-wise scales
   // fold each group's sum into out; per-row scales multiply acc once at the end.
-  f32x16 acc[2][NBT];
-  f32x16 out[2][RS == 1 ? NBT : 1];
+  f32x16 acc[RB][NBT];
+  f32x16 out[RB][RS == 1 ? NBT : 1];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < RB; ++i) {
 #pragma unroll
     for (int j = 0; j < NBT; ++j) acc[i][j] = f32x16{};
 #pragma unroll
@@ -311,9 +319,9 @@ void gemm_mfma_kernel(const MfmaArgs a) {
   };
 
   auto compute = [&](int cis, int buf) {
-    u32x4 nw[2];
+    u32x4 nw[RB];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) nw[i] = ~ws[buf][wr * kTileRows + 32 * i + m];
+    for (int i = 0; i < RB; ++i) nw[i] = ~ws[buf][wr * kWaveRows + 32 * i + m];
     // block-wise scale q of lane row i (q a compile-time index after unrolling)
     auto rscale = [&](int i, int q) {
       const uint32_t w = q < 8 ? rqa[i][(q >> 1) & 3] : rqb[i][(q >> 1) & 3];
@@ -328,7 +336,7 @@ void gemm_mfma_kernel(const MfmaArgs a) {
       for (int j = 0; j < NBT; ++j)
         aop[j] = *(const half8_t *)&xs[buf][((wb * NBT + j) * 32 + m) * kMfmaXStride + kc];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
+      for (int i = 0; i < RB; ++i) {
         const uint32_t neg = (nw[i][t >> 1] >> (16 * (t & 1) + 8 * kq)) & 0xffu;
         const half8_t bop = signed_scales(neg, c8);
         if (RS == 1 && S.salient && gpc == 16) {
@@ -352,7 +360,7 @@ void gemm_mfma_kernel(const MfmaArgs a) {
     }
     if (RS == 1 && !S.salient) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i) fold(i, rscale(i, 0));
+      for (int i = 0; i < RB; ++i) fold(i, rscale(i, 0));
     }
   };
 
@@ -380,7 +388,7 @@ void gemm_mfma_kernel(const MfmaArgs a) {
   // to part[range][batch row][n_pad], added in range order by the finalize
   // kernel (a fixed order, so repeated calls agree bit for bit).
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < RB; ++i) {
     const int row = row0 + 32 * i + m;
     if (row >= L.n) continue;
     const float r = rrow[i];  // per-row scale of the range's sum (1 when block-wise)
