@@ -48,6 +48,7 @@ bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 constexpr int kTargetBlocks = 1024;  // about four workgroups per CU
+constexpr int64_t kWideWork = 32768;  // row tiles x chunks from which per-row layers take 8 waves
 
 struct Plan {
   int32_t waves;       // waves per workgroup (64 rows each)
@@ -129,10 +130,17 @@ fluxbin_status validate_shape(const fluxbin_layer_desc *d) {
 // table build, more workgroups hide latency), at least 2 chunks, a power of
 // two up to 8 and a multiple of 8 above (the prefetch depths), within the
 // LDS and register budget (cmax) and the split limit.
-int32_t auto_cpb(int32_t cmax, int32_t waves, int64_t row_tiles, int32_t total_chunks) {
+//
+// Eight-wave g = 4 workgroups take at most 7 chunks: the depth-4 instance
+// that serves them holds 58 VGPRs (8 waves per SIMD) against 78 (6 waves)
+// for depth 8, and on the 70B gate+up projection (8192 -> 57344) 7-chunk
+// ranges ran 34.7 us against 37.8 us for 8-chunk ones.
+int32_t auto_cpb(int32_t g, int32_t cmax, int32_t waves, int64_t row_tiles, int32_t total_chunks) {
   int64_t c = (int64_t)row_tiles * total_chunks / ((int64_t)waves * kTargetBlocks);
   c = std::max<int64_t>(c, 2);
-  if (c <= 8) {
+  if (g == 4 && waves == 8 && c > 7) {
+    c = 7;
+  } else if (c <= 8) {
     int64_t p = 1;
     while (p * 2 <= c) p *= 2;
     c = p;
@@ -198,15 +206,21 @@ fluxbin_status make_plan(const fluxbin_layer_desc *d, Plan *p) {
     p->waves = d->waves_per_block;
   } else {
     // eight waves (512 rows) halve the per-row share of the table build: for
-    // the large g = 8 tables, and for very tall layers (measured on MI355X)
-    p->waves = (d->g == 8 || p->row_tiles >= 512) ? 8 : 4;
+    // the large g = 8 tables, for very tall layers, and for large layers with
+    // per-row scales (measured on MI355X: the 70B down projection, 128 row
+    // tiles x 455 chunks, ran 20.4-21.5 us with 8 waves against 21.5-22.9
+    // with 4, but 27.0 against 25.1-26.5 with block-wise scales; q_proj and
+    // the 70B qkv / o shapes, 4 200 - 21 000 tile-chunks, are as fast or
+    // faster with 4)
+    const bool wide = !d->row_group && (int64_t)p->row_tiles * p->total_chunks >= kWideWork;
+    p->waves = (d->g == 8 || p->row_tiles >= 512 || wide) ? 8 : 4;
   }
   const int32_t cmax = cpb_cap(d->g, p->nb, p->waves, entry_bytes(d));
   if (d->chunks_per_block > cmax)
     return fail(FLUXBIN_ERR_UNSUPPORTED, "chunks_per_block = %d exceeds %d for g = %d, max_batch = %lld, %d waves",
                 d->chunks_per_block, cmax, d->g, (long long)d->max_batch, p->waves);
   p->row_blocks = (int32_t)cdiv(p->row_tiles, p->waves);
-  p->cpb = d->chunks_per_block ? d->chunks_per_block : auto_cpb(cmax, p->waves, p->row_tiles, p->total_chunks);
+  p->cpb = d->chunks_per_block ? d->chunks_per_block : auto_cpb(d->g, cmax, p->waves, p->row_tiles, p->total_chunks);
   p->pf = prefetch_depth(p->cpb);
   if (d->row_group) {
     // block-wise: global and salient chunks take separate workgroup ranges
