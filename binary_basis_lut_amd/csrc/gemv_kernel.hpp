@@ -19,8 +19,18 @@ namespace fluxbin {
 // Tensor Core notes, section 3.1.3): each entry is summed in fp32 as before
 // and rounded to fp16 once, halving the tables' LDS; lookups add the fp16
 // entry into the fp32 accumulator with one v_fma_mix_f32.
+//
+//
+// Block-wise single-row g = 4 instances of prefetch depth 2 and 4 (the decode
+// plans) are held to 6 waves per SIMD (at most 80 VGPRs): left alone the
+// compiler keeps the salient lookup loop's 32-byte scale slots and expanded
+// scales live at once, 83-111 VGPRs, which caps every workgroup of the call,
+// global or salient, at 4-5 waves.  These instances need no spills for it;
+// depth 8, wider batches and g = 8 would spill and are left alone.
 template <int G, int NB, int WAVES, int PF, int RS, int TQ>
-__global__ __launch_bounds__(WAVES * 64) void lut_gemv_kernel(const GemvArgs a) {
+__global__ __launch_bounds__(WAVES * 64)
+__attribute__((amdgpu_waves_per_eu(G == 4 && NB == 1 && RS == 1 && PF <= 4 ? 6 : 1)))
+void lut_gemv_kernel(const GemvArgs a) {
   constexpr int NT = WAVES * 64;
   constexpr int SUB = kChunkCols / G;      // sub-vectors per chunk
   constexpr int TAB = 1 << G;              // full table entries
