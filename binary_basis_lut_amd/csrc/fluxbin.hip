@@ -173,12 +173,12 @@ fluxbin_status make_mfma_plan(const fluxbin_layer_desc *d, Plan *p) {
   p->nb = 0;
   p->pf = 0;
   p->waves = kMfmaWaves;
-  p->row_blocks = (int32_t)cdiv(d->n, 2 * kTileRows);  // at the widest batch: 128 rows per workgroup
+  p->row_blocks = (int32_t)cdiv(d->n, kMfmaRowsPerBlock);
   const int32_t nc_g = (int32_t)cdiv(d->k, kChunkCols), nc_s = d->ks > 0 ? (int32_t)cdiv(d->s, kChunkCols) : 0;
   auto splits_for = [&](int32_t c) { return d->kb * (int32_t)cdiv(nc_g, c) + d->ks * (int32_t)cdiv(nc_s, c); };
   int32_t cpb = d->chunks_per_block;
   if (!cpb) {
-    cpb = mfma_auto_cpb(p->row_blocks, d->kb, nc_g, d->ks, nc_s, d->max_batch);
+    cpb = mfma_auto_cpb((int32_t)cdiv(d->n, 2 * kTileRows), d->kb, nc_g, d->ks, nc_s, d->max_batch);
     while (splits_for(cpb) > kMaxSplits && cpb < kMaxCpb) ++cpb;
   }
   p->cpb = cpb;
@@ -672,12 +672,12 @@ fluxbin_status fluxbin_destroy(fluxbin_handle h) {
 fluxbin_status fluxbin_get_plan(fluxbin_handle h, fluxbin_plan *plan) {
   if (!h || !plan) return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "NULL argument");
   const Plan &p = h->plan;
-  plan->rows_per_block = p.mfma ? 2 * kTileRows : p.waves * kTileRows;  // matrix cores: at batches above 64
+  plan->rows_per_block = p.mfma ? kMfmaRowsPerBlock : p.waves * kTileRows;
   plan->chunks_per_block = p.cpb;
   plan->row_blocks = p.row_blocks;
   plan->splits = p.splits;
   plan->total_chunks = p.total_chunks;
-  plan->lds_bytes = p.mfma ? mfma_lds_bytes(2, 2, 2) : lds_bytes(h->d.g, p.nb, p.cpb, entry_bytes(&h->d));
+  plan->lds_bytes = p.mfma ? mfma_lds_bytes(1, 1, 2) : lds_bytes(h->d.g, p.nb, p.cpb, entry_bytes(&h->d));
   plan->grid = (int64_t)p.row_blocks * p.splits;
   return ok();
 }

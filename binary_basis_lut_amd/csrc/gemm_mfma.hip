@@ -7,8 +7,8 @@ namespace fluxbin {
 namespace {
 
 // Automatic range length: 8 chunks for handles of at most 32 batch rows, 16
-// above, doubled while the grid keeps at least kMfmaPlentyBlocks workgroups of
-// 128 rows (very tall layers: fewer partial sums to store and add).  Measured
+// above, doubled while at least kMfmaPlentyBlocks 128-row blocks times
+// ranges remain (very tall layers: fewer partial sums to store and add).  Measured
 // on MI355X on the 7B shapes: q_proj 4096x4096 17.5 / 39.6 us at b = 32 / 128
 // with 8 / 16 chunks (20.2 / 58.3 with 4, 32.5 / 50.3 with 32); the MLP
 // projections within 5 % of their best.
@@ -20,18 +20,16 @@ int32_t ceil_div(int32_t a, int32_t b) { return (a + b - 1) / b; }
 
 MfmaInstance mfma_instance(int64_t batch, int rs) {
   if (batch < 1 || batch > 32 * kMfmaMaxBlocks) return {nullptr, 0, 0, 0};
-  if (rs == 0) {
-    if (batch <= 32) return {gemm_mfma_kernel<1, 1, 2, 0>, 1, 1, 2};
-    // 32 weight rows per wave here: twice the workgroups of 64 (q_proj 4096x4096 at b = 64:
-    // 23.5 against 28.2 us; the MLP projections within 3 %)
-    if (batch <= 64) return {gemm_mfma_kernel<2, 1, 1, 0>, 2, 1, 1};
-    return {gemm_mfma_kernel<2, 2, 2, 0>, 2, 2, 2};
-  }
-  // block-wise scales fold per group into a second accumulator set: one batch block per wave, so
-  // that two waves per SIMD fit; wider batches take more waves along the batch
-  if (batch <= 32) return {gemm_mfma_kernel<1, 1, 2, 1>, 1, 1, 2};
-  if (batch <= 64) return {gemm_mfma_kernel<1, 2, 2, 1>, 1, 2, 2};
-  return {gemm_mfma_kernel<1, 4, 2, 1>, 1, 4, 2};
+  // One instance for every batch: a wave multiplies 64 weight rows by 32 batch rows, a workgroup
+  // 256 by 32, and wider batches run as more workgroups along the batch.  Instances that stage 64
+  // or 128 batch rows per workgroup expand each weight bit for more batch rows but give fewer
+  // workgroups and waves to hide the staging; measured on MI355X they were slower or level at
+  // every batch of 32..128 rows (q_proj 4096x4096 at b = 96 / 128: 23.7 / 29.6 us against
+  // 37.9 / 39.6 us; 11008 -> 4096 at b = 128: 51.9 against 58.4 us; block-wise s8 at b = 128:
+  // q_proj 66.8 against 75.6 us, 11008 -> 4096 139 against 205 us).
+  static_assert(kMfmaRowsPerBlock == kMfmaWaves * 32 * 2, "rows per workgroup of the instance");
+  if (rs == 0) return {gemm_mfma_kernel<1, 1, 2, 0>, 1, 1, 2};
+  return {gemm_mfma_kernel<1, 1, 2, 1>, 1, 1, 2};
 }
 
 int32_t mfma_auto_cpb(int32_t row_blocks, int32_t kb, int32_t nc_g, int32_t ks, int32_t nc_s, int64_t max_batch) {

@@ -46,6 +46,7 @@ namespace fluxbin {
 
 constexpr int kMfmaWaves = 4;
 constexpr int kMfmaMaxBlocks = 4;               // 32-row batch blocks per workgroup (NBT * WB)
+constexpr int kMfmaRowsPerBlock = 256;          // weight rows per workgroup of the instance in use
 constexpr int kMfmaXStride = kChunkCols + 8;    // halfs per staged batch row: 272 B, conflict-free 16-B reads
 
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
@@ -82,7 +83,9 @@ struct MfmaInstance {
 };
 
 // The instance for a call of `batch` rows (1..128) with row-scale format rs
-// (0 per row, 1 block-wise); fn is nullptr outside that range.
+// (0 per row, 1 block-wise); fn is nullptr outside that range.  The same
+// instance serves every batch (NBT = WB = 1, RB = 2: kMfmaRowsPerBlock
+// weight rows by 32 batch rows per workgroup).
 MfmaInstance mfma_instance(int64_t batch, int rs);
 
 // Static LDS of an instance: two buffers of x ([32 * nbt * wb][kMfmaXStride]
@@ -367,7 +370,7 @@ __attribute__((amdgpu_waves_per_eu(MfmaWavesPerEu<NBT, WB, RB, RS>::value))) voi
   // Pipeline: chunk u is multiplied from LDS buffer u % 2 while the loads of
   // chunk u + 1 are in flight; they are published to the other buffer after
   // the multiply, then one barrier, then the loads of chunk u + 2 start.  (A
-  // second register set in flight costs the wide instance its second wave
+  // second register set in flight cost the widest instance its second wave
   // per SIMD, and was measured slower.)
   Stage st;
   stage(c0, st);

@@ -163,14 +163,13 @@ typedef struct {
 
 /* How a handle splits the work (read-only introspection). */
 typedef struct {
-  int32_t rows_per_block;   /* output rows per workgroup (64 per wave; matrix cores: 128 at batches above 64,
-                               256 below, and row_blocks and grid likewise) */
+  int32_t rows_per_block;   /* output rows per workgroup (64 per wave; matrix cores: 256) */
   int32_t chunks_per_block; /* 128-column chunks per workgroup */
   int32_t row_blocks;       /* workgroups along the rows */
   int32_t splits;           /* workgroups along the concatenated columns of all segments */
   int32_t total_chunks;     /* sum over segments of ceil(len/128) */
-  int32_t lds_bytes;        /* LDS per workgroup at max_batch (matrix cores: of the widest instance) */
-  int64_t grid;             /* workgroups per fluxbin_gemv launch */
+  int32_t lds_bytes;        /* LDS per workgroup at max_batch */
+  int64_t grid;             /* workgroups per fluxbin_gemv launch (matrix cores: per 32 batch rows) */
 } fluxbin_plan;
 
 int32_t fluxbin_abi_version(void);
