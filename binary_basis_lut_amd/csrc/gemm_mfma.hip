@@ -6,12 +6,14 @@ namespace fluxbin {
 
 namespace {
 
-// Automatic range length: 8 chunks for handles of at most 32 batch rows, 16
+// Automatic range length: 8 chunks for handles of at most 64 batch rows, 16
 // above, doubled while at least kMfmaPlentyBlocks 128-row blocks times
-// ranges remain (very tall layers: fewer partial sums to store and add).  Measured
-// on MI355X on the 7B shapes: q_proj 4096x4096 17.5 / 39.6 us at b = 32 / 128
-// with 8 / 16 chunks (20.2 / 58.3 with 4, 32.5 / 50.3 with 32); the MLP
-// projections within 5 % of their best.
+// ranges remain (very tall layers: fewer partial sums to store and add).
+// Measured on MI355X on the 7B shapes (4, 8, 16, 32 chunks): q_proj 4096x4096
+// at b = 32 / 64 / 128 best or level with 8 / 8 / 8-16 chunks (17.5 / 21.9 /
+// 29.5 us), 4096 -> 11008 with 8 / 8 / 16 (21.4 / 30.5 / 51.8 us; 33.0 at
+// b = 64 with 16), 11008 -> 4096 within 10 % of its best (23.2 / 31.8 / 50.9
+// us with 16 / 16 / 32).
 constexpr int64_t kMfmaPlentyBlocks = 2048;
 
 int32_t ceil_div(int32_t a, int32_t b) { return (a + b - 1) / b; }
@@ -34,7 +36,7 @@ MfmaInstance mfma_instance(int64_t batch, int rs) {
 
 int32_t mfma_auto_cpb(int32_t row_blocks, int32_t kb, int32_t nc_g, int32_t ks, int32_t nc_s, int64_t max_batch) {
   auto splits = [&](int32_t c) { return kb * ceil_div(nc_g, c) + ks * (nc_s ? ceil_div(nc_s, c) : 0); };
-  int32_t cpb = max_batch > 32 ? 16 : 8;
+  int32_t cpb = max_batch > 64 ? 16 : 8;
   while (cpb < kMaxCpb && (int64_t)row_blocks * splits(cpb * 2) >= kMfmaPlentyBlocks) cpb *= 2;
   return cpb;
 }
