@@ -125,9 +125,11 @@ fluxbin_status validate_shape(const fluxbin_layer_desc *d) {
   return FLUXBIN_OK;
 }
 
-// Chunks per workgroup: about kTargetBlocks workgroups in all (measured on
-// MI355X over 4096..57344-row layers: fewer, longer ranges amortise the
-// table build, more workgroups hide latency), at least 2 chunks, a power of
+// Chunks per workgroup: about kTargetBlocks workgroups' worth of work in all,
+// a workgroup of nb batch rows counting nb times (measured on MI355X over
+// 4096..57344-row layers: fewer, longer ranges amortise the table build, more
+// workgroups hide latency; at 4 batch rows the 4096 -> 11008 projection ran
+// 15.3 us with 4 chunks against 18.2 with 2), at least 2 chunks, a power of
 // two up to 8 and a multiple of 8 above (the prefetch depths), within the
 // LDS and register budget (cmax) and the split limit.
 //
@@ -135,8 +137,8 @@ fluxbin_status validate_shape(const fluxbin_layer_desc *d) {
 // that serves them holds 58 VGPRs (8 waves per SIMD) against 78 (6 waves)
 // for depth 8, and on the 70B gate+up projection (8192 -> 57344) 7-chunk
 // ranges ran 34.7 us against 37.8 us for 8-chunk ones.
-int32_t auto_cpb(int32_t g, int32_t cmax, int32_t waves, int64_t row_tiles, int32_t total_chunks) {
-  int64_t c = (int64_t)row_tiles * total_chunks / ((int64_t)waves * kTargetBlocks);
+int32_t auto_cpb(int32_t g, int32_t nb, int32_t cmax, int32_t waves, int64_t row_tiles, int32_t total_chunks) {
+  int64_t c = (int64_t)row_tiles * total_chunks * nb / ((int64_t)waves * kTargetBlocks);
   c = std::max<int64_t>(c, 2);
   if (g == 4 && waves == 8 && c > 7) {
     c = 7;
@@ -220,7 +222,7 @@ fluxbin_status make_plan(const fluxbin_layer_desc *d, Plan *p) {
     return fail(FLUXBIN_ERR_UNSUPPORTED, "chunks_per_block = %d exceeds %d for g = %d, max_batch = %lld, %d waves",
                 d->chunks_per_block, cmax, d->g, (long long)d->max_batch, p->waves);
   p->row_blocks = (int32_t)cdiv(p->row_tiles, p->waves);
-  p->cpb = d->chunks_per_block ? d->chunks_per_block : auto_cpb(d->g, cmax, p->waves, p->row_tiles, p->total_chunks);
+  p->cpb = d->chunks_per_block ? d->chunks_per_block : auto_cpb(d->g, p->nb, cmax, p->waves, p->row_tiles, p->total_chunks);
   p->pf = prefetch_depth(p->cpb);
   if (d->row_group) {
     // block-wise: global and salient chunks take separate workgroup ranges

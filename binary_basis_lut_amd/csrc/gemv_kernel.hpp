@@ -25,11 +25,19 @@ namespace fluxbin {
 // plans) are held to 6 waves per SIMD (at most 80 VGPRs): left alone the
 // compiler keeps the salient lookup loop's 32-byte scale slots and expanded
 // scales live at once, 83-111 VGPRs, which caps every workgroup of the call,
-// global or salient, at 4-5 waves.  These instances need no spills for it;
-// depth 8, wider batches and g = 8 would spill and are left alone.
+// global or salient, at 4-5 waves.  So are the per-row g = 4 instances of 4
+// batch rows and depth 4 or 8 (115-121 VGPRs left alone).  These instances
+// need no spills for it; the others would spill and are left alone.
+template <int G, int NB, int WAVES, int PF, int RS, int TQ>
+constexpr int lut_waves_per_eu() {
+  if (G != 4) return 1;
+  if (RS == 1) return NB == 1 && PF <= 4 ? 6 : 1;
+  return NB == 4 && PF >= 4 ? 6 : 1;
+}
+
 template <int G, int NB, int WAVES, int PF, int RS, int TQ>
 __global__ __launch_bounds__(WAVES * 64)
-__attribute__((amdgpu_waves_per_eu(G == 4 && NB == 1 && RS == 1 && PF <= 4 ? 6 : 1)))
+__attribute__((amdgpu_waves_per_eu(lut_waves_per_eu<G, NB, WAVES, PF, RS, TQ>())))
 void lut_gemv_kernel(const GemvArgs a) {
   constexpr int NT = WAVES * 64;
   constexpr int SUB = kChunkCols / G;      // sub-vectors per chunk
