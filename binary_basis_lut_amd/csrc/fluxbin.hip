@@ -671,16 +671,34 @@ fluxbin_status fluxbin_destroy(fluxbin_handle h) {
   return ok();
 }
 
-fluxbin_status fluxbin_get_plan(fluxbin_handle h, fluxbin_plan *plan) {
-  if (!h || !plan) return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "NULL argument");
-  const Plan &p = h->plan;
+namespace {
+
+void fill_plan(const fluxbin_layer_desc &d, const Plan &p, fluxbin_plan *plan) {
   plan->rows_per_block = p.mfma ? kMfmaRowsPerBlock : p.waves * kTileRows;
   plan->chunks_per_block = p.cpb;
   plan->row_blocks = p.row_blocks;
   plan->splits = p.splits;
   plan->total_chunks = p.total_chunks;
-  plan->lds_bytes = p.mfma ? mfma_lds_bytes(1, 1, 2) : lds_bytes(h->d.g, p.nb, p.cpb, entry_bytes(&h->d));
+  plan->lds_bytes = p.mfma ? mfma_lds_bytes(1, 1, 2) : lds_bytes(d.g, p.nb, p.cpb, entry_bytes(&d));
   plan->grid = (int64_t)p.row_blocks * p.splits;
+}
+
+}  // namespace
+
+fluxbin_status fluxbin_get_plan(fluxbin_handle h, fluxbin_plan *plan) {
+  if (!h || !plan) return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "NULL argument");
+  fill_plan(h->d, h->plan, plan);
+  return ok();
+}
+
+fluxbin_status fluxbin_plan_of(const fluxbin_layer_desc *d, fluxbin_plan *plan) {
+  fluxbin_status st = validate_shape(d);
+  if (st) return st;
+  if (!plan) return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "plan is NULL");
+  Plan p;
+  st = make_plan(d, &p);
+  if (st) return st;
+  fill_plan(*d, p, plan);
   return ok();
 }
 

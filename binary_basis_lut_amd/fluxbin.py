@@ -82,6 +82,7 @@ _decl("fluxbin_workspace_size", ctypes.c_int, [ctypes.POINTER(LayerDesc), ctypes
 _decl("fluxbin_create", ctypes.c_int, [ctypes.POINTER(LayerDesc), ctypes.POINTER(P)])
 _decl("fluxbin_destroy", ctypes.c_int, [P])
 _decl("fluxbin_get_plan", ctypes.c_int, [P, ctypes.POINTER(PlanInfo)])
+_decl("fluxbin_plan_of", ctypes.c_int, [ctypes.POINTER(LayerDesc), ctypes.POINTER(PlanInfo)])
 _decl("fluxbin_lut_size", ctypes.c_int, [P, I64, ctypes.POINTER(ctypes.c_size_t)])
 _decl("fluxbin_build_lut", ctypes.c_int, [P, P, I64, P, P])
 _decl("fluxbin_gemv", ctypes.c_int, [P, P, P, I64, P])
@@ -97,7 +98,8 @@ _decl("fluxbin_decomp_error", ctypes.c_int, [P, I64, I64, I32, P, P, P, P, P, P,
 SYMBOLS = [
     "fluxbin_abi_version", "fluxbin_status_string", "fluxbin_last_error", "fluxbin_tiled_words", "fluxbin_pack",
     "fluxbin_relayout", "fluxbin_tiled_scale_elems", "fluxbin_relayout_scales", "fluxbin_vcm_gather",
-    "fluxbin_workspace_size", "fluxbin_create", "fluxbin_destroy", "fluxbin_get_plan", "fluxbin_lut_size",
+    "fluxbin_workspace_size", "fluxbin_create", "fluxbin_destroy", "fluxbin_get_plan", "fluxbin_plan_of",
+    "fluxbin_lut_size",
     "fluxbin_build_lut", "fluxbin_gemv", "fluxbin_dense_gemv_f16", "fluxbin_decomp_workspace_size",
     "fluxbin_decompose", "fluxbin_decomp_row_scales", "fluxbin_decomp_col_scales", "fluxbin_decomp_signs",
     "fluxbin_decomp_residual_signs", "fluxbin_decomp_error",
@@ -187,6 +189,12 @@ def fluxbin_destroy(handle) -> None:
 def fluxbin_get_plan(handle) -> dict:
     info = PlanInfo()
     _check(_lib.fluxbin_get_plan(handle, ctypes.byref(info)), "fluxbin_get_plan")
+    return info.as_dict()
+
+
+def fluxbin_plan_of(desc: LayerDesc) -> dict:
+    info = PlanInfo()
+    _check(_lib.fluxbin_plan_of(ctypes.byref(desc), ctypes.byref(info)), "fluxbin_plan_of")
     return info.as_dict()
 
 

@@ -241,6 +241,12 @@ fluxbin_status fluxbin_create(const fluxbin_layer_desc *d, fluxbin_handle *out);
 fluxbin_status fluxbin_destroy(fluxbin_handle h);
 fluxbin_status fluxbin_get_plan(fluxbin_handle h, fluxbin_plan *plan);
 
+/* The plan fluxbin_create would choose for d (host-side arithmetic on the
+ * shape fields, no device access; pointers are not examined), for capacity
+ * planning and tests.  Fails like fluxbin_workspace_size on an invalid or
+ * unsupported shape. */
+fluxbin_status fluxbin_plan_of(const fluxbin_layer_desc *d, fluxbin_plan *plan);
+
 /* Floats fluxbin_build_lut writes for `batch` rows:
  * batch * (kb*ceil(k/g) + ks*ceil(s/g)) * 2^(g-1). */
 fluxbin_status fluxbin_lut_size(fluxbin_handle h, int64_t batch, size_t *floats);
