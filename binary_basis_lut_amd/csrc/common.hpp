@@ -403,13 +403,15 @@ __device__ __forceinline__ void lookup_word_scaled(uint32_t w, uint32_t base, fl
   }
 }
 
-// Segment and chunk-in-segment stepped to the next chunk (when `step`),
-// branch-free: scalar selects, so that loop bodies stay one basic block.
-__device__ __forceinline__ void next_chunk(const ULayer &L, int &sg, int &cis, bool step = true) {
-  const int n1 = cis + 1;
-  const bool wrap = n1 == (sg < L.kb ? L.nc_g : L.nc_s);
-  cis = step ? (wrap ? 0 : n1) : cis;
-  sg = step ? sg + (int)wrap : sg;
+// Segment and chunk-in-segment stepped to the next chunk when step is 1
+// (unchanged when 0), in integer arithmetic: uniform booleans are held as lane
+// masks, and turning them back into integers takes vector instructions.
+__device__ __forceinline__ void next_chunk(const ULayer &L, int &sg, int &cis, int step = 1) {
+  const int n1 = cis + step;                                // <= the segment's chunk count
+  const int nc = sg < L.kb ? L.nc_g : L.nc_s;
+  const int wrap = (int)((uint32_t)(nc - n1 - 1) >> 31);    // 1 when n1 == nc
+  cis = n1 - (nc & -wrap);
+  sg += wrap;
 }
 
 // Dynamic LDS of the GEMV kernel: [cpb][NB][SUB][TAB] tables of eb-byte

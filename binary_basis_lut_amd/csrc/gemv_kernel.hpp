@@ -135,9 +135,9 @@ void lut_gemv_kernel(const GemvArgs a) {
         rsa[u] = __builtin_nontemporal_load(rp);
         rsb[u] = __builtin_nontemporal_load(rp + sal_hi);
       }
-      const bool step = pidx < nch - 1;  // past the last chunk the last one is read again
-      next_chunk(L, ps, pcis, step);
-      pidx += (int)step;
+      const int step = (int)((uint32_t)(pidx - nch + 1) >> 31);  // 1 while pidx < nch - 1: past
+      next_chunk(L, ps, pcis, step);                               // the last chunk it is read again
+      pidx += step;
     };
     auto issue_weights = [&]() {
 #pragma unroll
