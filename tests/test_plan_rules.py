@@ -73,6 +73,20 @@ def test_large_per_row_layer_takes_eight_waves(fb):
         assert (p["rows_per_block"], p["chunks_per_block"], p["splits"]) == (256, 4, 33)
 
 
+def test_g8_layers_take_eight_waves_within_the_lds_budget(fb):
+    # 7B layer, 3 global bases + 2 % salient, g = 8: 512 rows per workgroup; a chunk's g = 8
+    # tables are 16 sub-vectors x 256 entries, 16 KiB per batch row (fp32), so qkv and down take
+    # 2-chunk ranges and the gate+up projection 4 (64 KiB of tables plus the staged inputs)
+    expect = {0: (2, 49), 1: (2, 49), 2: (4, 25), 3: (2, 130)}
+    for shape, (cpb, splits) in expect.items():
+        p = plan(fb, workload_desc(fb, 3, shape))
+        assert (p["rows_per_block"], p["chunks_per_block"], p["splits"]) == (512, cpb, splits), shape
+    assert plan(fb, workload_desc(fb, 3, 2))["lds_bytes"] == 4 * (16 * 256 * 4 + 128 * 4) + 256
+    # fp16 entries halve the tables
+    assert plan(fb, workload_desc(fb, 3, 2, table_precision=fb.TABLE_F16, chunks_per_block=4))["lds_bytes"] == \
+        4 * (16 * 256 * 2 + 128 * 4) + 256
+
+
 def test_explicit_choices_override_the_rules(fb):
     p = plan(fb, workload_desc(fb, 5, 2, waves_per_block=4, chunks_per_block=8))
     assert (p["rows_per_block"], p["chunks_per_block"], p["splits"]) == (256, 8, 17)
