@@ -45,7 +45,7 @@
 namespace fluxbin {
 
 constexpr int kMfmaWaves = 4;
-constexpr int kMfmaMaxBlocks = 4;               // 32-row batch blocks per workgroup (NBT * WB)
+constexpr int kMfmaMaxBlocks = 4;               // 32-row batch blocks of a call, at most (batch <= 128)
 constexpr int kMfmaRowsPerBlock = 256;          // weight rows per workgroup of the instance in use
 constexpr int kMfmaXStride = kChunkCols + 8;    // halfs per staged batch row: 272 B, conflict-free 16-B reads
 

@@ -158,7 +158,7 @@ typedef struct {
   int32_t compute;             /* fluxbin_compute.  FLUXBIN_COMPUTE_MFMA ignores g and table_precision,
                                   takes chunks_per_block as the 128-column chunks of one segment per
                                   workgroup (a workgroup never spans two segments) and needs
-                                  waves_per_block 0 or 4 (128 rows per workgroup) */
+                                  waves_per_block 0 or 4 (256 rows per workgroup) */
 } fluxbin_layer_desc;
 
 /* How a handle splits the work (read-only introspection). */
