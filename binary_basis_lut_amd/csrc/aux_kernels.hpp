@@ -212,4 +212,13 @@ __global__ __launch_bounds__(256) void dense_f16_gemv_kernel(const uint16_t *w, 
   }
 }
 
+// --------------------------------------------------------------------------
+// Workspace reset: zero `words` 64-bit words (a kernel, not a memset, so that
+// the call can be captured in a graph)
+// --------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void zero_words_kernel(uint64_t *w, int64_t words) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < words; i += (int64_t)gridDim.x * blockDim.x)
+    w[i] = 0;
+}
+
 }  // namespace fluxbin

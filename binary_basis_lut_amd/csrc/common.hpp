@@ -27,11 +27,15 @@
 //   * a workgroup of WAVES waves shares the tables of CPB consecutive chunks of
 //     the concatenated column space of all segments; a grid of
 //     row_blocks x splits workgroups covers the layer;
+//   * a workgroup's column range never leaves one segment, so its sign words
+//     are consecutive 1 KiB blocks and its partial sum takes one row scale;
 //   * splits > 1: each workgroup adds its fp32 partial of every row, as an
 //     exact fixed-point integer, into a per-row 64-bit word that also counts
 //     arrivals; the lane whose atomic brings the last contribution writes the
 //     fp16 row.  One launch does the whole GEMV, the result is bitwise
-//     deterministic, and no workgroup ever waits for another.
+//     deterministic, and no workgroup ever waits for another.  A partial too
+//     large for the fixed-point range sets a sticky flag in the word, and the
+//     row is then written as NaN instead of a wrong number.
 #pragma once
 
 #include <hip/hip_fp16.h>
@@ -45,19 +49,26 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kChunkCols = 128;  // columns per chunk = 4 sign words per row
 constexpr int kTileRows = 64;    // rows per tile = one wave, one row per lane
 constexpr int kMaxSeg = 6;       // kb <= 4 global + ks <= 2 salient bases
-// Split reduction: one 64-bit word per (batch row, output row) holds the
-// number of contributions so far (top 8 bits) and the sum of the
-// contributions' biased fixed-point values (low 56 bits).  Each contribution
-// is round(partial * 2^30), clamped to |.| < 2^47, plus a bias of 2^47, so it
-// lies in [0, 2^48) and up to 255 of them never carry into the count.
-constexpr int kCountShift = 56;
+// Split reduction: one 64-bit word per (batch row, output row).  Bit 63 is a
+// sticky overflow flag, bits 55-62 count the contributions so far and bits
+// 0-54 hold the sum of their biased fixed-point values.  A contribution is
+// round(partial * 2^29) + 2^46, which lies in [0, 2^47) for |partial| < 2^17;
+// up to 255 of them sum below 2^55, so the value never carries into the count
+// and the count (at most 255) never reaches the flag.  A partial outside that
+// range is clamped and also ORs the flag into the word before it adds itself:
+// both are atomics on the same word from the same lane, so the flag precedes
+// the contribution in the word's modification order and the last arriver sees
+// it.
+constexpr int kCountShift = 55;
 constexpr int kMaxSplits = 255;
 constexpr uint64_t kOneArrival = 1ull << kCountShift;
 constexpr uint64_t kValueMask = kOneArrival - 1;
-constexpr int64_t kFixBias = 1ll << 47;
-constexpr float kFixScale = 1073741824.0f;          // 2^30
-constexpr float kFixInv = 1.0f / 1073741824.0f;     // 2^-30
-constexpr float kFixClamp = 140737479966720.0f;     // 2^47 - 2^23, the largest float below 2^47
+constexpr uint64_t kOverflow = 1ull << 63;
+constexpr int64_t kFixBias = 1ll << 46;
+constexpr float kFixScale = 536870912.0f;           // 2^29
+constexpr float kFixInv = 1.0f / 536870912.0f;      // 2^-29
+constexpr float kFixLimit = 70368744177664.0f;      // 2^46: |partial * 2^29| must stay below it
+constexpr uint16_t kHalfNaN = 0x7e00;
 
 // The segments of one layer (kb global bases over k columns, then ks salient
 // bases over s compact columns), addressed arithmetically: the descriptor of
@@ -173,40 +184,27 @@ __device__ __forceinline__ SegRef gemv_segment(const SegDesc (&seg)[kMaxSeg], in
   return r;
 }
 
-// Segment of chunk gc of the concatenated chunk space, and the chunk's index inside it.
-__device__ __forceinline__ int seg_of(const ULayer &L, int gc, int *cis) {
-  const int gch = L.kb * L.nc_g;
-  if (gc < gch) {
-    const int b = gc / L.nc_g;
-    *cis = gc - b * L.nc_g;
-    return b;
-  }
-  const int b = (gc - gch) / L.nc_s;
-  *cis = gc - gch - b * L.nc_s;
-  return L.kb + b;
-}
-
 struct GemvArgs {
   SegDesc seg[kMaxSeg];   // kb global segments, then ks salient ones
-  LayerArgs L;
   const int32_t *idx_or_dummy;  // sal_idx, or a valid one-element array when ks == 0
-  int32_t cpb;            // 128-column chunks per workgroup (tables sized in dynamic LDS)
-  int32_t total_chunks;
-  int32_t row_tiles;
-  int32_t row_blocks;
-  int32_t splits;
-  int32_t batch;
-  int64_t n_pad;          // row_tiles * 64
   const uint16_t *x;      // fp16 [batch][k]
   uint16_t *y;            // fp16 [batch][n]
-  uint64_t *acc;          // [batch][n_pad] packed (arrivals, fixed-point sum); zero between calls
-  // Workgroup ranges: splits [0, gsplits) cover chunks [0, gchunks) and the
-  // rest cover [gchunks, total_chunks), cpb chunks each (the last range of
-  // each part may be shorter).  Per-row scales: one part (gsplits = splits,
-  // gchunks = total_chunks).  Block-wise scales: global and salient chunks
-  // never share a workgroup (gchunks = kb * ceil(k / 128)).
-  int32_t gsplits;
-  int32_t gchunks;
+  uint64_t *acc;          // [batch][n_pad] split-reduction words; zero between calls
+  int64_t n;              // output rows
+  int64_t k;              // input columns (x row stride)
+  int64_t n_pad;          // row_tiles * 64
+  int32_t kb, ks;
+  // Column ranges: every segment is cut into equal-as-possible ranges of
+  // consecutive chunks, rpg per global and rps per salient segment; split sp
+  // < kb * rpg is range sp % rpg of global segment sp / rpg, the rest follow
+  // the same rule over the salient segments.  No range is longer than cpb
+  // chunks (the dynamic LDS is sized for cpb).
+  int32_t rpg, rps;
+  int32_t cpb;
+  int32_t row_tiles;
+  int32_t row_blocks;
+  int32_t splits;         // kb * rpg + ks * rps
+  int32_t batch;
   int32_t sal16;          // block-wise: 16 salient row-scale groups per chunk (8 columns each), else 8
 };
 
@@ -227,19 +225,6 @@ gemv_fn gemv_pick_g8_rs1_t16(int nb, int waves, int pf);
 
 __device__ __forceinline__ float h2f(uint16_t h) { return __half2float(__ushort_as_half(h)); }
 __device__ __forceinline__ uint16_t f2h(float f) { return __half_as_ushort(__float2half_rn(f)); }
-
-// Value number s of six scalars (s uniform).  Plain SSA values, never an
-// aggregate: an array or struct indexed by a runtime segment number would be
-// placed in LDS or scratch memory by the compiler.
-__device__ __forceinline__ float pick6(int s, float v0, float v1, float v2, float v3, float v4, float v5) {
-  float r = v0;
-  r = s == 1 ? v1 : r;
-  r = s == 2 ? v2 : r;
-  r = s == 3 ? v3 : r;
-  r = s == 4 ? v4 : r;
-  r = s == 5 ? v5 : r;
-  return r;
-}
 
 #define FB_LDS __attribute__((address_space(3)))
 
@@ -324,11 +309,15 @@ __device__ __forceinline__ uint32_t byte_pattern(uint32_t w) {
 
 // Accumulate the lookups of one 32-bit word (32 columns) of one row.  `base`
 // is the LDS byte address of the chunk's table block (a multiple of 256, or of
-// 512 for 256-entry tables, below 2^24); j0 is the first sub-vector of the
+// 1024 for 256-entry tables, below 2^24); j0 is the first sub-vector of the
 // word.  Sub-vector j of batch row b has its TAB-entry table at
-// base + ((b * SUB + j) * TAB) * EB.
+// base + ((b * SUB + j) * TAB) * EB.  Even sub-vectors (low nibbles / bytes 0
+// and 2) go to acc0, odd ones to acc1: two independent chains of fp32 adds,
+// or one when the caller passes the same array twice (wide batches, whose NB
+// rows already give independent chains).
 template <int G, int NB, int EB>
-__device__ __forceinline__ void lookup_word(uint32_t w, uint32_t base, float (&acc)[NB], int j0) {
+__device__ __forceinline__ void lookup_word(uint32_t w, uint32_t base, float (&acc0)[NB], float (&acc1)[NB],
+                                            int j0) {
   constexpr int SUB = kChunkCols / G;
   constexpr int TAB = 1 << G;
   if constexpr (G == 4) {
@@ -341,8 +330,8 @@ __device__ __forceinline__ void lookup_word(uint32_t w, uint32_t base, float (&a
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
         const int off0 = ((b * SUB + j0 + 2 * kk) * TAB) * EB;
-        acc[b] = add_entry<EB>(acc[b], ia[kk] + off0);
-        acc[b] = add_entry<EB>(acc[b], ib[kk] + off0 + TAB * EB);
+        acc0[b] = add_entry<EB>(acc0[b], ia[kk] + off0);
+        acc1[b] = add_entry<EB>(acc1[b], ib[kk] + off0 + TAB * EB);
       }
       // wide batches: at most 2 * NB table reads in flight per step, or the
       // scheduler hoists all of them and runs out of registers
@@ -353,11 +342,12 @@ __device__ __forceinline__ void lookup_word(uint32_t w, uint32_t base, float (&a
     const uint32_t ix[4] = {byte_pattern<EB, 0>(w) | base, byte_pattern<EB, 1>(w) | base,
                             byte_pattern<EB, 2>(w) | base, byte_pattern<EB, 3>(w) | base};
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
+    for (int kk = 0; kk < 4; kk += 2) {
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
         const int off0 = ((b * SUB + j0 + kk) * TAB) * EB;
-        acc[b] = add_entry<EB>(acc[b], ix[kk] + off0);
+        acc0[b] = add_entry<EB>(acc0[b], ix[kk] + off0);
+        acc1[b] = add_entry<EB>(acc1[b], ix[kk + 1] + off0 + TAB * EB);
       }
       if constexpr (NB >= 8) asm volatile("" ::: "memory");
     }
@@ -403,17 +393,6 @@ __device__ __forceinline__ void lookup_word_scaled(uint32_t w, uint32_t base, fl
   }
 }
 
-// Segment and chunk-in-segment stepped to the next chunk when step is 1
-// (unchanged when 0), in integer arithmetic: uniform booleans are held as lane
-// masks, and turning them back into integers takes vector instructions.
-__device__ __forceinline__ void next_chunk(const ULayer &L, int &sg, int &cis, int step = 1) {
-  const int n1 = cis + step;                                // <= the segment's chunk count
-  const int nc = sg < L.kb ? L.nc_g : L.nc_s;
-  const int wrap = (int)((uint32_t)(nc - n1 - 1) >> 31);    // 1 when n1 == nc
-  cis = n1 - (nc & -wrap);
-  sg += wrap;
-}
-
 // Dynamic LDS of the GEMV kernel: [cpb][NB][SUB][TAB] tables of eb-byte
 // entries (fp32, or fp16 when quantised), then [cpb][NB][128] fp32
 // scale-fused inputs, then a 64-float sink for the stores of unused input
@@ -430,27 +409,22 @@ __host__ __device__ constexpr int lds_bytes(int g, int nb, int cpb, int eb) {
   return cpb * lds_per_chunk(g, nb, eb) + kLdsSink;
 }
 
-constexpr int kMaxItems = 8;  // table-build inputs per thread (registers)
-
 __host__ __device__ constexpr int cmin(int a, int b) { return a < b ? a : b; }
 
-// Most chunks one workgroup may take for table width g, batch width nb,
-// `waves` waves and eb-byte entries: its tables must fit the LDS budget, and
-// its table-build inputs (nb * 128 per chunk) at most kMaxItems per thread.
-__host__ __device__ constexpr int cpb_cap(int g, int nb, int waves, int eb) {
-  return cmin(cmin(kMaxCpb, (kLdsBudget - kLdsSink) / lds_per_chunk(g, nb, eb)),
-              kMaxItems * waves * 64 / (nb * kChunkCols)) < 1
+// Table-build inputs (c * x) each thread stages per round: 4 for one batch
+// row, 8 for several (the first round's loads are all in flight at once).
+__host__ __device__ constexpr int stage_items(int nb) { return nb == 1 ? 4 : 8; }
+
+// Most chunks one workgroup may take for table width g, batch width nb and
+// eb-byte entries: its tables and inputs must fit the LDS budget.
+__host__ __device__ constexpr int cpb_cap(int g, int nb, int eb) {
+  return cmin(kMaxCpb, (kLdsBudget - kLdsSink) / lds_per_chunk(g, nb, eb)) < 1
              ? 1
-             : cmin(cmin(kMaxCpb, (kLdsBudget - kLdsSink) / lds_per_chunk(g, nb, eb)),
-                    kMaxItems * waves * 64 / (nb * kChunkCols));
+             : cmin(kMaxCpb, (kLdsBudget - kLdsSink) / lds_per_chunk(g, nb, eb));
 }
 
-// Prefetch depth for a workgroup range of cpb chunks: the deepest of 8, 4, 2
-// that the range fills (a shorter range would re-read its last chunk).
-__host__ __device__ constexpr int prefetch_depth(int cpb) { return cpb >= 8 ? 8 : cpb >= 4 ? 4 : 2; }
-
-// Most chunks a kernel instance with prefetch depth pf serves.
-__host__ __device__ constexpr int cpb_for_depth(int pf, int cap) { return pf == 8 ? cap : cmin(2 * pf - 1, cap); }
+// Chunks of weights in flight per wave for ranges of up to cpb chunks.
+__host__ __device__ constexpr int prefetch_depth(int cpb) { return cpb >= 4 ? 4 : 2; }
 
 template <bool B>
 struct BoolTag {

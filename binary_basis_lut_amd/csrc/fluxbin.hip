@@ -17,7 +17,7 @@
 #include <vector>
 
 #include "aux_kernels.hpp"
-#include "gemm_mfma.hpp"
+#include "probes.hpp"
 #include "decomp_kernels.hpp"
 
 using namespace fluxbin;
@@ -53,19 +53,15 @@ constexpr int64_t kWideWork = 32768;  // row tiles x chunks from which per-row l
 struct Plan {
   int32_t waves;       // waves per workgroup (64 rows each)
   int32_t nb;          // compiled batch width = batch rows per group (see batch_group)
-  int32_t cpb;         // chunks per workgroup
-  int32_t pf;          // chunks of weights in flight per wave (2 or 8)
+  int32_t cpb;         // most chunks in one column range (LDS is sized for it)
+  int32_t pf;          // chunks of weights in flight per wave (2 or 4)
   int32_t row_tiles;
   int32_t row_blocks;
   int32_t total_chunks;
-  int32_t gchunks;     // chunks of the first range part (all chunks, or the global ones when block-wise)
-  int32_t gsplits;     // workgroup ranges over the first part
-  int32_t splits;
+  int32_t rpg, rps;    // column ranges per global / salient segment
+  int32_t splits;      // kb * rpg + ks * rps
   int64_t n_pad;
-  size_t acc_bytes;    // workspace (splits > 1): packed reduction words (LUT) or fp32 partials (MFMA)
-  bool mfma;           // matrix-core route: ranges of one segment each
-  int32_t ranges_g;    // matrix-core ranges per global / salient segment
-  int32_t ranges_s;
+  size_t acc_bytes;    // workspace (splits > 1): packed reduction words
 };
 
 constexpr int kMaxBatch = 128;
@@ -99,11 +95,8 @@ fluxbin_status validate_shape(const fluxbin_layer_desc *d) {
                 kMaxCpb);
   if (d->waves_per_block != 0 && d->waves_per_block != 4 && d->waves_per_block != 8)
     return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "waves_per_block = %d (0, 4 or 8)", d->waves_per_block);
-  if (d->compute != FLUXBIN_COMPUTE_LUT && d->compute != FLUXBIN_COMPUTE_MFMA)
-    return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "compute = %d (0 = LUT, 1 = MFMA)", d->compute);
-  if (d->compute == FLUXBIN_COMPUTE_MFMA && d->waves_per_block != 0 && d->waves_per_block != kMfmaWaves)
-    return fail(FLUXBIN_ERR_UNSUPPORTED, "waves_per_block = %d with compute MFMA (0 or %d)", d->waves_per_block,
-                kMfmaWaves);
+  if (d->layout != FLUXBIN_LAYOUT_ROWMAJOR && d->layout != FLUXBIN_LAYOUT_TILED)
+    return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "layout = %d (0 = row-major, 1 = tiled)", d->layout);
   if (d->table_precision != FLUXBIN_TABLE_F32 && d->table_precision != FLUXBIN_TABLE_F16)
     return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "table_precision = %d (0 = fp32, 1 = fp16)", d->table_precision);
   if (d->row_group != 0 && d->row_group != kChunkCols)
@@ -125,21 +118,19 @@ fluxbin_status validate_shape(const fluxbin_layer_desc *d) {
   return FLUXBIN_OK;
 }
 
-// Chunks per workgroup: about kTargetBlocks workgroups' worth of work in all,
-// a workgroup of nb batch rows counting nb times (measured on MI355X over
-// 4096..57344-row layers: fewer, longer ranges amortise the table build, more
-// workgroups hide latency; at 4 batch rows the 4096 -> 11008 projection ran
-// 15.3 us with 4 chunks against 18.2 with 2), at least 2 chunks, a power of
-// two up to 8 and a multiple of 8 above (the prefetch depths), within the
-// LDS and register budget (cmax) and the split limit.
-//
-// Eight-wave g = 4 workgroups take at most 7 chunks: the depth-4 instance
-// that serves them holds 58 VGPRs (8 waves per SIMD) against 78 (6 waves)
-// for depth 8, and on the 70B gate+up projection (8192 -> 57344) 7-chunk
-// ranges ran 34.7 us against 37.8 us for 8-chunk ones.
+// Target chunks per column range: about kTargetBlocks workgroups' worth of
+// work in all, a workgroup of nb batch rows counting nb times (measured on
+// MI355X over 4096..57344-row layers: fewer, longer ranges amortise the table
+// build, more workgroups hide latency), at least 2, a power of two up to 8 and
+// a multiple of 8 above, at most 7 for eight-wave g = 4 workgroups and 4 for
+// several batch rows (the 4096 -> 11008 projection at 4 batch rows: 15.2 us
+// with 4-chunk ranges, 18.0 with 7), within the LDS budget (cmax).  Every
+// segment is then cut into ceil(chunks / target) ranges of equal length
+// (within one chunk).
 int32_t auto_cpb(int32_t g, int32_t nb, int32_t cmax, int32_t waves, int64_t row_tiles, int32_t total_chunks) {
   int64_t c = (int64_t)row_tiles * total_chunks * nb / ((int64_t)waves * kTargetBlocks);
   c = std::max<int64_t>(c, 2);
+  if (nb > 1) c = std::min<int64_t>(c, 4);
   if (g == 4 && waves == 8 && c > 7) {
     c = 7;
   } else if (c <= 8) {
@@ -149,8 +140,6 @@ int32_t auto_cpb(int32_t g, int32_t nb, int32_t cmax, int32_t waves, int64_t row
   } else {
     c = c / 8 * 8;
   }
-  c = std::max<int64_t>(c, cdiv(total_chunks, kMaxSplits));
-  if (c > 8) c = cdiv(c, 8) * 8;
   return (int32_t)std::max<int64_t>(1, std::min<int64_t>(c, cmax));
 }
 
@@ -164,45 +153,10 @@ int32_t batch_group(int32_t g, int64_t max_batch) {
 
 int entry_bytes(const fluxbin_layer_desc *d) { return d->table_precision == FLUXBIN_TABLE_F16 ? 2 : 4; }
 
-// Matrix-core route: ranges of cpb chunks inside one segment (automatic cpb:
-// mfma_auto_cpb, next to the kernel).
-fluxbin_status make_mfma_plan(const fluxbin_layer_desc *d, Plan *p) {
-  // x is addressed with 32-bit element offsets: batch row * k + column
-  if (d->max_batch * d->k > (int64_t)INT32_MAX - kChunkCols)
-    return fail(FLUXBIN_ERR_UNSUPPORTED, "max_batch * k = %lld too large for compute MFMA (below 2^31)",
-                (long long)(d->max_batch * d->k));
-  p->mfma = true;
-  p->nb = 0;
-  p->pf = 0;
-  p->waves = kMfmaWaves;
-  p->row_blocks = (int32_t)cdiv(d->n, kMfmaRowsPerBlock);
-  const int32_t nc_g = (int32_t)cdiv(d->k, kChunkCols), nc_s = d->ks > 0 ? (int32_t)cdiv(d->s, kChunkCols) : 0;
-  auto splits_for = [&](int32_t c) { return d->kb * (int32_t)cdiv(nc_g, c) + d->ks * (int32_t)cdiv(nc_s, c); };
-  int32_t cpb = d->chunks_per_block;
-  if (!cpb) {
-    cpb = mfma_auto_cpb((int32_t)cdiv(d->n, 2 * kTileRows), d->kb, nc_g, d->ks, nc_s, d->max_batch);
-    while (splits_for(cpb) > kMaxSplits && cpb < kMaxCpb) ++cpb;
-  }
-  p->cpb = cpb;
-  p->ranges_g = (int32_t)cdiv(nc_g, cpb);
-  p->ranges_s = d->ks > 0 ? (int32_t)cdiv(nc_s, cpb) : 0;
-  p->splits = splits_for(cpb);
-  p->gsplits = d->kb * p->ranges_g;
-  p->gchunks = d->kb * nc_g;
-  if (p->splits > kMaxSplits)
-    return fail(FLUXBIN_ERR_UNSUPPORTED, "%d column ranges exceed %d (chunks_per_block %d)", p->splits, kMaxSplits,
-                cpb);
-  p->acc_bytes = p->splits > 1 ? (size_t)p->splits * d->max_batch * p->n_pad * sizeof(float) : 0;
-  return FLUXBIN_OK;
-}
-
 fluxbin_status make_plan(const fluxbin_layer_desc *d, Plan *p) {
   p->row_tiles = (int32_t)cdiv(d->n, kTileRows);
   p->n_pad = (int64_t)p->row_tiles * kTileRows;
   p->total_chunks = (int32_t)(d->kb * cdiv(d->k, kChunkCols) + d->ks * cdiv(d->s, kChunkCols));
-  p->mfma = false;
-  p->ranges_g = p->ranges_s = 0;
-  if (d->compute == FLUXBIN_COMPUTE_MFMA) return make_mfma_plan(d, p);
   p->nb = batch_group(d->g, d->max_batch);
   if (d->waves_per_block) {
     p->waves = d->waves_per_block;
@@ -217,27 +171,59 @@ fluxbin_status make_plan(const fluxbin_layer_desc *d, Plan *p) {
     const bool wide = !d->row_group && (int64_t)p->row_tiles * p->total_chunks >= kWideWork;
     p->waves = (d->g == 8 || p->row_tiles >= 512 || wide) ? 8 : 4;
   }
-  const int32_t cmax = cpb_cap(d->g, p->nb, p->waves, entry_bytes(d));
+  const int32_t cmax = cpb_cap(d->g, p->nb, entry_bytes(d));
   if (d->chunks_per_block > cmax)
     return fail(FLUXBIN_ERR_UNSUPPORTED, "chunks_per_block = %d exceeds %d for g = %d, max_batch = %lld, %d waves",
                 d->chunks_per_block, cmax, d->g, (long long)d->max_batch, p->waves);
   p->row_blocks = (int32_t)cdiv(p->row_tiles, p->waves);
-  p->cpb = d->chunks_per_block ? d->chunks_per_block : auto_cpb(d->g, p->nb, cmax, p->waves, p->row_tiles, p->total_chunks);
-  p->pf = prefetch_depth(p->cpb);
-  if (d->row_group) {
-    // block-wise: global and salient chunks take separate workgroup ranges
-    p->gchunks = (int32_t)(d->kb * cdiv(d->k, kChunkCols));
-    p->gsplits = (int32_t)cdiv(p->gchunks, p->cpb);
-    p->splits = p->gsplits + (int32_t)cdiv(p->total_chunks - p->gchunks, p->cpb);
-  } else {
-    p->gchunks = p->total_chunks;
-    p->splits = p->gsplits = (int32_t)cdiv(p->total_chunks, p->cpb);
+  int32_t target =
+      d->chunks_per_block ? d->chunks_per_block : auto_cpb(d->g, p->nb, cmax, p->waves, p->row_tiles, p->total_chunks);
+  const int32_t nc_g = (int32_t)cdiv(d->k, kChunkCols), nc_s = d->ks > 0 ? (int32_t)cdiv(d->s, kChunkCols) : 0;
+  for (;;) {
+    p->rpg = (int32_t)cdiv(nc_g, target);
+    p->rps = d->ks > 0 ? (int32_t)cdiv(nc_s, target) : 0;
+    p->splits = d->kb * p->rpg + d->ks * p->rps;
+    if (p->splits <= kMaxSplits || d->chunks_per_block || target >= cmax) break;
+    ++target;  // automatic plan: longer ranges until the splits fit the reduction word
   }
   if (p->splits > kMaxSplits)
-    return fail(FLUXBIN_ERR_UNSUPPORTED, "%d column splits exceed %d (too many 128-column chunks for chunks_per_block %d)",
-                p->splits, kMaxSplits, p->cpb);
+    return fail(FLUXBIN_ERR_UNSUPPORTED, "%d column ranges exceed %d (too many 128-column chunks for chunks_per_block %d)",
+                p->splits, kMaxSplits, target);
+  // the longest range (balanced cut: ceil(chunks / ranges))
+  p->cpb = (int32_t)std::max<int64_t>(cdiv(nc_g, p->rpg), d->ks > 0 ? cdiv(nc_s, p->rps) : 0);
+  p->pf = prefetch_depth(p->cpb);
   p->acc_bytes = p->splits > 1 ? (size_t)d->max_batch * p->n_pad * sizeof(uint64_t) : 0;
   return FLUXBIN_OK;
+}
+
+// Regions of a handle's workspace (byte offsets, each 256-B aligned): the
+// split-reduction words, then, for row-major inputs, the tiled copies made by
+// fluxbin_create.
+struct WsLayout {
+  size_t acc, bits_g, bits_s, r_g, r_s, total;
+};
+
+WsLayout ws_layout(const fluxbin_layer_desc *d, const Plan &p) {
+  WsLayout w{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += (bytes + 255) / 256 * 256;
+    return o;
+  };
+  w.acc = take(p.acc_bytes);
+  if (d->layout == FLUXBIN_LAYOUT_ROWMAJOR) {
+    w.bits_g = take((size_t)d->kb * fluxbin_tiled_words(d->n, d->k) * 4);
+    if (d->ks > 0) w.bits_s = take((size_t)d->ks * fluxbin_tiled_words(d->n, d->s) * 4);
+    if (d->row_group) {
+      const int64_t groups = cdiv(d->k, d->row_group);
+      w.r_g = take((size_t)d->kb * fluxbin_tiled_scale_elems(d->n, groups, 1) * 2);
+      if (d->ks > 0)
+        w.r_s = take((size_t)d->ks * fluxbin_tiled_scale_elems(d->n, groups, kChunkCols / d->sal_group) * 2);
+    }
+  }
+  w.total = off;
+  return w;
 }
 
 }  // namespace
@@ -471,6 +457,22 @@ void run_error(hipStream_t st, const uint16_t *w, int64_t n, int64_t k, int kb, 
 // ---------------------------------------------------------------------------
 // C ABI
 // ---------------------------------------------------------------------------
+namespace {
+
+template <int G, int NB>
+hipError_t launch_lookup_probe(int64_t workgroups, int32_t iters, float never, float *sink, hipStream_t st) {
+  constexpr int lds = NB * (kChunkCols / G) * (1 << G) * 4;
+  hipError_t e =
+      hipFuncSetAttribute(reinterpret_cast<const void *>(lds_lookup_kernel<G, NB>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((lds_lookup_kernel<G, NB>), dim3((unsigned)workgroups), dim3(256), lds, st, iters, 0x2545f491u,
+                     never, sink);
+  return hipGetLastError();
+}
+
+}  // namespace
+
 extern "C" {
 
 int32_t fluxbin_abi_version(void) { return FLUXBIN_ABI_VERSION; }
@@ -584,7 +586,7 @@ fluxbin_status fluxbin_workspace_size(const fluxbin_layer_desc *d, size_t *bytes
   Plan p;
   st = make_plan(d, &p);
   if (st) return st;
-  *bytes = p.acc_bytes;
+  *bytes = ws_layout(d, p).total;
   return ok();
 }
 
@@ -594,21 +596,24 @@ fluxbin_status fluxbin_create(const fluxbin_layer_desc *d, fluxbin_handle *out) 
   if (!out) return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "out is NULL");
   if (!d->bits_global || !d->r_global || !d->c_global)
     return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "global basis pointers must be non-NULL");
-  if (!aligned(d->bits_global, 16)) return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "bits_global not 16-byte aligned");
+  const bool tiled = d->layout == FLUXBIN_LAYOUT_TILED;
+  if (!aligned(d->bits_global, tiled ? 16 : 4))
+    return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "bits_global not %d-byte aligned", tiled ? 16 : 4);
   if (d->ks > 0) {
     if (!d->bits_sal || !d->r_sal || !d->c_sal || !d->sal_idx)
       return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "salient pointers must be non-NULL when ks > 0");
-    if (!aligned(d->bits_sal, 16)) return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "bits_sal not 16-byte aligned");
-    if (d->row_group && !aligned(d->r_sal, 16))
+    if (!aligned(d->bits_sal, tiled ? 16 : 4))
+      return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "bits_sal not %d-byte aligned", tiled ? 16 : 4);
+    if (d->row_group && tiled && !aligned(d->r_sal, 16))
       return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "r_sal not 16-byte aligned (block-wise scales)");
   }
   Plan p;
   st = make_plan(d, &p);
   if (st) return st;
-  const size_t need = p.acc_bytes;
-  if (need > 0) {
-    if (!d->workspace || d->workspace_bytes < need)
-      return fail(FLUXBIN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+  const WsLayout wl = ws_layout(d, p);
+  if (wl.total > 0) {
+    if (!d->workspace || d->workspace_bytes < wl.total)
+      return fail(FLUXBIN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", wl.total,
                   d->workspace ? d->workspace_bytes : (size_t)0);
     if (!aligned(d->workspace, 256)) return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "workspace not 256-byte aligned");
   }
@@ -629,22 +634,59 @@ fluxbin_status fluxbin_create(const fluxbin_layer_desc *d, fluxbin_handle *out) 
                     (long long)i, idx[i], (long long)(i / d->sal_group), d->sal_group);
     }
   }
-  if (p.acc_bytes) {
-    hipError_t e = hipMemset(d->workspace, 0, p.acc_bytes);
-    if (e != hipSuccess) return hip_fail(e, "zeroing the split-reduction words");
-    e = hipDeviceSynchronize();
+  // the description the handle keeps: row-major inputs are replaced by their
+  // tiled copies in the workspace
+  fluxbin_layer_desc hd = *d;
+  char *ws = static_cast<char *>(d->workspace);
+  if (!tiled) {
+    const int64_t wpr_g = cdiv(d->k, 32), wpr_s = cdiv(d->s, 32);
+    const int64_t tw_g = fluxbin_tiled_words(d->n, d->k), tw_s = d->ks > 0 ? fluxbin_tiled_words(d->n, d->s) : 0;
+    uint32_t *bg = reinterpret_cast<uint32_t *>(ws + wl.bits_g);
+    for (int b = 0; b < d->kb && !st; ++b)
+      st = fluxbin_relayout(d->bits_global + b * d->n * wpr_g, d->n, d->k, FLUXBIN_LAYOUT_ROWMAJOR,
+                            FLUXBIN_LAYOUT_TILED, bg + b * tw_g, nullptr);
+    hd.bits_global = bg;
+    if (d->ks > 0) {
+      uint32_t *bs = reinterpret_cast<uint32_t *>(ws + wl.bits_s);
+      for (int b = 0; b < d->ks && !st; ++b)
+        st = fluxbin_relayout(d->bits_sal + b * d->n * wpr_s, d->n, d->s, FLUXBIN_LAYOUT_ROWMAJOR,
+                              FLUXBIN_LAYOUT_TILED, bs + b * tw_s, nullptr);
+      hd.bits_sal = bs;
+    }
+    if (d->row_group) {
+      const int64_t groups = cdiv(d->k, d->row_group), m = kChunkCols / (d->ks > 0 ? d->sal_group : kChunkCols);
+      const int64_t te_g = fluxbin_tiled_scale_elems(d->n, groups, 1);
+      uint16_t *rg = reinterpret_cast<uint16_t *>(ws + wl.r_g);
+      for (int b = 0; b < d->kb && !st; ++b)
+        st = fluxbin_relayout_scales(d->r_global + b * d->n * groups, d->n, groups, 1, FLUXBIN_LAYOUT_ROWMAJOR,
+                                     FLUXBIN_LAYOUT_TILED, rg + b * te_g, nullptr);
+      hd.r_global = rg;
+      if (d->ks > 0) {
+        const int64_t te_s = fluxbin_tiled_scale_elems(d->n, groups, m);
+        uint16_t *rs = reinterpret_cast<uint16_t *>(ws + wl.r_s);
+        for (int b = 0; b < d->ks && !st; ++b)
+          st = fluxbin_relayout_scales(d->r_sal + b * d->n * groups, d->n, groups, m, FLUXBIN_LAYOUT_ROWMAJOR,
+                                       FLUXBIN_LAYOUT_TILED, rs + b * te_s, nullptr);
+        hd.r_sal = rs;
+      }
+    }
+    if (st) return st;
+    hd.layout = FLUXBIN_LAYOUT_TILED;
+  }
+  if (p.acc_bytes || !tiled) {
+    if (p.acc_bytes) {
+      hipError_t e = hipMemset(ws + wl.acc, 0, p.acc_bytes);
+      if (e != hipSuccess) return hip_fail(e, "zeroing the split-reduction words");
+    }
+    hipError_t e = hipDeviceSynchronize();
     if (e != hipSuccess) return hip_fail(e, "synchronising after create");
   }
-  gemv_fn fn = nullptr;
-  size_t lds = 0;
-  hipError_t e = hipSuccess;
-  if (!p.mfma) {
-    fn = pick_gemv(d->g, d->row_group ? 1 : 0, d->table_precision, p.nb, p.waves, p.pf);
-    if (!fn) return fail(FLUXBIN_ERR_UNSUPPORTED, "no kernel for g = %d, batch width %d, %d waves", d->g, p.nb, p.waves);
-    lds = (size_t)lds_bytes(d->g, p.nb, p.cpb, entry_bytes(d));
-    e = hipFuncSetAttribute(reinterpret_cast<const void *>(fn), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return hip_fail(e, "setting the kernel's dynamic LDS size");
-  }
+  gemv_fn fn = pick_gemv(d->g, d->row_group ? 1 : 0, d->table_precision, p.nb, p.waves, p.pf);
+  if (!fn) return fail(FLUXBIN_ERR_UNSUPPORTED, "no kernel for g = %d, batch width %d, %d waves", d->g, p.nb, p.waves);
+  const size_t lds = (size_t)lds_bytes(d->g, p.nb, p.cpb, entry_bytes(d));
+  hipError_t e =
+      hipFuncSetAttribute(reinterpret_cast<const void *>(fn), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return hip_fail(e, "setting the kernel's dynamic LDS size");
   const int32_t *idx = d->sal_idx;
   if (d->ks == 0) {
     void *z = nullptr;
@@ -657,7 +699,7 @@ fluxbin_status fluxbin_create(const fluxbin_layer_desc *d, fluxbin_handle *out) 
   h->fn = fn;
   h->lds = lds;
   h->idx_or_dummy = idx;
-  h->d = *d;
+  h->d = hd;
   h->plan = p;
   const char *f = getenv("FLUXBIN_FAULT");
   h->fault_launch = f && strcmp(f, "launch") == 0;
@@ -674,12 +716,12 @@ fluxbin_status fluxbin_destroy(fluxbin_handle h) {
 namespace {
 
 void fill_plan(const fluxbin_layer_desc &d, const Plan &p, fluxbin_plan *plan) {
-  plan->rows_per_block = p.mfma ? kMfmaRowsPerBlock : p.waves * kTileRows;
+  plan->rows_per_block = p.waves * kTileRows;
   plan->chunks_per_block = p.cpb;
   plan->row_blocks = p.row_blocks;
   plan->splits = p.splits;
   plan->total_chunks = p.total_chunks;
-  plan->lds_bytes = p.mfma ? mfma_lds_bytes(1, 1, 2) : lds_bytes(d.g, p.nb, p.cpb, entry_bytes(&d));
+  plan->lds_bytes = lds_bytes(d.g, p.nb, p.cpb, entry_bytes(&d));
   plan->grid = (int64_t)p.row_blocks * p.splits;
 }
 
@@ -740,50 +782,6 @@ fluxbin_status fluxbin_build_lut(fluxbin_handle h, const uint16_t *x, int64_t ba
   return ok();
 }
 
-namespace {
-
-// The matrix-core route (instance for the batch: mfma_instance, next to the
-// kernel; the per-element arithmetic does not depend on it).
-fluxbin_status mfma_gemv(fluxbin_handle h, const uint16_t *x, uint16_t *y, int64_t batch, hipStream_t stream) {
-  const fluxbin_layer_desc &d = h->d;
-  const Plan &p = h->plan;
-  const MfmaInstance in = mfma_instance(batch, d.row_group ? 1 : 0);
-  if (!in.fn) return fail(FLUXBIN_ERR_UNSUPPORTED, "no matrix-core kernel for batch %lld", (long long)batch);
-  const int64_t rows_per_block = (int64_t)(kMfmaWaves / in.wb) * 32 * in.rb;
-  MfmaArgs a;
-  a.L = layer_args(d);
-  a.idx_or_dummy = h->idx_or_dummy;
-  a.x = x;
-  a.y = y;
-  a.part = p.splits > 1 ? reinterpret_cast<float *>(d.workspace) : nullptr;
-  a.n_pad = p.n_pad;
-  const int64_t groups = d.row_group ? cdiv(d.k, d.row_group) : 0;
-  a.rstride_g = d.row_group ? fluxbin_tiled_scale_elems(d.n, groups, 1) : d.n;
-  a.rstride_s = d.row_group && d.ks > 0 ? fluxbin_tiled_scale_elems(d.n, groups, kChunkCols / d.sal_group) : d.n;
-  a.cpb = p.cpb;
-  a.ranges_g = p.ranges_g;
-  a.ranges_s = p.ranges_s;
-  a.row_tiles = p.row_tiles;
-  a.row_blocks = (int32_t)cdiv(d.n, rows_per_block);
-  a.splits = p.splits;
-  a.batch = (int32_t)batch;
-  a.xvec = d.k % 8 == 0 && aligned(x, 16) && aligned(d.c_global, 16) ? 1 : 0;
-  a.sal_group = d.row_group && d.ks > 0 ? d.sal_group : kChunkCols;
-  const dim3 grid((unsigned)((int64_t)a.row_blocks * p.splits), (unsigned)cdiv(batch, 32 * in.nbt * in.wb));
-  hipLaunchKernelGGL(in.fn, grid, dim3(kMfmaWaves * 64), 0, stream, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return hip_fail(e, "matrix-core gemv launch");
-  if (p.splits > 1) {
-    hipLaunchKernelGGL(mfma_finalize_kernel, dim3(grid_for(batch * d.n)), dim3(256), 0, stream, a.part, p.splits,
-                       (int32_t)batch, d.n, p.n_pad, y);
-    e = hipGetLastError();
-    if (e != hipSuccess) return hip_fail(e, "matrix-core finalize launch");
-  }
-  return ok();
-}
-
-}  // namespace
-
 fluxbin_status fluxbin_gemv(fluxbin_handle h, const uint16_t *x, uint16_t *y, int64_t batch, void *stream) {
   if (!h) return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "handle is NULL");
   if (batch < 0 || batch > h->d.max_batch)
@@ -794,20 +792,21 @@ fluxbin_status fluxbin_gemv(fluxbin_handle h, const uint16_t *x, uint16_t *y, in
   if (h->fault_launch) return fail(FLUXBIN_ERR_HIP, "injected launch fault (FLUXBIN_FAULT=launch)");
   const fluxbin_layer_desc &d = h->d;
   const Plan &p = h->plan;
-  if (p.mfma) return mfma_gemv(h, x, y, batch, (hipStream_t)stream);
   GemvArgs a;
-  a.L = layer_args(d);
   gemv_segments(d, a.seg);
   a.idx_or_dummy = h->idx_or_dummy;
+  a.n = d.n;
+  a.k = d.k;
+  a.n_pad = p.n_pad;
+  a.kb = d.kb;
+  a.ks = d.ks;
+  a.rpg = p.rpg;
+  a.rps = p.rps;
   a.cpb = p.cpb;
-  a.total_chunks = p.total_chunks;
-  a.gsplits = p.gsplits;
-  a.gchunks = p.gchunks;
-  a.sal16 = d.row_group && d.ks > 0 && d.sal_group == 8 ? 1 : 0;
   a.row_tiles = p.row_tiles;
   a.row_blocks = p.row_blocks;
   a.splits = p.splits;
-  a.n_pad = p.n_pad;
+  a.sal16 = d.row_group && d.ks > 0 && d.sal_group == 8 ? 1 : 0;
   uint64_t *acc = p.splits > 1 ? reinterpret_cast<uint64_t *>(d.workspace) : nullptr;
   const int64_t grid = (int64_t)p.row_blocks * p.splits;
   // one launch per group of p.nb batch rows (a prefill batch runs as several groups,
@@ -821,6 +820,76 @@ fluxbin_status fluxbin_gemv(fluxbin_handle h, const uint16_t *x, uint16_t *y, in
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "gemv launch");
   }
+  return ok();
+}
+
+fluxbin_status fluxbin_reset_workspace(fluxbin_handle h, void *stream) {
+  if (!h) return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "handle is NULL");
+  if (h->fault_launch) return fail(FLUXBIN_ERR_HIP, "injected launch fault (FLUXBIN_FAULT=launch)");
+  const Plan &p = h->plan;
+  if (!p.acc_bytes) return ok();
+  const int64_t words = (int64_t)(p.acc_bytes / sizeof(uint64_t));
+  hipLaunchKernelGGL(zero_words_kernel, dim3(grid_for(words)), dim3(256), 0, (hipStream_t)stream,
+                     reinterpret_cast<uint64_t *>(h->d.workspace), words);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "workspace reset launch");
+  return ok();
+}
+
+fluxbin_status fluxbin_probe_stream_read(const void *buf, int64_t bytes, int32_t depth, int64_t workgroups,
+                                         uint32_t never, uint32_t *sink, void *stream) {
+  if (!buf || !sink) return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "NULL pointer");
+  if (bytes < 1024 || bytes % 16) return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "bytes = %lld (a multiple of 16, >= 1024)",
+                                              (long long)bytes);
+  if (!aligned(buf, 16)) return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "buf not 16-byte aligned");
+  if (workgroups < 1 || workgroups > 65536)
+    return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "workgroups = %lld (1..65536)", (long long)workgroups);
+  const int64_t n16 = bytes / 16, waves = workgroups * 4;
+  const int64_t per_wave = cdiv(cdiv(n16, waves), 64) * 64;  // whole 1 KiB blocks per wave
+  const u32x4 *b = static_cast<const u32x4 *>(buf);
+  const dim3 grid((unsigned)workgroups), block(256);
+  hipStream_t st = (hipStream_t)stream;
+  switch (depth) {
+    case 1: hipLaunchKernelGGL(stream_read_kernel<1>, grid, block, 0, st, b, n16, per_wave, never, sink); break;
+    case 2: hipLaunchKernelGGL(stream_read_kernel<2>, grid, block, 0, st, b, n16, per_wave, never, sink); break;
+    case 4: hipLaunchKernelGGL(stream_read_kernel<4>, grid, block, 0, st, b, n16, per_wave, never, sink); break;
+    case 8: hipLaunchKernelGGL(stream_read_kernel<8>, grid, block, 0, st, b, n16, per_wave, never, sink); break;
+    case 16: hipLaunchKernelGGL(stream_read_kernel<16>, grid, block, 0, st, b, n16, per_wave, never, sink); break;
+    default: return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "depth = %d (1, 2, 4, 8 or 16)", depth);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "stream probe launch");
+  return ok();
+}
+
+fluxbin_status fluxbin_probe_empty(int64_t workgroups, int32_t threads, void *stream) {
+  if (workgroups < 1 || workgroups > (1 << 20))
+    return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "workgroups = %lld (1..2^20)", (long long)workgroups);
+  if (threads < 1 || threads > 1024) return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "threads = %d (1..1024)", threads);
+  hipLaunchKernelGGL(empty_kernel, dim3((unsigned)workgroups), dim3(threads), 0, (hipStream_t)stream);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "empty probe launch");
+  return ok();
+}
+
+fluxbin_status fluxbin_probe_lds_lookup(int32_t g, int32_t nb, int64_t workgroups, int32_t iters, float never,
+                                        float *sink, void *stream) {
+  if (!sink) return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "sink is NULL");
+  if (workgroups < 1 || workgroups > 65536 || iters < 1)
+    return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "workgroups = %lld (1..65536), iters = %d (>= 1)", (long long)workgroups,
+                iters);
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e;
+  if (g == 4 && nb == 1) e = launch_lookup_probe<4, 1>(workgroups, iters, never, sink, st);
+  else if (g == 4 && nb == 2) e = launch_lookup_probe<4, 2>(workgroups, iters, never, sink, st);
+  else if (g == 4 && nb == 4) e = launch_lookup_probe<4, 4>(workgroups, iters, never, sink, st);
+  else if (g == 4 && nb == 8) e = launch_lookup_probe<4, 8>(workgroups, iters, never, sink, st);
+  else if (g == 4 && nb == 16) e = launch_lookup_probe<4, 16>(workgroups, iters, never, sink, st);
+  else if (g == 8 && nb == 1) e = launch_lookup_probe<8, 1>(workgroups, iters, never, sink, st);
+  else if (g == 8 && nb == 2) e = launch_lookup_probe<8, 2>(workgroups, iters, never, sink, st);
+  else if (g == 8 && nb == 4) e = launch_lookup_probe<8, 4>(workgroups, iters, never, sink, st);
+  else return fail(FLUXBIN_ERR_UNSUPPORTED, "g = %d, nb = %d (g 4: nb 1, 2, 4, 8, 16; g 8: nb 1, 2, 4)", g, nb);
+  if (e != hipSuccess) return hip_fail(e, "lookup probe launch");
   return ok();
 }
 

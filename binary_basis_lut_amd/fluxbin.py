@@ -20,12 +20,11 @@ if not LIB_PATH.exists():
 
 _lib = ctypes.CDLL(str(LIB_PATH))
 
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
 LAYOUT_ROWMAJOR, LAYOUT_TILED = 0, 1
 TABLE_F32, TABLE_F16 = 0, 1
-COMPUTE_LUT, COMPUTE_MFMA = 0, 1
 DT_I8, DT_F16, DT_BITS = 0, 1, 2
 
 P = ctypes.c_void_p
@@ -41,7 +40,7 @@ class LayerDesc(ctypes.Structure):
         ("bits_sal", P), ("r_sal", P), ("c_sal", P), ("sal_idx", P),
         ("workspace", P), ("workspace_bytes", ctypes.c_size_t),
         ("chunks_per_block", I32), ("waves_per_block", I32),
-        ("row_group", I32), ("sal_group", I32), ("table_precision", I32), ("compute", I32),
+        ("row_group", I32), ("sal_group", I32), ("table_precision", I32), ("layout", I32),
     ]
 
 
@@ -86,7 +85,11 @@ _decl("fluxbin_plan_of", ctypes.c_int, [ctypes.POINTER(LayerDesc), ctypes.POINTE
 _decl("fluxbin_lut_size", ctypes.c_int, [P, I64, ctypes.POINTER(ctypes.c_size_t)])
 _decl("fluxbin_build_lut", ctypes.c_int, [P, P, I64, P, P])
 _decl("fluxbin_gemv", ctypes.c_int, [P, P, P, I64, P])
+_decl("fluxbin_reset_workspace", ctypes.c_int, [P, P])
 _decl("fluxbin_dense_gemv_f16", ctypes.c_int, [P, I64, I64, P, P, I64, P])
+_decl("fluxbin_probe_stream_read", ctypes.c_int, [P, I64, I32, I64, ctypes.c_uint32, P, P])
+_decl("fluxbin_probe_empty", ctypes.c_int, [I64, I32, P])
+_decl("fluxbin_probe_lds_lookup", ctypes.c_int, [I32, I32, I64, I32, ctypes.c_float, P, P])
 _decl("fluxbin_decomp_workspace_size", ctypes.c_int, [I64, I64, I32, ctypes.POINTER(ctypes.c_size_t)])
 _decl("fluxbin_decompose", ctypes.c_int, [P, I64, I64, I32, I32, P, P, P, P, P, P, P, P, ctypes.c_size_t, P])
 _decl("fluxbin_decomp_row_scales", ctypes.c_int, [P, I64, I64, I32, I32, P, P, P, P, P, P, ctypes.c_size_t, P])
@@ -100,7 +103,8 @@ SYMBOLS = [
     "fluxbin_relayout", "fluxbin_tiled_scale_elems", "fluxbin_relayout_scales", "fluxbin_vcm_gather",
     "fluxbin_workspace_size", "fluxbin_create", "fluxbin_destroy", "fluxbin_get_plan", "fluxbin_plan_of",
     "fluxbin_lut_size",
-    "fluxbin_build_lut", "fluxbin_gemv", "fluxbin_dense_gemv_f16", "fluxbin_decomp_workspace_size",
+    "fluxbin_build_lut", "fluxbin_gemv", "fluxbin_reset_workspace", "fluxbin_dense_gemv_f16",
+    "fluxbin_probe_stream_read", "fluxbin_probe_empty", "fluxbin_probe_lds_lookup", "fluxbin_decomp_workspace_size",
     "fluxbin_decompose", "fluxbin_decomp_row_scales", "fluxbin_decomp_col_scales", "fluxbin_decomp_signs",
     "fluxbin_decomp_residual_signs", "fluxbin_decomp_error",
 ]
@@ -212,6 +216,24 @@ def fluxbin_gemv(handle, x, y, batch, stream=None):
     _check(_lib.fluxbin_gemv(handle, _ptr(x), _ptr(y), batch, _stream(stream)), "fluxbin_gemv")
 
 
+def fluxbin_reset_workspace(handle, stream=None):
+    _check(_lib.fluxbin_reset_workspace(handle, _stream(stream)), "fluxbin_reset_workspace")
+
+
+def fluxbin_probe_stream_read(buf, nbytes, depth, workgroups, never, sink, stream=None):
+    _check(_lib.fluxbin_probe_stream_read(_ptr(buf), nbytes, depth, workgroups, never, _ptr(sink), _stream(stream)),
+           "fluxbin_probe_stream_read")
+
+
+def fluxbin_probe_empty(workgroups, threads, stream=None):
+    _check(_lib.fluxbin_probe_empty(workgroups, threads, _stream(stream)), "fluxbin_probe_empty")
+
+
+def fluxbin_probe_lds_lookup(g, nb, workgroups, iters, never, sink, stream=None):
+    _check(_lib.fluxbin_probe_lds_lookup(g, nb, workgroups, iters, never, _ptr(sink), _stream(stream)),
+           "fluxbin_probe_lds_lookup")
+
+
 def fluxbin_dense_gemv_f16(w, n, k, x, y, batch, stream=None):
     _check(_lib.fluxbin_dense_gemv_f16(_ptr(w), n, k, _ptr(x), _ptr(y), batch, _stream(stream)),
            "fluxbin_dense_gemv_f16")
@@ -269,40 +291,49 @@ def raw_status(name: str, *args) -> int:
 class DeviceLayer:
     """Upload one synthetic layer (binary_basis_lut_amd.inputs.Layer) and create its handle.
 
-    Canonical sign words are copied to the device and converted to the tiled
-    layout with fluxbin_relayout; block-wise row scales ([basis][n][groups])
-    are converted to the tiled scale layout with fluxbin_relayout_scales.
-    Scales, index and workspace are torch CUDA tensors owned by this object,
-    which keeps them alive for the handle.
+    layout=LAYOUT_TILED (default): canonical sign words are copied to the
+    device and converted to the tiled layout with fluxbin_relayout, block-wise
+    row scales ([basis][n][groups]) to the tiled scale layout with
+    fluxbin_relayout_scales.  layout=LAYOUT_ROWMAJOR: the canonical words and
+    scales are passed as they are and fluxbin_create converts them into the
+    workspace.  Scales, index and workspace are torch CUDA tensors owned by
+    this object, which keeps them alive for the handle.
     """
 
     def __init__(self, layer, max_batch: int = 1, chunks_per_block: int = 0, waves_per_block: int = 0,
-                 device="cuda", table_precision: int = TABLE_F32, compute: int = COMPUTE_LUT):
+                 device="cuda", table_precision: int = TABLE_F32, layout: int = LAYOUT_TILED):
         import numpy as np
         import torch
 
         self.layer = layer
         self.max_batch = max_batch
         self.table_precision = table_precision
-        self.compute = compute
+        self.layout = layout
         dev = torch.device(device)
 
         def up(a, dtype):
             return torch.from_numpy(np.ascontiguousarray(a).view(dtype)).to(dev)
 
         n, k, s = layer.n, layer.k, layer.s
-        tw_g = fluxbin_tiled_words(n, k)
-        self.bits_g = torch.zeros(max(layer.kb * tw_g, 4), dtype=torch.int32, device=dev)
-        canon = up(layer.bits_g, np.int32)
-        for b in range(layer.kb):
-            fluxbin_relayout(canon[b], n, k, LAYOUT_ROWMAJOR, LAYOUT_TILED, self.bits_g[b * tw_g:(b + 1) * tw_g])
-        del canon
+        rowmajor = layout == LAYOUT_ROWMAJOR
         rgroup = int(getattr(layer, "row_group", 0) or 0)
         self.row_group = rgroup
         self.sal_group = int(getattr(layer, "sal_group", 0) or 0) if layer.ks else 0
 
+        def tiled_bits(canon_np, bases, cols):
+            if rowmajor:
+                return up(canon_np, np.int32)
+            tw = fluxbin_tiled_words(n, cols)
+            out = torch.zeros(max(bases * tw, 4), dtype=torch.int32, device=dev)
+            canon = up(canon_np, np.int32)
+            for b in range(bases):
+                fluxbin_relayout(canon[b], n, cols, LAYOUT_ROWMAJOR, LAYOUT_TILED, out[b * tw:(b + 1) * tw])
+            return out
+
         def tiled_scales(r, bases, m):
             """[bases][n][groups] canonical -> concatenated tiled blocks (m groups per chunk)."""
+            if rowmajor:
+                return up(r, np.int16)
             groups = r.shape[2]
             te = fluxbin_tiled_scale_elems(n, groups, m)
             out = torch.zeros(max(bases * te, 8), dtype=torch.int16, device=dev)
@@ -312,16 +343,11 @@ class DeviceLayer:
                                         out[b * te:(b + 1) * te])
             return out
 
+        self.bits_g = tiled_bits(layer.bits_g, layer.kb, k)
         self.r_g = tiled_scales(layer.r_g, layer.kb, 1) if rgroup else up(layer.r_g, np.int16)
         self.c_g = up(layer.c_g, np.int16)
         if layer.ks:
-            tw_s = fluxbin_tiled_words(n, s)
-            self.bits_s = torch.zeros(layer.ks * tw_s, dtype=torch.int32, device=dev)
-            canon_s = up(layer.bits_s, np.int32)
-            for b in range(layer.ks):
-                fluxbin_relayout(canon_s[b], n, s, LAYOUT_ROWMAJOR, LAYOUT_TILED,
-                                 self.bits_s[b * tw_s:(b + 1) * tw_s])
-            del canon_s
+            self.bits_s = tiled_bits(layer.bits_s, layer.ks, s)
             self.r_s = (tiled_scales(layer.r_s, layer.ks, 128 // self.sal_group) if rgroup
                         else up(layer.r_s, np.int16))
             self.c_s = up(layer.c_s, np.int16)
@@ -352,11 +378,14 @@ class DeviceLayer:
         d.row_group = self.row_group
         d.sal_group = self.sal_group
         d.table_precision = self.table_precision
-        d.compute = self.compute
+        d.layout = self.layout
         return d
 
     def gemv(self, x, y, batch=None, stream=None):
         fluxbin_gemv(self.handle, x, y, x.shape[0] if batch is None else batch, stream)
+
+    def reset_workspace(self, stream=None):
+        fluxbin_reset_workspace(self.handle, stream)
 
     def close(self):
         if getattr(self, "handle", None):

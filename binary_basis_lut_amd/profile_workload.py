@@ -23,7 +23,23 @@ profiles/ (each summary names the exact command).  Two modes:
 
   python3 -m binary_basis_lut_amd.profile_workload copy --bytes 1073741824 --reps 4
       a plain device-to-device copy of known size (torch's copy kernel): the
-      reference that scales the FETCH_SIZE / WRITE_SIZE counters to bytes.
+      reference that scales the FETCH_SIZE / WRITE_SIZE counters to bytes;
+
+  python3 -m binary_basis_lut_amd.profile_workload stream --bytes 1073741824 --reps 10
+      the HBM read rate of the GEMV's access pattern (fluxbin_probe_stream_read:
+      1 KiB per wave load, non-temporal, each wave a contiguous span) over a
+      buffer larger than the 256 MB Infinity Cache, at every in-flight depth and
+      a few grid sizes: GB/s per configuration and the best one;
+
+  python3 -m binary_basis_lut_amd.profile_workload empty --workgroups 528 --threads 256 --nodes 256 --reps 20
+      the launch floor: a HIP graph of `nodes` empty kernels of the given grid,
+      microseconds per node;
+
+  python3 -m binary_basis_lut_amd.profile_workload lookup --iters 2000 --reps 5
+      the table-lookup rate alone (fluxbin_probe_lds_lookup) for g = 4 at 1, 2,
+      4, 8, 16 batch rows and g = 8 at 1, 2, 4: lookups per second, per CU per
+      clock (2.4 GHz), and the packed-weight GB/s that rate would sustain at
+      b = 1 (one lookup per g bits).
 """
 from __future__ import annotations
 
@@ -60,8 +76,7 @@ def run_gemv(args) -> None:
         if args.g:
             lay.g = args.g  # table width is a kernel choice: the packed sign bits do not depend on it
         dls.append(F.DeviceLayer(lay, max_batch=args.batch, chunks_per_block=args.chunks_per_block,
-                                 waves_per_block=args.waves_per_block, table_precision=args.table_precision,
-                                 compute=F.COMPUTE_MFMA if args.compute == "mfma" else F.COMPUTE_LUT))
+                                 waves_per_block=args.waves_per_block, table_precision=args.table_precision))
         xs.append(torch.from_numpy(x.view(np.int16)).cuda())
         ys.append(torch.empty((args.batch, lay.n), dtype=torch.int16, device="cuda"))
     stream = torch.cuda.Stream()
@@ -88,8 +103,6 @@ def run_gemv(args) -> None:
     wb = (A.grouped_weight_bytes(lay.n, lay.k, lay.kb, lay.ks, 128, args.sal_group) if blockwise
           else A.weight_bytes(lay.n, lay.k, lay.s, lay.kb, lay.ks))
     tables = "fp16 tables" if args.table_precision else "fp32 tables"
-    if args.compute == "mfma":
-        tables = "matrix cores"
     print(f"gemv workload {args.workload} shape {args.shape} ({sh.name} {sh.k}->{sh.n}, {args.format}, {tables}, "
           f"batch {args.batch}): "
           f"{args.sets} sets x {args.reps} replays, {us:.3f} us per call, {wb / us / 1e3:.1f} GB/s of "
@@ -182,6 +195,98 @@ def run_copy(args) -> None:
     print(f"copy: {args.reps} x {n * 4} bytes read and written", flush=True)
 
 
+def _events():
+    import torch
+    return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+
+def run_stream(args) -> None:
+    import torch
+
+    from binary_basis_lut_amd import fluxbin as F
+
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    buf = torch.ones(args.bytes // 4, dtype=torch.int32, device="cuda")
+    best = (0.0, None)
+    for wg_per_cu in (4, 8, 16):
+        wgs = cus * wg_per_cu
+        sink = torch.zeros(wgs * 256, dtype=torch.int32, device="cuda")
+        for depth in (1, 2, 4, 8, 16):
+            F.fluxbin_probe_stream_read(buf, args.bytes, depth, wgs, 0x9E3779B9, sink)
+            torch.cuda.synchronize()
+            e0, e1 = _events()
+            e0.record()
+            for _ in range(args.reps):
+                F.fluxbin_probe_stream_read(buf, args.bytes, depth, wgs, 0x9E3779B9, sink)
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / args.reps
+            gbs = args.bytes / us / 1e3
+            print(f"stream read {args.bytes} B, {wgs} workgroups x 4 waves, depth {depth}: {us:.1f} us, "
+                  f"{gbs:.0f} GB/s", flush=True)
+            if gbs > best[0]:
+                best = (gbs, (wgs, depth))
+    print(f"stream read best: {best[0]:.0f} GB/s at {best[1][0]} workgroups, depth {best[1][1]} "
+          f"({cus} CUs)", flush=True)
+
+
+def run_empty(args) -> None:
+    import torch
+
+    from binary_basis_lut_amd import fluxbin as F
+
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        F.fluxbin_probe_empty(args.workgroups, args.threads, stream=stream)
+    stream.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(graph, stream=stream):
+            for _ in range(args.nodes):
+                F.fluxbin_probe_empty(args.workgroups, args.threads, stream=stream)
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = _events()
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for _ in range(args.reps):
+            graph.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (args.reps * args.nodes)
+    print(f"empty kernel {args.workgroups} x {args.threads} threads: {us:.3f} us per graph node "
+          f"({args.nodes} nodes x {args.reps} replays)", flush=True)
+
+
+def run_lookup(args) -> None:
+    import torch
+
+    from binary_basis_lut_amd import fluxbin as F
+
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    wgs = cus * 8  # 32 waves per CU
+    sink = torch.zeros(wgs * 256, dtype=torch.float32, device="cuda")
+    for g, nb in ((4, 1), (4, 2), (4, 4), (4, 8), (4, 16), (8, 1), (8, 2), (8, 4)):
+        F.fluxbin_probe_lds_lookup(g, nb, wgs, args.iters, -1.0, sink)
+        torch.cuda.synchronize()
+        e0, e1 = _events()
+        e0.record()
+        for _ in range(args.reps):
+            F.fluxbin_probe_lds_lookup(g, nb, wgs, args.iters, -1.0, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        s = e0.elapsed_time(e1) * 1e-3 / args.reps
+        lookups = wgs * 256 * args.iters * nb * 128 // g
+        rate = lookups / s
+        per_cu_clk = rate / cus / 2.4e9
+        # at b = nb the weights of one lookup-set are g bits per row: bytes/s = rate / nb * g / 8
+        gbs = rate / nb * g / 8 / 1e9
+        print(f"lookups g={g} batch rows={nb}: {rate / 1e12:.3f} T lookups/s, {per_cu_clk:.2f} per CU per clock, "
+              f"weight stream it sustains {gbs:.0f} GB/s", flush=True)
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     sub = ap.add_subparsers(dest="mode", required=True)
@@ -198,7 +303,6 @@ def main() -> int:
     g.add_argument("--kb", type=int, default=2, help="blockwise: global bases")
     g.add_argument("--ks", type=int, default=2, help="blockwise: salient bases")
     g.add_argument("--sal-group", type=int, default=8, choices=[8, 16])
-    g.add_argument("--compute", choices=["lut", "mfma"], default="lut")
     g.add_argument("--g", type=int, default=0, choices=[0, 4, 8], help="table width (0: the workload's)")
     dp = sub.add_parser("decompose")
     dp.add_argument("--n", type=int, default=4096)
@@ -215,8 +319,20 @@ def main() -> int:
     c = sub.add_parser("copy")
     c.add_argument("--bytes", type=int, default=1 << 30)
     c.add_argument("--reps", type=int, default=4)
+    st = sub.add_parser("stream")
+    st.add_argument("--bytes", type=int, default=1 << 30)
+    st.add_argument("--reps", type=int, default=10)
+    em = sub.add_parser("empty")
+    em.add_argument("--workgroups", type=int, default=528)
+    em.add_argument("--threads", type=int, default=256)
+    em.add_argument("--nodes", type=int, default=256)
+    em.add_argument("--reps", type=int, default=20)
+    lk = sub.add_parser("lookup")
+    lk.add_argument("--iters", type=int, default=2000)
+    lk.add_argument("--reps", type=int, default=5)
     args = ap.parse_args()
-    {"gemv": run_gemv, "decompose": run_decompose, "dense": run_dense, "copy": run_copy}[args.mode](args)
+    {"gemv": run_gemv, "decompose": run_decompose, "dense": run_dense, "copy": run_copy, "stream": run_stream,
+     "empty": run_empty, "lookup": run_lookup}[args.mode](args)
     return 0
 
 

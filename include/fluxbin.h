@@ -41,11 +41,11 @@
  *     outputs are left untouched and fluxbin_last_error() holds a
  *     thread-local message.  Device faults surface at the caller's next
  *     synchronisation.  No C++ exception crosses this boundary.
- *   - fluxbin_build_lut launches one kernel and fluxbin_gemv one kernel per
- *     group of batch rows (LUT route: 16 at g = 4, 4 at g = 8; one launch up
- *     to that batch; matrix-core route: one, plus a summing launch when the plan
- *     splits the columns); neither ever allocates, copies, sets memory or synchronises, so
- *     they may be captured in a HIP graph.  fluxbin_create does synchronise.
+ *   - fluxbin_build_lut and fluxbin_reset_workspace launch one kernel and
+ *     fluxbin_gemv one kernel per group of batch rows (16 at g = 4, 4 at
+ *     g = 8; one launch up to that batch); none of them ever allocates,
+ *     copies, sets memory or synchronises, so they may be captured in a HIP
+ *     graph.  fluxbin_create does synchronise.
  */
 #ifndef FLUXBIN_H
 #define FLUXBIN_H
@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define FLUXBIN_ABI_VERSION 4
+#define FLUXBIN_ABI_VERSION 5
 
 typedef enum {
   FLUXBIN_OK = 0,
@@ -91,16 +91,6 @@ typedef enum {
   FLUXBIN_TABLE_F16 = 1  /* fp16 entries: each entry summed in fp32, rounded to fp16 (nearest even) */
 } fluxbin_table_precision;
 
-/* How fluxbin_gemv evaluates a handle's product (fluxbin_layer_desc.compute).
- * The choice is made per handle, not per call, so that the result of a batch
- * row never depends on the batch it came with. */
-typedef enum {
-  FLUXBIN_COMPUTE_LUT = 0, /* table lookups in LDS (the GEMV of the FluxBin summary, section 3 bullet
-                              "LUT-Based GEMV Kernel"): decode, batches of a few rows */
-  FLUXBIN_COMPUTE_MFMA = 1 /* matrix cores: the sign bits expanded in registers to +-c (exact in fp16)
-                              against fp16 x, fp32 accumulation; prefill batches (tens of rows and up) */
-} fluxbin_compute;
-
 /* Element kinds for fluxbin_vcm_gather. */
 typedef enum {
   FLUXBIN_DT_I8 = 0,  /* int8 elements, [rows][cols] */
@@ -125,26 +115,30 @@ typedef struct {
   int64_t max_batch;     /* largest batch a call may pass: 1..128.  A workgroup serves up to 16 batch
                             rows (g = 8: 4); wider batches run as groups of that many rows, each
                             building its own tables and streaming the weights again */
-  const uint32_t *bits_global; /* TILED words, kb blocks of fluxbin_tiled_words(n, k), 16-B aligned */
+  const uint32_t *bits_global; /* kb blocks of sign words in `layout`: TILED, fluxbin_tiled_words(n, k)
+                                  words each, 16-B aligned; or ROWMAJOR, n * ceil(k/32) words each */
   const uint16_t *r_global;    /* fp16 row scales: [kb][n], or block-wise (see row_group) */
   const uint16_t *c_global;    /* fp16 [kb][k] column scales */
-  const uint32_t *bits_sal;    /* TILED words, ks blocks of fluxbin_tiled_words(n, s), 16-B aligned */
+  const uint32_t *bits_sal;    /* ks blocks over the s compact columns, in `layout` like bits_global */
   const uint16_t *r_sal;       /* fp16 [ks][n], or block-wise (see row_group) */
   const uint16_t *c_sal;       /* fp16 [ks][s], compact order (entry c belongs to column sal_idx[c]) */
   const int32_t *sal_idx;      /* [s] salient columns, strictly ascending, in [0, k) */
-  void *workspace;             /* >= fluxbin_workspace_size() bytes, 256-B aligned; may be NULL if that size is 0 */
+  void *workspace;             /* >= fluxbin_workspace_size() bytes, 256-B aligned, caller-owned; may be NULL
+                                  if that size is 0 */
   size_t workspace_bytes;
-  int32_t chunks_per_block;    /* tuning: 0 = automatic, else 1..32 128-column chunks per workgroup; the
-                                  limit for a given g, batch width and waves_per_block follows from 80 KiB
-                                  of tables per workgroup and 8 table-build inputs per thread
-                                  (FLUXBIN_ERR_UNSUPPORTED beyond it) */
+  int32_t chunks_per_block;    /* tuning: 0 = automatic, else 1..32: the longest column range of one
+                                  workgroup, in 128-column chunks (each segment is cut into equal ranges no
+                                  longer than this); the limit for a given g, batch width and
+                                  waves_per_block follows from 80 KiB of tables per workgroup and the table
+                                  inputs one thread stages (FLUXBIN_ERR_UNSUPPORTED beyond it) */
   int32_t waves_per_block;     /* tuning: 0 = automatic, else 4 or 8 (64 output rows per wave) */
   int32_t row_group;           /* row-scale format.  0: one scale per row per basis, r_global fp16 [kb][n],
                                   r_sal fp16 [ks][n].  128: block-wise, one scale per row per basis per group
-                                  of 128 columns of x; with G = ceil(k/128), r_global holds kb blocks of
-                                  fluxbin_tiled_scale_elems(n, G, 1) and r_sal (16-B aligned) ks blocks of
-                                  fluxbin_tiled_scale_elems(n, G, 128/sal_group), each the TILED scale layout
-                                  of a [n][G] matrix (see fluxbin_relayout_scales).  Other values:
+                                  of 128 columns of x; with G = ceil(k/128), r_global holds kb and r_sal ks
+                                  [n][G] fp16 matrices in `layout`: TILED, blocks of
+                                  fluxbin_tiled_scale_elems(n, G, 1) (global) and of
+                                  fluxbin_tiled_scale_elems(n, G, 128/sal_group) (salient, 16-B aligned), see
+                                  fluxbin_relayout_scales; or ROWMAJOR, n * G each.  Other values:
                                   FLUXBIN_ERR_UNSUPPORTED */
   int32_t sal_group;           /* block-wise with ks > 0: salient columns per 128-column group, 8 or 16 (a
                                   multiple of g).  S must take exactly sal_group columns from every group:
@@ -153,23 +147,23 @@ typedef struct {
   int32_t table_precision;     /* fluxbin_table_precision of the GEMV's tables.  FLUXBIN_TABLE_F16 stores
                                   the scale-fused tables in fp16 (quantised tables, LUT Tensor Core notes,
                                   section 3.1.3): half the LDS per table; each entry adds one fp16
-                                  rounding, |error| <= 2^-11 |entry| (accumulation stays fp32).  Ignored by
-                                  FLUXBIN_COMPUTE_MFMA, which builds no tables */
-  int32_t compute;             /* fluxbin_compute.  FLUXBIN_COMPUTE_MFMA ignores g and table_precision,
-                                  takes chunks_per_block as the 128-column chunks of one segment per
-                                  workgroup (a workgroup never spans two segments) and needs
-                                  waves_per_block 0 or 4 (256 rows per workgroup) */
+                                  rounding, |error| <= 2^-11 |entry| (accumulation stays fp32) */
+  int32_t layout;              /* fluxbin_layout of the sign words and of block-wise row scales.  TILED:
+                                  streamed as given.  ROWMAJOR (the canonical words): fluxbin_create converts
+                                  them into the workspace (fluxbin_workspace_size counts that copy), and the
+                                  caller's buffers are not read again after it returns */
 } fluxbin_layer_desc;
 
 /* How a handle splits the work (read-only introspection). */
 typedef struct {
-  int32_t rows_per_block;   /* output rows per workgroup (64 per wave; matrix cores: 256) */
-  int32_t chunks_per_block; /* 128-column chunks per workgroup */
+  int32_t rows_per_block;   /* output rows per workgroup (64 per wave) */
+  int32_t chunks_per_block; /* most 128-column chunks in one workgroup's column range */
   int32_t row_blocks;       /* workgroups along the rows */
-  int32_t splits;           /* workgroups along the concatenated columns of all segments */
+  int32_t splits;           /* column ranges: every segment is cut into ranges of consecutive chunks of
+                               equal length (within one chunk), none longer than chunks_per_block */
   int32_t total_chunks;     /* sum over segments of ceil(len/128) */
   int32_t lds_bytes;        /* LDS per workgroup at max_batch */
-  int64_t grid;             /* workgroups per fluxbin_gemv launch (matrix cores: per 32 batch rows) */
+  int64_t grid;             /* workgroups per fluxbin_gemv launch (per group of batch rows) */
 } fluxbin_plan;
 
 int32_t fluxbin_abi_version(void);
@@ -225,16 +219,18 @@ fluxbin_status fluxbin_relayout_scales(const uint16_t *src, int64_t rows, int64_
 fluxbin_status fluxbin_vcm_gather(const int32_t *idx, int64_t s, const void *src, int64_t rows, int64_t cols,
                                   int32_t dtype, void *dst, void *stream);
 
-/* Workspace bytes a layer needs (host-side arithmetic, no device access):
- * 0 when the plan has one column range per row (fluxbin_plan.splits == 1);
- * else LUT route: max_batch * ceil(n/64)*64 packed 64-bit reduction words
- * (zeroed by fluxbin_create, left zero by every call); matrix-core route:
- * splits * max_batch * ceil(n/64)*64 fp32 partial sums (no zeroing). */
+/* Workspace bytes a layer needs (host-side arithmetic, no device access): the
+ * split-reduction words, max_batch * ceil(n/64)*64 packed 64-bit words when the
+ * plan cuts a row's columns into several ranges (fluxbin_plan.splits > 1,
+ * zeroed by fluxbin_create and left zero by every completed call), then, when
+ * desc.layout is ROWMAJOR, the TILED copies fluxbin_create makes of the sign
+ * words (and of block-wise row scales), each region 256-B aligned. */
 fluxbin_status fluxbin_workspace_size(const fluxbin_layer_desc *d, size_t *bytes);
 
-/* Validate the description (copies sal_idx to the host to check it), zero the
- * workspace's split-reduction words, and return a handle.  Synchronises the
- * device; not capturable.  The environment variable FLUXBIN_FAULT=launch,
+/* Validate the description (copies sal_idx to the host to check it), convert
+ * ROWMAJOR sign words and block-wise scales into the workspace, zero the
+ * split-reduction words, and return a handle.  Synchronises the device; not
+ * capturable.  The environment variable FLUXBIN_FAULT=launch,
  * read here, makes every launching call of this handle fail with
  * FLUXBIN_ERR_HIP before launching (error-path testing). */
 fluxbin_status fluxbin_create(const fluxbin_layer_desc *d, fluxbin_handle *out);
@@ -264,31 +260,65 @@ fluxbin_status fluxbin_build_lut(fluxbin_handle h, const uint16_t *x, int64_t ba
 
 /* y = the layer applied to x.  x: fp16 [batch][k], y: fp16 [batch][n]
  * (round to nearest even), 0 <= batch <= max_batch (0 launches nothing).
- * FLUXBIN_COMPUTE_LUT: tables and accumulation are fp32.  Per-row scales multiply a segment's
- * accumulated sum; block-wise scales multiply the sum of each global chunk
- * (one group) and of each 8 salient columns (one group, or half of one when
- * sal_group = 16), before those sums are added.  When the handle's plan splits the
- * columns over several workgroups (fluxbin_plan.splits > 1), the partial
- * sums of a row are combined exactly as 2^-30 fixed-point integers: each
- * partial is rounded to 2^-31 (absolute) and partials beyond +-2^17 saturate.
- * FLUXBIN_COMPUTE_MFMA (one launch, two with splits): each weight is used as +-c_j
- * in fp16 against x in fp16, products exact, sums accumulated in fp32 by
- * the matrix cores 16 columns at a time; a per-row scale multiplies the sum
- * of a workgroup's range of one segment, a block-wise scale the sum of each
- * global chunk and of each salient group (sal_group columns); when a row has
- * several ranges (fluxbin_plan.splits, at least kb + ks then) their fp32
- * partials are added in range order by a second launch.
- * Uses the handle's workspace: at most one call per handle may be in flight
- * at a time (use one handle per concurrent stream).  For a given handle the
- * result of row b does not depend on the other rows of the batch, and
- * repeated calls give bitwise identical y. */
+ * Tables and accumulation are fp32 (or fp16 tables, see table_precision).
+ * Each workgroup sums one column range of one segment; a per-row scale
+ * multiplies that range's accumulated sum, block-wise scales multiply the sum
+ * of each global chunk (one group) and of each 8 salient columns (one group,
+ * or half of one when sal_group = 16), before those sums are added.  When the
+ * plan cuts the columns into several ranges (fluxbin_plan.splits > 1), the
+ * partial sums of a row are combined exactly as fixed-point integers: each
+ * partial is rounded to a multiple of 2^-29 (an error of at most 2^-30); a
+ * partial of magnitude 2^17 or more (or a non-finite one) cannot be
+ * represented, and its row is then written as NaN, never as a wrong finite
+ * number.  Uses the handle's workspace: at most one call per handle may be in
+ * flight at a time (use one handle per concurrent stream).  For a given
+ * handle the result of row b does not depend on the other rows of the batch,
+ * and repeated calls give bitwise identical y. */
 fluxbin_status fluxbin_gemv(fluxbin_handle h, const uint16_t *x, uint16_t *y, int64_t batch, void *stream);
+
+/* Zero the handle's split-reduction words (the workspace's first region,
+ * max_batch * ceil(n/64)*64 64-bit words) with a fill kernel on `stream`.
+ * Every completed fluxbin_gemv leaves them zero; a call that did not complete
+ * (a device fault, an aborted stream) can leave them dirty, and this restores
+ * them.  Nothing is launched when the plan has no split reduction.  Allocates
+ * nothing and synchronises nothing (capturable); it must not overlap a
+ * fluxbin_gemv on the same handle. */
+fluxbin_status fluxbin_reset_workspace(fluxbin_handle h, void *stream);
 
 /* Context kernel, not part of the method: dense fp16 y = W x with fp32
  * accumulation.  w: fp16 [n][k] row-major (16-B aligned, k a multiple of 8),
  * x: fp16 [batch][k], y: fp16 [batch][n], 1 <= batch <= 16. */
 fluxbin_status fluxbin_dense_gemv_f16(const uint16_t *w, int64_t n, int64_t k, const uint16_t *x, uint16_t *y,
                                       int64_t batch, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Measurement kernels, not part of the method: the device's own rooflines for
+ * the GEMV's access and instruction patterns.  Each launches one kernel and
+ * allocates nothing.
+ * ------------------------------------------------------------------------ */
+
+/* Read `bytes` (a multiple of 16, >= 1024) at `buf` (16-B aligned) with
+ * non-temporal 16-byte loads: the buffer is cut into one contiguous span per
+ * wave of `workgroups` x 4 waves, and each wave reads its span in 1 KiB
+ * blocks (64 lanes x 16 bytes), `depth` (1, 2, 4, 8 or 16) loads in flight.
+ * sink: uint32 [workgroups * 256], written only in the practically
+ * impossible case that a lane's XOR of everything it read equals `never`. */
+fluxbin_status fluxbin_probe_stream_read(const void *buf, int64_t bytes, int32_t depth, int64_t workgroups,
+                                         uint32_t never, uint32_t *sink, void *stream);
+
+/* An empty kernel of `workgroups` x `threads` (1..1024) threads: the cost of a
+ * launch of that grid. */
+fluxbin_status fluxbin_probe_empty(int64_t workgroups, int32_t threads, void *stream);
+
+/* The GEMV's table lookups alone: every lane of `workgroups` x 256 threads
+ * holds 16 bytes of pseudo-random sign words and looks them up `iters` times
+ * in the tables of nb batch rows (g = 4: nb in 1, 2, 4, 8, 16; g = 8: 1, 2,
+ * 4), with the same address, LDS-read and fp32-add instructions as
+ * fluxbin_gemv; per call 64 * 4 * workgroups * iters * nb * 128 / g lookups.
+ * sink: float [workgroups * 256], written only if a lane's sum equals
+ * `never`. */
+fluxbin_status fluxbin_probe_lds_lookup(int32_t g, int32_t nb, int64_t workgroups, int32_t iters, float never,
+                                        float *sink, void *stream);
 
 /* ------------------------------------------------------------------------
  * Offline decomposition W ~ sum_{b<kb} diag(r_b) B_b diag(c_b), the step that

@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported(fb):
 
 
 def test_abi_version_and_strings(fb):
-    assert fb.fluxbin_abi_version() == fb.ABI_VERSION == 4
+    assert fb.fluxbin_abi_version() == fb.ABI_VERSION == 5
     assert fb.fluxbin_status_string(fb.OK) == "ok"
     assert "invalid" in fb.fluxbin_status_string(fb.ERR_INVALID_ARGUMENT)
     assert fb.fluxbin_status_string(99) == "unknown status"
@@ -56,6 +56,7 @@ def good_desc(fb, **kw):
     d.abi_version = fb.ABI_VERSION
     d.g, d.kb, d.ks = 4, 2, 1
     d.n, d.k, d.s, d.max_batch = 4096, 4096, 256, 1
+    d.layout = fb.LAYOUT_TILED
     for k, v in kw.items():
         setattr(d, k, v)
     return d
@@ -90,7 +91,7 @@ def test_too_many_splits_is_unsupported(fb):
     ("n", 0, 1), ("k", 0, 1), ("s", 0, 1), ("s", 5000, 1), ("max_batch", 0, 2), ("max_batch", 129, 2),
     ("chunks_per_block", 33, 1), ("chunks_per_block", -1, 1), ("waves_per_block", 2, 1), ("waves_per_block", 16, 1),
     ("row_group", 64, 2), ("row_group", -1, 2), ("sal_group", 8, 1), ("table_precision", 2, 1),
-    ("table_precision", -1, 1), ("compute", 2, 1), ("compute", -1, 1),
+    ("table_precision", -1, 1), ("layout", 2, 1), ("layout", -1, 1),
 ])
 def test_workspace_size_rejects(fb, field, value, status):
     st, _ = ws_status(fb, good_desc(fb, **{field: value}))
@@ -110,23 +111,43 @@ def test_g8_batch_limit_and_salient_flags(fb):
     assert ws_status(fb, good_desc(fb, chunks_per_block=8, max_batch=8))[0] == fb.ERR_UNSUPPORTED
 
 
-def test_mfma_plan_ranges_never_span_segments(fb):
-    # 4096 x 4096, kb = 2, ks = 1, s = 256: 32 global chunks per basis, 2 salient chunks
-    mf = fb.COMPUTE_MFMA
-    for cpb, splits in [(1, 66), (2, 33), (4, 17), (8, 9), (32, 3)]:
-        st, ws = ws_status(fb, good_desc(fb, compute=mf, chunks_per_block=cpb, max_batch=64))
-        assert st == fb.OK and ws == splits * 64 * 4096 * 4, fb.fluxbin_last_error()  # fp32 partials
-    # one segment in one range: no split, no workspace (kb = 1, k = 4096, 32 chunks)
-    st, ws = ws_status(fb, good_desc(fb, compute=mf, kb=1, ks=0, s=0, chunks_per_block=32))
+def plan_of(fb, d):
+    info = fb.PlanInfo()
+    assert fb.raw_status("fluxbin_plan_of", ctypes.byref(d), ctypes.byref(info)) == fb.OK, fb.fluxbin_last_error()
+    return info.as_dict()
+
+
+def test_column_ranges_never_span_segments(fb):
+    # 4096 x 4096, kb = 2, ks = 1, s = 256: 32 global chunks per basis, 2 salient chunks; every
+    # segment is cut into ceil(chunks / cpb) ranges, and the longest range is reported
+    for cpb, splits, longest in [(1, 66, 1), (2, 33, 2), (3, 2 * 11 + 1, 3), (4, 17, 4), (5, 2 * 7 + 1, 5),
+                                 (7, 2 * 5 + 1, 7), (8, 9, 8), (16, 5, 16)]:
+        p = plan_of(fb, good_desc(fb, chunks_per_block=cpb, waves_per_block=8))
+        assert (p["splits"], p["chunks_per_block"]) == (splits, longest), (cpb, p)
+    # 86 chunks (k = 11008) at a target of 7: 13 ranges of 6 or 7 chunks (balanced, never 7 x 12 + 2)
+    p = plan_of(fb, good_desc(fb, k=11008, kb=1, ks=0, s=0, chunks_per_block=7, waves_per_block=8))
+    assert (p["splits"], p["chunks_per_block"]) == (13, 7)
+    # one segment in one range: no split, no workspace
+    st, ws = ws_status(fb, good_desc(fb, k=2048, kb=1, ks=0, s=0, chunks_per_block=16, waves_per_block=8))
     assert st == fb.OK and ws == 0
-    # the matrix-core route ignores g and the table type, and runs 4 waves per workgroup
-    assert ws_status(fb, good_desc(fb, compute=mf, g=8, max_batch=128))[0] == fb.OK
-    assert ws_status(fb, good_desc(fb, compute=mf, waves_per_block=4))[0] == fb.OK
-    assert ws_status(fb, good_desc(fb, compute=mf, waves_per_block=8))[0] == fb.ERR_UNSUPPORTED
-    assert ws_status(fb, good_desc(fb, compute=mf, k=1 << 17, ks=0, s=0, chunks_per_block=1))[0] == \
-        fb.ERR_UNSUPPORTED  # 2 x 1024 ranges
-    assert ws_status(fb, good_desc(fb, compute=mf, k=1 << 25, ks=0, s=0, max_batch=64))[0] == \
-        fb.ERR_UNSUPPORTED  # batch row offsets of x beyond 32 bits
+    # the longest range: its tables and inputs within 80 KiB of LDS (31 chunks of 2.5 KiB at g = 4)
+    assert ws_status(fb, good_desc(fb, chunks_per_block=31, waves_per_block=4))[0] == fb.OK
+    assert ws_status(fb, good_desc(fb, chunks_per_block=32, waves_per_block=8))[0] == fb.ERR_UNSUPPORTED
+
+
+def test_row_major_inputs_add_their_tiled_copies_to_the_workspace(fb):
+    rnd = lambda b: -(-b // 256) * 256
+    tiled = ws_status(fb, good_desc(fb))[1]
+    st, ws = ws_status(fb, good_desc(fb, layout=fb.LAYOUT_ROWMAJOR))
+    assert st == fb.OK
+    assert ws == tiled + rnd(2 * fb.fluxbin_tiled_words(4096, 4096) * 4) + rnd(fb.fluxbin_tiled_words(4096, 256) * 4)
+    # block-wise scales are converted too: kb blocks with 1 group per chunk, ks with 16 (8 salient per group)
+    d = grouped_desc(fb, layout=fb.LAYOUT_ROWMAJOR)
+    st, ws = ws_status(fb, d)
+    assert st == fb.OK
+    expect = (rnd(4096 * 8) + rnd(2 * fb.fluxbin_tiled_words(4096, 4096) * 4) + rnd(2 * fb.fluxbin_tiled_words(4096, 256) * 4)
+              + rnd(2 * fb.fluxbin_tiled_scale_elems(4096, 32, 1) * 2) + rnd(2 * fb.fluxbin_tiled_scale_elems(4096, 32, 16) * 2))
+    assert ws == expect
 
 
 def test_create_rejects_before_touching_the_device(fb):
@@ -144,6 +165,37 @@ def test_create_rejects_before_touching_the_device(fb):
     assert fb.raw_status("fluxbin_create", ctypes.byref(d), ctypes.byref(h)) == fb.ERR_WORKSPACE
     assert fb.raw_status("fluxbin_create", None, ctypes.byref(h)) == fb.ERR_INVALID_ARGUMENT
     assert not h.value
+
+
+def test_row_major_create_needs_word_alignment_only(fb):
+    h = ctypes.c_void_p()
+    d = good_desc(fb, layout=fb.LAYOUT_ROWMAJOR)
+    d.bits_global = d.r_global = d.c_global = 0x1002
+    d.bits_sal = d.r_sal = d.c_sal = d.sal_idx = 0x2000
+    assert fb.raw_status("fluxbin_create", ctypes.byref(d), ctypes.byref(h)) == fb.ERR_INVALID_ARGUMENT
+    assert "4-byte" in fb.fluxbin_last_error()
+    d.bits_global = 0x1004  # 4-byte aligned is enough for row-major words; the workspace check comes next
+    d.workspace = None
+    assert fb.raw_status("fluxbin_create", ctypes.byref(d), ctypes.byref(h)) == fb.ERR_WORKSPACE
+    assert not h.value
+
+
+def test_reset_and_probes_reject_on_the_host(fb):
+    s = fb.raw_status
+    assert s("fluxbin_reset_workspace", None, None) == fb.ERR_INVALID_ARGUMENT
+    I64, I32 = ctypes.c_int64, ctypes.c_int32
+    P = 0x1000
+    assert s("fluxbin_probe_stream_read", None, I64(1 << 20), I32(4), I64(64), ctypes.c_uint32(0), P, None) == 1
+    assert s("fluxbin_probe_stream_read", P, I64(1000), I32(4), I64(64), ctypes.c_uint32(0), P, None) == 1
+    assert s("fluxbin_probe_stream_read", P + 8, I64(1 << 20), I32(4), I64(64), ctypes.c_uint32(0), P, None) == 1
+    assert s("fluxbin_probe_stream_read", P, I64(1 << 20), I32(3), I64(64), ctypes.c_uint32(0), P, None) == 1
+    assert s("fluxbin_probe_stream_read", P, I64(1 << 20), I32(4), I64(0), ctypes.c_uint32(0), P, None) == 1
+    assert s("fluxbin_probe_empty", I64(0), I32(64), None) == 1
+    assert s("fluxbin_probe_empty", I64(8), I32(2048), None) == 1
+    assert s("fluxbin_probe_lds_lookup", I32(4), I32(3), I64(8), I32(1), ctypes.c_float(0), P, None) == 2
+    assert s("fluxbin_probe_lds_lookup", I32(8), I32(8), I64(8), I32(1), ctypes.c_float(0), P, None) == 2
+    assert s("fluxbin_probe_lds_lookup", I32(4), I32(1), I64(8), I32(0), ctypes.c_float(0), P, None) == 1
+    assert s("fluxbin_probe_lds_lookup", I32(4), I32(1), I64(8), I32(1), ctypes.c_float(0), None, None) == 1
 
 
 def test_launching_calls_reject_bad_arguments_on_the_host(fb):
@@ -188,9 +240,10 @@ def grouped_desc(fb, **kw):
 
 
 def test_block_wise_plan_keeps_global_and_salient_ranges_apart(fb):
-    # 64 global + 4 salient chunks; with 8 chunks per workgroup: 8 global ranges + 1 salient range
+    # 2 x 32 global + 2 x 2 salient chunks; with 8 chunks per workgroup: 2 x 4 global ranges + 2 salient ranges
     st, ws = ws_status(fb, grouped_desc(fb, chunks_per_block=8))
     assert st == fb.OK and ws == 4096 * 8
+    assert plan_of(fb, grouped_desc(fb, chunks_per_block=8))["splits"] == 10
     # one global chunk (k = 128) and one salient chunk: two ranges, hence a split reduction
     st, ws = ws_status(fb, grouped_desc(fb, k=128, s=8, chunks_per_block=2, kb=1, ks=1))
     assert st == fb.OK and ws == 4096 * 8

@@ -38,7 +38,7 @@ def check_fp16_tables(orc, layer, x, y16, plan, rows=None):
     y_ex, mag = orc.gemv_dense(layer, x, rows=rows)
     M = magnitude(layer, x, rows)
     steps = layer.g + max(layer.k, layer.s) / layer.g + layer.kb + layer.ks + plan["splits"] + 3
-    fp32 = 2.0 ** -24 * steps * M + plan["splits"] * 2.0 ** -31
+    fp32 = 2.0 ** -24 * steps * M + plan["splits"] * 2.0 ** -30
     tight = 2.0 ** -11 * (np.abs(y_q) + fp32) * (1 + 2.0 ** -23) + fp32 + 2.0 ** -25
     err_q = np.abs(y - y_q)
     assert np.all(err_q <= tight), f"vs quantised reference: worst ratio {float((err_q / tight).max()):.3g}"
