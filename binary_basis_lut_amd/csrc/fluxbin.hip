@@ -6,6 +6,7 @@
 // aux_kernels.hpp.
 #include "fluxbin.h"
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -48,7 +49,6 @@ bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 constexpr int kTargetBlocks = 1024;  // about four workgroups per CU
-constexpr int64_t kWideWork = 32768;  // row tiles x chunks from which per-row layers take 8 waves
 
 struct Plan {
   int32_t waves;       // waves per workgroup (64 rows each)
@@ -119,28 +119,22 @@ fluxbin_status validate_shape(const fluxbin_layer_desc *d) {
 }
 
 // Target chunks per column range: about kTargetBlocks workgroups' worth of
-// work in all, a workgroup of nb batch rows counting nb times (measured on
-// MI355X over 4096..57344-row layers: fewer, longer ranges amortise the table
-// build, more workgroups hide latency), at least 2, a power of two up to 8 and
-// a multiple of 8 above, at most 7 for eight-wave g = 4 workgroups and 4 for
-// several batch rows (the 4096 -> 11008 projection at 4 batch rows: 15.2 us
-// with 4-chunk ranges, 18.0 with 7), within the LDS budget (cmax).  Every
-// segment is then cut into ceil(chunks / target) ranges of equal length
-// (within one chunk).
-int32_t auto_cpb(int32_t g, int32_t nb, int32_t cmax, int32_t waves, int64_t row_tiles, int32_t total_chunks) {
+// work in all, a workgroup of nb batch rows counting nb times, at least 2, a
+// power of two, at most 8, and at most 4 for several batch rows, within the
+// LDS budget (cmax).  Every segment is then cut into ceil(chunks / target)
+// ranges of equal length (within one chunk).  Measured on MI355X (graph of
+// distinct resident weight sets, 8 / 4 waves): the 70B gate+up projection
+// (8192 -> 57344, 8 waves) ran 31.2 / 29.1 / 27.2 / 28.8 / 31.5 us with 5 / 7 /
+// 8 / 10 / 16-chunk ranges; the down projection (28672 -> 8192, 4 waves)
+// 17.1 / 16.3 / 20.9 us with 4 / 8 / 16; the qkv projection 10.0 / 8.8 /
+// 10.4 us with 2 / 4 / 8; the 4096 -> 11008 projection at 4 batch rows 15.2
+// us with 4 chunks, 18.0 with 7.
+int32_t auto_cpb(int32_t nb, int32_t cmax, int32_t waves, int64_t row_tiles, int32_t total_chunks) {
   int64_t c = (int64_t)row_tiles * total_chunks * nb / ((int64_t)waves * kTargetBlocks);
-  c = std::max<int64_t>(c, 2);
-  if (nb > 1) c = std::min<int64_t>(c, 4);
-  if (g == 4 && waves == 8 && c > 7) {
-    c = 7;
-  } else if (c <= 8) {
-    int64_t p = 1;
-    while (p * 2 <= c) p *= 2;
-    c = p;
-  } else {
-    c = c / 8 * 8;
-  }
-  return (int32_t)std::max<int64_t>(1, std::min<int64_t>(c, cmax));
+  c = std::min<int64_t>(std::max<int64_t>(c, 2), nb > 1 ? 4 : 8);
+  int64_t p = 1;
+  while (p * 2 <= c) p *= 2;
+  return (int32_t)std::max<int64_t>(1, std::min<int64_t>(p, cmax));
 }
 
 // Batch rows one workgroup serves (the kernel's compiled width): the next
@@ -162,14 +156,10 @@ fluxbin_status make_plan(const fluxbin_layer_desc *d, Plan *p) {
     p->waves = d->waves_per_block;
   } else {
     // eight waves (512 rows) halve the per-row share of the table build: for
-    // the large g = 8 tables, for very tall layers, and for large layers with
-    // per-row scales (measured on MI355X: the 70B down projection, 128 row
-    // tiles x 455 chunks, ran 20.4-21.5 us with 8 waves against 21.5-22.9
-    // with 4, but 27.0 against 25.1-26.5 with block-wise scales; q_proj and
-    // the 70B qkv / o shapes, 4 200 - 21 000 tile-chunks, are as fast or
-    // faster with 4)
-    const bool wide = !d->row_group && (int64_t)p->row_tiles * p->total_chunks >= kWideWork;
-    p->waves = (d->g == 8 || p->row_tiles >= 512 || wide) ? 8 : 4;
+    // the large g = 8 tables and for very tall layers (the 70B gate+up
+    // projection, 896 row tiles: 27.2 us with 8 waves, 29.9 with 4); the 70B
+    // down, qkv and o shapes (128 - 160 row tiles) are faster with 4
+    p->waves = (d->g == 8 || p->row_tiles >= 512) ? 8 : 4;
   }
   const int32_t cmax = cpb_cap(d->g, p->nb, entry_bytes(d));
   if (d->chunks_per_block > cmax)
@@ -177,7 +167,7 @@ fluxbin_status make_plan(const fluxbin_layer_desc *d, Plan *p) {
                 d->chunks_per_block, cmax, d->g, (long long)d->max_batch, p->waves);
   p->row_blocks = (int32_t)cdiv(p->row_tiles, p->waves);
   int32_t target =
-      d->chunks_per_block ? d->chunks_per_block : auto_cpb(d->g, p->nb, cmax, p->waves, p->row_tiles, p->total_chunks);
+      d->chunks_per_block ? d->chunks_per_block : auto_cpb(p->nb, cmax, p->waves, p->row_tiles, p->total_chunks);
   const int32_t nc_g = (int32_t)cdiv(d->k, kChunkCols), nc_s = d->ks > 0 ? (int32_t)cdiv(d->s, kChunkCols) : 0;
   for (;;) {
     p->rpg = (int32_t)cdiv(nc_g, target);
@@ -782,7 +772,12 @@ fluxbin_status fluxbin_build_lut(fluxbin_handle h, const uint16_t *x, int64_t ba
   return ok();
 }
 
-fluxbin_status fluxbin_gemv(fluxbin_handle h, const uint16_t *x, uint16_t *y, int64_t batch, void *stream) {
+namespace {
+
+// The GEMV's launches; with events, start_event is recorded when the first
+// launch begins and stop_event when the last one ends (hipExtLaunchKernel).
+fluxbin_status gemv_launch(fluxbin_handle h, const uint16_t *x, uint16_t *y, int64_t batch, void *stream,
+                           hipEvent_t start_event, hipEvent_t stop_event) {
   if (!h) return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "handle is NULL");
   if (batch < 0 || batch > h->d.max_batch)
     return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "batch = %lld outside [0, %lld]", (long long)batch,
@@ -816,11 +811,32 @@ fluxbin_status fluxbin_gemv(fluxbin_handle h, const uint16_t *x, uint16_t *y, in
     a.x = x + b0 * d.k;
     a.y = y + b0 * d.n;
     a.acc = acc ? acc + b0 * p.n_pad : nullptr;
-    hipLaunchKernelGGL(h->fn, dim3((unsigned)grid), dim3(p.waves * 64), h->lds, (hipStream_t)stream, a);
+    if (start_event || stop_event) {
+      void *args[] = {&a};
+      hipError_t e = hipExtLaunchKernel(reinterpret_cast<const void *>(h->fn), dim3((unsigned)grid),
+                                        dim3(p.waves * 64), args, h->lds, (hipStream_t)stream,
+                                        b0 == 0 ? start_event : nullptr, b0 + p.nb >= batch ? stop_event : nullptr, 0);
+      if (e != hipSuccess) return hip_fail(e, "gemv launch");
+    } else {
+      hipLaunchKernelGGL(h->fn, dim3((unsigned)grid), dim3(p.waves * 64), h->lds, (hipStream_t)stream, a);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "gemv launch");
   }
   return ok();
+}
+
+}  // namespace
+
+fluxbin_status fluxbin_gemv(fluxbin_handle h, const uint16_t *x, uint16_t *y, int64_t batch, void *stream) {
+  return gemv_launch(h, x, y, batch, stream, nullptr, nullptr);
+}
+
+fluxbin_status fluxbin_gemv_timed(fluxbin_handle h, const uint16_t *x, uint16_t *y, int64_t batch, void *stream,
+                                  void *start_event, void *stop_event) {
+  if (!start_event || !stop_event) return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "events must be non-NULL");
+  return gemv_launch(h, x, y, batch, stream, static_cast<hipEvent_t>(start_event),
+                     static_cast<hipEvent_t>(stop_event));
 }
 
 fluxbin_status fluxbin_reset_workspace(fluxbin_handle h, void *stream) {

@@ -276,6 +276,14 @@ fluxbin_status fluxbin_build_lut(fluxbin_handle h, const uint16_t *x, int64_t ba
  * and repeated calls give bitwise identical y. */
 fluxbin_status fluxbin_gemv(fluxbin_handle h, const uint16_t *x, uint16_t *y, int64_t batch, void *stream);
 
+/* fluxbin_gemv, and the device time of its kernels: start_event (a
+ * hipEvent_t) is recorded when its first kernel starts and stop_event when
+ * its last kernel ends (hipExtLaunchKernel), so hipEventElapsedTime gives the
+ * kernels' own duration without the launch gaps around them.  For
+ * measurement; not capturable in a HIP graph (events). */
+fluxbin_status fluxbin_gemv_timed(fluxbin_handle h, const uint16_t *x, uint16_t *y, int64_t batch, void *stream,
+                                  void *start_event, void *stop_event);
+
 /* Zero the handle's split-reduction words (the workspace's first region,
  * max_batch * ceil(n/64)*64 64-bit words) with a fill kernel on `stream`.
  * Every completed fluxbin_gemv leaves them zero; a call that did not complete

@@ -183,6 +183,8 @@ def test_row_major_create_needs_word_alignment_only(fb):
 def test_reset_and_probes_reject_on_the_host(fb):
     s = fb.raw_status
     assert s("fluxbin_reset_workspace", None, None) == fb.ERR_INVALID_ARGUMENT
+    assert s("fluxbin_gemv_timed", None, 0x1000, 0x2000, 1, None, 0x10, 0x20) == fb.ERR_INVALID_ARGUMENT
+    assert s("fluxbin_gemv_timed", 0x1000, 0x1000, 0x2000, 1, None, None, 0x20) == fb.ERR_INVALID_ARGUMENT
     I64, I32 = ctypes.c_int64, ctypes.c_int32
     P = 0x1000
     assert s("fluxbin_probe_stream_read", None, I64(1 << 20), I32(4), I64(64), ctypes.c_uint32(0), P, None) == 1

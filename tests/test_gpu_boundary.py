@@ -154,6 +154,24 @@ def test_row_major_inputs_match_tiled_inputs_bitwise(fb, kind):
     assert np.array_equal(ys[0], ys[1])
 
 
+def test_timed_gemv_matches_the_plain_call(fb):
+    note("timed gemv: workload 2 and a 2-group batch")
+    for layer, batch, mb in ((I.workload_layer(2), 1, 1), (I.make_layer(300, 700, 2, 1, 4, s=40, seed=(76, 0, 0)), 20, 20)):
+        x = dev(I.make_x(layer, batch, seed=(76, 1, 0)), np.int16)
+        dl = fb.DeviceLayer(layer, max_batch=mb)
+        y0 = torch.empty((batch, layer.n), dtype=torch.int16, device="cuda")
+        dl.gemv(x, y0)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        e1.record()  # creates the events
+        y = torch.zeros_like(y0)
+        fb.fluxbin_gemv_timed(dl.handle, x, y, batch, e0, e1)
+        torch.cuda.synchronize()
+        assert torch.equal(y, y0)
+        assert e0.elapsed_time(e1) > 0
+        dl.close()
+
+
 def test_measurement_kernels_run(fb):
     note("probes: stream read, empty kernel, table lookups")
     buf = torch.zeros(64 << 20, dtype=torch.uint8, device="cuda")

@@ -54,20 +54,20 @@ def test_q_proj_decode_plan(fb):
     assert p["total_chunks"] == 66 and p["grid"] == 528
 
 
-def test_tall_layer_takes_eight_waves_and_seven_chunk_ranges(fb):
-    # 70B gate+up 8192 -> 57344: 896 row tiles, 8 waves; g = 4 eight-wave ranges stop at 7 chunks:
-    # each 64-chunk global segment in 10 ranges of 6-7 chunks, the 2 salient chunks in one
+def test_tall_layer_takes_eight_waves_and_eight_chunk_ranges(fb):
+    # 70B gate+up 8192 -> 57344: 896 row tiles, 8 waves; ranges stop at 8 chunks: each 64-chunk
+    # global segment in 8 ranges, the 2 salient chunks in one
     p = plan(fb, workload_desc(fb, 5, 2))
-    assert (p["rows_per_block"], p["chunks_per_block"], p["splits"]) == (512, 7, 21)
+    assert (p["rows_per_block"], p["chunks_per_block"], p["splits"]) == (512, 8, 17)
     p = plan(fb, blockwise_desc(fb, 57344, 8192))
-    assert p["rows_per_block"] == 512 and p["chunks_per_block"] == 7
+    assert p["rows_per_block"] == 512 and p["chunks_per_block"] == 8
 
 
-def test_large_per_row_layer_takes_eight_waves(fb):
-    # 70B down 28672 -> 8192: 128 row tiles x 455 chunks of per-row work: 8 waves
+def test_wide_layers_keep_four_waves(fb):
+    # 70B down 28672 -> 8192: 128 row tiles x 455 chunks: 4 waves, 8-chunk ranges (224 global
+    # chunks per basis in 28 ranges, the 7 salient chunks in one)
     p = plan(fb, workload_desc(fb, 5, 3))
-    assert (p["rows_per_block"], p["chunks_per_block"], p["splits"]) == (512, 4, 114)
-    # the same shape with block-wise scales keeps 4 waves
+    assert (p["rows_per_block"], p["chunks_per_block"], p["splits"]) == (256, 8, 57)
     assert plan(fb, blockwise_desc(fb, 8192, 28672))["rows_per_block"] == 256
     # qkv and o (160 / 128 row tiles x 130 chunks) stay at 4 waves
     for shape in (0, 1):
