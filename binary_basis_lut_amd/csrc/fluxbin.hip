@@ -14,6 +14,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -230,6 +231,40 @@ struct fluxbin_layer {
 // A valid index array for layers without salient bases: the GEMV reads its
 // entry 0 (and ignores it) where a salient chunk would read its gather index.
 __device__ int32_t g_zero_index[4];
+
+// Split-reduction words of fluxbin_gemv_static: a file-scope device array (8
+// MiB), one copy per GPU the library runs on, held until the process ends.
+// Host code never passes `scratch` itself to a kernel (on the host the name
+// is a stand-in, not a device address): the address each device gives for it
+// (hipGetSymbolAddress, taken once per device with that device current) is
+// kept in g_scratch_ptr and used instead.
+constexpr int64_t kScratchWords = 1 << 20;
+static __device__ __align__(256) uint64_t scratch[kScratchWords];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+uint64_t *g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's address of `scratch` (looked up on its first use on that device).
+fluxbin_status scratch_words(uint64_t **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(FLUXBIN_ERR_UNSUPPORTED, "device %d (at most %d)", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "locating the static scratch array");
+    g_scratch_ptr[dev] = static_cast<uint64_t *>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return FLUXBIN_OK;
+}
+
+}  // namespace
 
 // ---------------------------------------------------------------------------
 // launch table for the GEMV kernel
@@ -601,7 +636,10 @@ fluxbin_status fluxbin_create(const fluxbin_layer_desc *d, fluxbin_handle *out) 
   st = make_plan(d, &p);
   if (st) return st;
   const WsLayout wl = ws_layout(d, p);
-  if (wl.total > 0) {
+  // a tiled layer may be created without a workspace (NULL, 0 bytes): its split
+  // reduction then runs only through fluxbin_gemv_static
+  const bool no_ws = tiled && !d->workspace && d->workspace_bytes == 0;
+  if (wl.total > 0 && !no_ws) {
     if (!d->workspace || d->workspace_bytes < wl.total)
       return fail(FLUXBIN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", wl.total,
                   d->workspace ? d->workspace_bytes : (size_t)0);
@@ -663,8 +701,8 @@ fluxbin_status fluxbin_create(const fluxbin_layer_desc *d, fluxbin_handle *out) 
     if (st) return st;
     hd.layout = FLUXBIN_LAYOUT_TILED;
   }
-  if (p.acc_bytes || !tiled) {
-    if (p.acc_bytes) {
+  if ((p.acc_bytes && !no_ws) || !tiled) {
+    if (p.acc_bytes && !no_ws) {
       hipError_t e = hipMemset(ws + wl.acc, 0, p.acc_bytes);
       if (e != hipSuccess) return hip_fail(e, "zeroing the split-reduction words");
     }
@@ -777,7 +815,7 @@ namespace {
 // The GEMV's launches; with events, start_event is recorded when the first
 // launch begins and stop_event when the last one ends (hipExtLaunchKernel).
 fluxbin_status gemv_launch(fluxbin_handle h, const uint16_t *x, uint16_t *y, int64_t batch, void *stream,
-                           hipEvent_t start_event, hipEvent_t stop_event) {
+                           hipEvent_t start_event, hipEvent_t stop_event, uint64_t *words) {
   if (!h) return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "handle is NULL");
   if (batch < 0 || batch > h->d.max_batch)
     return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "batch = %lld outside [0, %lld]", (long long)batch,
@@ -802,7 +840,7 @@ fluxbin_status gemv_launch(fluxbin_handle h, const uint16_t *x, uint16_t *y, int
   a.row_blocks = p.row_blocks;
   a.splits = p.splits;
   a.sal16 = d.row_group && d.ks > 0 && d.sal_group == 8 ? 1 : 0;
-  uint64_t *acc = p.splits > 1 ? reinterpret_cast<uint64_t *>(d.workspace) : nullptr;
+  uint64_t *acc = p.splits > 1 ? words : nullptr;
   const int64_t grid = (int64_t)p.row_blocks * p.splits;
   // one launch per group of p.nb batch rows (a prefill batch runs as several groups,
   // each building its own tables and streaming the weights again)
@@ -826,24 +864,69 @@ fluxbin_status gemv_launch(fluxbin_handle h, const uint16_t *x, uint16_t *y, int
   return ok();
 }
 
+// The handle's own reduction words (its workspace), or an error when the plan
+// needs them and the handle was created without a workspace.
+fluxbin_status handle_words(fluxbin_handle h, uint64_t **words) {
+  *words = reinterpret_cast<uint64_t *>(h->d.workspace);
+  if (h->plan.splits > 1 && !*words)
+    return fail(FLUXBIN_ERR_WORKSPACE,
+                "the handle has no workspace (created without one): use fluxbin_gemv_static, or create it with "
+                "fluxbin_workspace_size() bytes");
+  return FLUXBIN_OK;
+}
+
 }  // namespace
 
 fluxbin_status fluxbin_gemv(fluxbin_handle h, const uint16_t *x, uint16_t *y, int64_t batch, void *stream) {
-  return gemv_launch(h, x, y, batch, stream, nullptr, nullptr);
+  if (!h) return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "handle is NULL");
+  uint64_t *words;
+  fluxbin_status st = handle_words(h, &words);
+  if (st) return st;
+  return gemv_launch(h, x, y, batch, stream, nullptr, nullptr, words);
 }
 
 fluxbin_status fluxbin_gemv_timed(fluxbin_handle h, const uint16_t *x, uint16_t *y, int64_t batch, void *stream,
                                   void *start_event, void *stop_event) {
   if (!start_event || !stop_event) return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "events must be non-NULL");
+  if (!h) return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "handle is NULL");
+  uint64_t *words;
+  fluxbin_status st = handle_words(h, &words);
+  if (st) return st;
   return gemv_launch(h, x, y, batch, stream, static_cast<hipEvent_t>(start_event),
-                     static_cast<hipEvent_t>(stop_event));
+                     static_cast<hipEvent_t>(stop_event), words);
+}
+
+fluxbin_status fluxbin_gemv_static(fluxbin_handle h, const uint16_t *x, uint16_t *y, int64_t batch, void *stream) {
+  if (!h) return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "handle is NULL");
+  if (batch < 0 || batch > h->d.max_batch)
+    return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "batch = %lld outside [0, %lld]", (long long)batch,
+                (long long)h->d.max_batch);
+  const int64_t words = h->plan.splits > 1 ? batch * h->plan.n_pad : 0;
+  if (words > kScratchWords)
+    return fail(FLUXBIN_ERR_UNSUPPORTED,
+                "batch %lld x %lld padded rows = %lld split-reduction words exceed the %lld of the static scratch "
+                "array (use fluxbin_gemv with a workspace)",
+                (long long)batch, (long long)h->plan.n_pad, (long long)words, (long long)kScratchWords);
+  if (batch == 0) return ok();
+  if (!x || !y) return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "NULL pointer");
+  if (h->fault_launch) return fail(FLUXBIN_ERR_HIP, "injected launch fault (FLUXBIN_FAULT=launch)");
+  uint64_t *sw = nullptr;
+  fluxbin_status st = scratch_words(&sw);
+  if (st) return st;
+  if (words) {
+    // the array keeps the last call's contents: the words this call uses start at zero
+    hipLaunchKernelGGL(zero_words_kernel, dim3(grid_for(words)), dim3(256), 0, (hipStream_t)stream, sw, words);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "scratch clear launch");
+  }
+  return gemv_launch(h, x, y, batch, stream, nullptr, nullptr, sw);
 }
 
 fluxbin_status fluxbin_reset_workspace(fluxbin_handle h, void *stream) {
   if (!h) return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "handle is NULL");
   if (h->fault_launch) return fail(FLUXBIN_ERR_HIP, "injected launch fault (FLUXBIN_FAULT=launch)");
   const Plan &p = h->plan;
-  if (!p.acc_bytes) return ok();
+  if (!p.acc_bytes || !h->d.workspace) return ok();
   const int64_t words = (int64_t)(p.acc_bytes / sizeof(uint64_t));
   hipLaunchKernelGGL(zero_words_kernel, dim3(grid_for(words)), dim3(256), 0, (hipStream_t)stream,
                      reinterpret_cast<uint64_t *>(h->d.workspace), words);

@@ -86,6 +86,7 @@ _decl("fluxbin_lut_size", ctypes.c_int, [P, I64, ctypes.POINTER(ctypes.c_size_t)
 _decl("fluxbin_build_lut", ctypes.c_int, [P, P, I64, P, P])
 _decl("fluxbin_gemv", ctypes.c_int, [P, P, P, I64, P])
 _decl("fluxbin_gemv_timed", ctypes.c_int, [P, P, P, I64, P, P, P])
+_decl("fluxbin_gemv_static", ctypes.c_int, [P, P, P, I64, P])
 _decl("fluxbin_reset_workspace", ctypes.c_int, [P, P])
 _decl("fluxbin_dense_gemv_f16", ctypes.c_int, [P, I64, I64, P, P, I64, P])
 _decl("fluxbin_probe_stream_read", ctypes.c_int, [P, I64, I32, I64, ctypes.c_uint32, P, P])
@@ -104,7 +105,7 @@ SYMBOLS = [
     "fluxbin_relayout", "fluxbin_tiled_scale_elems", "fluxbin_relayout_scales", "fluxbin_vcm_gather",
     "fluxbin_workspace_size", "fluxbin_create", "fluxbin_destroy", "fluxbin_get_plan", "fluxbin_plan_of",
     "fluxbin_lut_size",
-    "fluxbin_build_lut", "fluxbin_gemv", "fluxbin_gemv_timed", "fluxbin_reset_workspace", "fluxbin_dense_gemv_f16",
+    "fluxbin_build_lut", "fluxbin_gemv", "fluxbin_gemv_timed", "fluxbin_gemv_static", "fluxbin_reset_workspace", "fluxbin_dense_gemv_f16",
     "fluxbin_probe_stream_read", "fluxbin_probe_empty", "fluxbin_probe_lds_lookup", "fluxbin_decomp_workspace_size",
     "fluxbin_decompose", "fluxbin_decomp_row_scales", "fluxbin_decomp_col_scales", "fluxbin_decomp_signs",
     "fluxbin_decomp_residual_signs", "fluxbin_decomp_error",
@@ -215,6 +216,10 @@ def fluxbin_build_lut(handle, x, batch, lut, stream=None):
 
 def fluxbin_gemv(handle, x, y, batch, stream=None):
     _check(_lib.fluxbin_gemv(handle, _ptr(x), _ptr(y), batch, _stream(stream)), "fluxbin_gemv")
+
+
+def fluxbin_gemv_static(handle, x, y, batch, stream=None):
+    _check(_lib.fluxbin_gemv_static(handle, _ptr(x), _ptr(y), batch, _stream(stream)), "fluxbin_gemv_static")
 
 
 def fluxbin_gemv_timed(handle, x, y, batch, start_event, stop_event, stream=None):

@@ -124,7 +124,10 @@ typedef struct {
   const uint16_t *c_sal;       /* fp16 [ks][s], compact order (entry c belongs to column sal_idx[c]) */
   const int32_t *sal_idx;      /* [s] salient columns, strictly ascending, in [0, k) */
   void *workspace;             /* >= fluxbin_workspace_size() bytes, 256-B aligned, caller-owned; may be NULL
-                                  if that size is 0 */
+                                  if that size is 0.  A TILED layer may also be created with NULL and
+                                  workspace_bytes 0 whatever its size: its split reduction then runs only
+                                  through fluxbin_gemv_static (fluxbin_gemv fails with
+                                  FLUXBIN_ERR_WORKSPACE when the plan splits the columns) */
   size_t workspace_bytes;
   int32_t chunks_per_block;    /* tuning: 0 = automatic, else 1..32: the longest column range of one
                                   workgroup, in 128-column chunks (each segment is cut into equal ranges no
@@ -275,6 +278,21 @@ fluxbin_status fluxbin_build_lut(fluxbin_handle h, const uint16_t *x, int64_t ba
  * handle the result of row b does not depend on the other rows of the batch,
  * and repeated calls give bitwise identical y. */
 fluxbin_status fluxbin_gemv(fluxbin_handle h, const uint16_t *x, uint16_t *y, int64_t batch, void *stream);
+
+/* fluxbin_gemv for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation), and
+ * for handles created without a workspace: the split-reduction words live in
+ * a static device array of the library (8 MiB: 2^20 64-bit words, one copy per
+ * GPU, held until the process ends) instead of the handle's workspace.  The
+ * words this call uses (batch * ceil(n/64)*64 when the plan splits the
+ * columns) are cleared by a fill kernel on `stream` first, then the GEMV runs
+ * as in fluxbin_gemv, with the same arithmetic (bitwise the same y).  Errors:
+ * FLUXBIN_ERR_UNSUPPORTED when those words exceed 2^20.  Allocates nothing
+ * (no hipMalloc or allocating library call); the array's device address is
+ * looked up once per device, on the first call there.  Every call on one GPU
+ * shares that GPU's array: calls that overlap on one GPU (concurrent streams,
+ * threads) race and must be serialised by the caller. */
+fluxbin_status fluxbin_gemv_static(fluxbin_handle h, const uint16_t *x, uint16_t *y, int64_t batch, void *stream);
 
 /* fluxbin_gemv, and the device time of its kernels: start_event (a
  * hipEvent_t) is recorded when its first kernel starts and stop_event when

@@ -162,6 +162,7 @@ def test_create_rejects_before_touching_the_device(fb):
     assert "aligned" in fb.fluxbin_last_error()
     d.bits_global = 0x1000
     d.workspace = None
+    d.workspace_bytes = 1  # a NULL workspace is accepted only as "none" (0 bytes)
     assert fb.raw_status("fluxbin_create", ctypes.byref(d), ctypes.byref(h)) == fb.ERR_WORKSPACE
     assert fb.raw_status("fluxbin_create", None, ctypes.byref(h)) == fb.ERR_INVALID_ARGUMENT
     assert not h.value
@@ -183,6 +184,7 @@ def test_row_major_create_needs_word_alignment_only(fb):
 def test_reset_and_probes_reject_on_the_host(fb):
     s = fb.raw_status
     assert s("fluxbin_reset_workspace", None, None) == fb.ERR_INVALID_ARGUMENT
+    assert s("fluxbin_gemv_static", None, 0x1000, 0x2000, 1, None) == fb.ERR_INVALID_ARGUMENT
     assert s("fluxbin_gemv_timed", None, 0x1000, 0x2000, 1, None, 0x10, 0x20) == fb.ERR_INVALID_ARGUMENT
     assert s("fluxbin_gemv_timed", 0x1000, 0x1000, 0x2000, 1, None, None, 0x20) == fb.ERR_INVALID_ARGUMENT
     I64, I32 = ctypes.c_int64, ctypes.c_int32
