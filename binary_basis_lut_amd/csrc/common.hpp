@@ -222,6 +222,9 @@ gemv_fn gemv_pick_g4_rs0_t16(int nb, int waves, int pf);
 gemv_fn gemv_pick_g4_rs1_t16(int nb, int waves, int pf);
 gemv_fn gemv_pick_g8_rs0_t16(int nb, int waves, int pf);
 gemv_fn gemv_pick_g8_rs1_t16(int nb, int waves, int pf);
+// The g = 8 kernel with bank-private tables (one batch row, per-row scales,
+// fp32 entries) for column ranges of up to `region` (2 or 4) chunks.
+gemv_fn gemv_pick_g8_banked(int region, int waves);
 
 __device__ __forceinline__ float h2f(uint16_t h) { return __half2float(__ushort_as_half(h)); }
 __device__ __forceinline__ uint16_t f2h(float f) { return __half_as_ushort(__float2half_rn(f)); }
@@ -409,6 +412,10 @@ __host__ __device__ constexpr int lds_bytes(int g, int nb, int cpb, int eb) {
   return cpb * lds_per_chunk(g, nb, eb) + kLdsSink;
 }
 
+// LDS of the g = 8 bank-private-table kernel over a region of r chunks: the
+// tables (16 r x 256 fp32), then the r * 128 fp32 scale-fused inputs.
+__host__ __device__ constexpr int banked_lds_bytes(int r) { return r * (16 * 256 * 4 + kChunkCols * 4); }
+
 __host__ __device__ constexpr int cmin(int a, int b) { return a < b ? a : b; }
 
 // Table-build inputs (c * x) each thread stages per round: 4 for one batch
@@ -425,6 +432,105 @@ __host__ __device__ constexpr int cpb_cap(int g, int nb, int eb) {
 
 // Chunks of weights in flight per wave for ranges of up to cpb chunks.
 __host__ __device__ constexpr int prefetch_depth(int cpb) { return cpb >= 4 ? 4 : 2; }
+
+// The column range of split sp: segment sg, chunks [c_lo, c_lo + nch) of it
+// (the balanced cut described at GemvArgs::rpg).
+struct ColRange {
+  SegRef S;
+  int sg, c_lo, nch;
+};
+
+__device__ __forceinline__ ColRange column_range(const GemvArgs &a, int sp) {
+  const int gsp = a.kb * a.rpg;
+  const bool gpart = sp < gsp;
+  const int rel = gpart ? sp : sp - gsp;
+  const int nr = gpart ? a.rpg : a.rps;
+  const int sq = rel / nr;
+  const int rr = rel - sq * nr;
+  ColRange c;
+  c.sg = (gpart ? 0 : a.kb) + sq;
+  c.S = gemv_segment(a.seg, a.kb, c.sg);
+  c.c_lo = (int)(((uint32_t)rr * (uint32_t)c.S.nchunks) / (uint32_t)nr);
+  c.nch = (int)(((uint32_t)(rr + 1) * (uint32_t)c.S.nchunks) / (uint32_t)nr) - c.c_lo;
+  return c;
+}
+
+// One g = 8 table build unit: the 16 entries p = (hb << 7) | (m << 3) | q3,
+// m = 0..15, of the sub-vector whose scale-fused inputs are v[0..7], for the
+// unit un = (hb << 3) | q3.  Entry p is the sum, in this order, of
+// sgn_7 v_7, sgn_0 v_0, sgn_1 v_1, ..., sgn_6 v_6 (sgn_t = +1 where bit t of
+// p is set, -1 where it is clear); the tree below shares the leading terms,
+// so every entry rounds exactly like that sequence, and the units with hb = 0
+// are the exact negations of those with hb = 1 (LUT[~p] = -LUT[p]).
+__device__ __forceinline__ void g8_unit_entries(const float *v, int un, float (&e)[16]) {
+  const float4 va = *reinterpret_cast<const float4 *>(v);
+  const float4 vb = *reinterpret_cast<const float4 *>(v + 4);
+  const int hb = un >> 3, q3 = un & 7;
+  float base = hb ? vb.w : -vb.w;
+  base = (q3 & 1) ? base + va.x : base - va.x;
+  base = (q3 & 2) ? base + va.y : base - va.y;
+  base = (q3 & 4) ? base + va.z : base - va.z;
+  const float l1[2] = {base - va.w, base + va.w};
+  float l2[4], l3[8];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) l2[i] = l1[i] - vb.x, l2[i + 2] = l1[i] + vb.x;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) l3[i] = l2[i] - vb.y, l3[i + 4] = l2[i] + vb.y;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) e[i] = l3[i] - vb.z, e[i + 8] = l3[i] + vb.z;
+}
+
+// The output of one lane's row: part[b] is the row's partial sum over the
+// workgroup's column range for batch row b, already row-scaled.
+//
+// One range per row (splits == 1): a direct fp16 store.  Several ranges:
+// every workgroup adds its partial of each row into that row's packed word
+// with one agent-scope atomic (performed at the memory side, coherent across
+// XCDs).  The atomic returns the previous word, so the lane that brings the
+// last of `splits` contributions knows it is last and holds the complete sum:
+// it writes y and clears the word for the next call.  No workgroup waits for
+// another, and since integer addition is exact the result does not depend on
+// the order in which the splits arrive.  A partial outside the fixed-point
+// range first sets the word's overflow flag (a rare second atomic on the same
+// word, ordered before the add), and the row is written as NaN.
+//
+// With several batch rows, all NB atomics are issued before any result is
+// examined, so that their round trips overlap instead of queueing one behind
+// the other.
+template <int NB>
+__device__ __forceinline__ void finish_rows(const GemvArgs &a, int row, bool row_ok, const float (&part)[NB]) {
+  if (a.splits == 1) {
+    if (row_ok) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+        if (b < a.batch) a.y[(int64_t)b * a.n + row] = f2h(part[b]);
+    }
+    return;
+  }
+  if (!row_ok) return;
+  uint64_t contrib[NB], old[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const float scaled = part[b] * kFixScale;
+    const bool ovf = !(fabsf(scaled) < kFixLimit);      // NaN and inf overflow too
+    const int64_t q = ovf ? 0 : __float2ll_rn(scaled);  // an overflowing partial adds 0 (the row is NaN)
+    contrib[b] = (uint64_t)(q + kFixBias);
+    old[b] = 0;
+    if (b < a.batch) {
+      uint64_t *slot = a.acc + (int64_t)b * a.n_pad + row;
+      if (ovf) __hip_atomic_fetch_or(slot, kOverflow, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      old[b] = __hip_atomic_fetch_add(slot, contrib[b] + kOneArrival, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    if (b < a.batch && (int)((old[b] >> kCountShift) & 0xffu) == a.splits - 1) {
+      const int64_t total = (int64_t)((old[b] & kValueMask) + contrib[b]) - (int64_t)a.splits * kFixBias;
+      a.y[(int64_t)b * a.n + row] = (old[b] & kOverflow) ? kHalfNaN : f2h(__ll2float_rn(total) * kFixInv);
+      __hip_atomic_store(a.acc + (int64_t)b * a.n_pad + row, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
 
 template <bool B>
 struct BoolTag {

@@ -61,6 +61,8 @@ struct Plan {
   int32_t total_chunks;
   int32_t rpg, rps;    // column ranges per global / salient segment
   int32_t splits;      // kb * rpg + ks * rps
+  int32_t banked;      // g = 8 bank-private tables over ranges of this many chunks (2 or 4), else 0
+  int32_t lds;         // dynamic LDS bytes of one workgroup
   int64_t n_pad;
   size_t acc_bytes;    // workspace (splits > 1): packed reduction words
 };
@@ -96,6 +98,7 @@ fluxbin_status validate_shape(const fluxbin_layer_desc *d) {
                 kMaxCpb);
   if (d->waves_per_block != 0 && d->waves_per_block != 4 && d->waves_per_block != 8)
     return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "waves_per_block = %d (0, 4 or 8)", d->waves_per_block);
+
   if (d->layout != FLUXBIN_LAYOUT_ROWMAJOR && d->layout != FLUXBIN_LAYOUT_TILED)
     return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "layout = %d (0 = row-major, 1 = tiled)", d->layout);
   if (d->table_precision != FLUXBIN_TABLE_F32 && d->table_precision != FLUXBIN_TABLE_F16)
@@ -138,6 +141,17 @@ int32_t auto_cpb(int32_t nb, int32_t cmax, int32_t waves, int64_t row_tiles, int
   return (int32_t)std::max<int64_t>(1, std::min<int64_t>(p, cmax));
 }
 
+// Ranges of the banked g = 8 kernel: 2 chunks (33 KiB of LDS, four
+// workgroups per CU), or 4 (two per CU) where 2-chunk ranges would cut the
+// layer into more than 64 column ranges.  Measured on MI355X (graph of 32
+// distinct resident weight sets of the LLaMA-2-7B g = 8 layer, 8 waves), 2 /
+// 4-chunk ranges: qkv 9.4 / 10.6 us, o 6.0 / 6.2, gate+up 13.7 / 15.2, down
+// (130 / 67 ranges) 11.8 / 11.1.
+int32_t banked_cpb(const fluxbin_layer_desc *d) {
+  const int64_t ranges2 = d->kb * cdiv(cdiv(d->k, kChunkCols), 2) + d->ks * cdiv(cdiv(d->s, kChunkCols), 2);
+  return ranges2 > 64 ? 4 : 2;
+}
+
 // Batch rows one workgroup serves (the kernel's compiled width): the next
 // power of two of max_batch, at most 16 (g = 4) or 4 (g = 8); wider batches
 // run as several groups.
@@ -166,9 +180,11 @@ fluxbin_status make_plan(const fluxbin_layer_desc *d, Plan *p) {
   if (d->chunks_per_block > cmax)
     return fail(FLUXBIN_ERR_UNSUPPORTED, "chunks_per_block = %d exceeds %d for g = %d, max_batch = %lld, %d waves",
                 d->chunks_per_block, cmax, d->g, (long long)d->max_batch, p->waves);
-  p->row_blocks = (int32_t)cdiv(p->row_tiles, p->waves);
-  int32_t target =
-      d->chunks_per_block ? d->chunks_per_block : auto_cpb(p->nb, cmax, p->waves, p->row_tiles, p->total_chunks);
+  // g = 8, one batch row, per-row scales, fp32 entries: bank-private tables
+  const bool bank_ok = d->g == 8 && p->nb == 1 && !d->row_group && entry_bytes(d) == 4;
+  int32_t target = d->chunks_per_block ? d->chunks_per_block
+                   : bank_ok           ? banked_cpb(d)
+                                       : auto_cpb(p->nb, cmax, p->waves, p->row_tiles, p->total_chunks);
   const int32_t nc_g = (int32_t)cdiv(d->k, kChunkCols), nc_s = d->ks > 0 ? (int32_t)cdiv(d->s, kChunkCols) : 0;
   for (;;) {
     p->rpg = (int32_t)cdiv(nc_g, target);
@@ -183,6 +199,11 @@ fluxbin_status make_plan(const fluxbin_layer_desc *d, Plan *p) {
   // the longest range (balanced cut: ceil(chunks / ranges))
   p->cpb = (int32_t)std::max<int64_t>(cdiv(nc_g, p->rpg), d->ks > 0 ? cdiv(nc_s, p->rps) : 0);
   p->pf = prefetch_depth(p->cpb);
+  // banked tables: one region of 2 or 4 chunks holds every range (cpb_cap
+  // keeps g = 8 fp32 ranges at <= 4 chunks)
+  p->banked = bank_ok ? (p->cpb <= 2 ? 2 : 4) : 0;
+  p->row_blocks = (int32_t)cdiv(p->row_tiles, p->waves);
+  p->lds = p->banked ? banked_lds_bytes(p->banked) : lds_bytes(d->g, p->nb, p->cpb, entry_bytes(d));
   p->acc_bytes = p->splits > 1 ? (size_t)d->max_batch * p->n_pad * sizeof(uint64_t) : 0;
   return FLUXBIN_OK;
 }
@@ -709,9 +730,10 @@ fluxbin_status fluxbin_create(const fluxbin_layer_desc *d, fluxbin_handle *out) 
     hipError_t e = hipDeviceSynchronize();
     if (e != hipSuccess) return hip_fail(e, "synchronising after create");
   }
-  gemv_fn fn = pick_gemv(d->g, d->row_group ? 1 : 0, d->table_precision, p.nb, p.waves, p.pf);
+  gemv_fn fn = p.banked ? gemv_pick_g8_banked(p.banked, p.waves)
+                        : pick_gemv(d->g, d->row_group ? 1 : 0, d->table_precision, p.nb, p.waves, p.pf);
   if (!fn) return fail(FLUXBIN_ERR_UNSUPPORTED, "no kernel for g = %d, batch width %d, %d waves", d->g, p.nb, p.waves);
-  const size_t lds = (size_t)lds_bytes(d->g, p.nb, p.cpb, entry_bytes(d));
+  const size_t lds = (size_t)p.lds;
   hipError_t e =
       hipFuncSetAttribute(reinterpret_cast<const void *>(fn), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return hip_fail(e, "setting the kernel's dynamic LDS size");
@@ -749,8 +771,9 @@ void fill_plan(const fluxbin_layer_desc &d, const Plan &p, fluxbin_plan *plan) {
   plan->row_blocks = p.row_blocks;
   plan->splits = p.splits;
   plan->total_chunks = p.total_chunks;
-  plan->lds_bytes = lds_bytes(d.g, p.nb, p.cpb, entry_bytes(&d));
+  plan->lds_bytes = p.lds;
   plan->grid = (int64_t)p.row_blocks * p.splits;
+  plan->banked_tables = p.banked;
 }
 
 }  // namespace

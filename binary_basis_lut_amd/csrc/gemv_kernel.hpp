@@ -83,16 +83,9 @@ void lut_gemv_kernel(const GemvArgs a) {
   const int rrow = row_ok ? row : 0;
 
   // The column range: segment sg, chunks [c_lo, c_lo + nch) of it.
-  const int gsp = a.kb * a.rpg;
-  const bool gpart = sp < gsp;
-  const int rel = gpart ? sp : sp - gsp;
-  const int nr = gpart ? a.rpg : a.rps;
-  const int sq = rel / nr;
-  const int rr = rel - sq * nr;
-  const int sg = (gpart ? 0 : a.kb) + sq;
-  const SegRef S = gemv_segment(a.seg, a.kb, sg);
-  const int c_lo = (int)(((uint32_t)rr * (uint32_t)S.nchunks) / (uint32_t)nr);
-  const int nch = (int)(((uint32_t)(rr + 1) * (uint32_t)S.nchunks) / (uint32_t)nr) - c_lo;
+  const ColRange cr = column_range(a, sp);
+  const SegRef S = cr.S;
+  const int sg = cr.sg, c_lo = cr.c_lo, nch = cr.nch;
   // element of this lane's 16 bytes in the range's first chunk; chunk u is 64 elements further
   const int64_t te0 = ((int64_t)ltile * S.nchunks + c_lo) * kTileRows + lane;
   const FB_GLOBAL u32x4 *wp = S.bits + te0;
@@ -208,7 +201,7 @@ void lut_gemv_kernel(const GemvArgs a) {
     // unit fixes the leading signs and branches on the rest as a tree, so its
     // entries round exactly like that sequence; the half with the top bit
     // clear is built from -v_{G-1} and is therefore the exact negation of
-    // the other half (LUT[~p] = -LUT[p]).
+    // the other half (LUT[~p] = -LUT[p]).  The g = 8 unit is g8_unit_entries.
     {
       constexpr int UPS = G == 4 ? 2 : 16;  // build units per sub-vector
       const int units = nch * NB * SUB * UPS;
@@ -237,21 +230,9 @@ void lut_gemv_kernel(const GemvArgs a) {
           }
         } else {
           // unit = (top bit h, low three bits q3); its 16 entries vary bits 3..6
-          const float4 va = *reinterpret_cast<const float4 *>(v);
-          const float4 vb = *reinterpret_cast<const float4 *>(v + 4);
+          float e[16];
+          g8_unit_entries(v, un, e);
           const int h = un >> 3, q3 = un & 7;
-          float base = h ? vb.w : -vb.w;
-          base = (q3 & 1) ? base + va.x : base - va.x;
-          base = (q3 & 2) ? base + va.y : base - va.y;
-          base = (q3 & 4) ? base + va.z : base - va.z;
-          const float l1[2] = {base - va.w, base + va.w};
-          float l2[4], l3[8], e[16];
-#pragma unroll
-          for (int i = 0; i < 2; ++i) l2[i] = l1[i] - vb.x, l2[i + 2] = l1[i] + vb.x;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) l3[i] = l2[i] - vb.y, l3[i + 4] = l2[i] + vb.y;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) e[i] = l3[i] - vb.z, e[i + 8] = l3[i] + vb.z;
           const int p0 = (h << 7) | q3;
           if constexpr (TQ == 0) {
             float *tb = s_tab + sv * TAB + p0;
@@ -339,54 +320,7 @@ void lut_gemv_kernel(const GemvArgs a) {
       for (int b = 0; b < NB; ++b) part[b] = rv * (TWO ? acc0[b] + acc1[b] : acc0[b]);
     }
 
-    // Output
-    if (a.splits == 1) {
-      if (row_ok) {
-#pragma unroll
-        for (int b = 0; b < NB; ++b)
-          if (b < a.batch) a.y[(int64_t)b * a.n + row] = f2h(part[b]);
-      }
-      return;
-    }
-    // splits > 1: every workgroup adds its partial sum of each row into that
-    // row's packed word with one agent-scope atomic (performed at the memory
-    // side, coherent across XCDs).  The atomic returns the previous word, so the
-    // lane that brings the last of `splits` contributions knows it is last and
-    // holds the complete sum: it writes y and clears the word for the next call.
-    // No workgroup waits for another, and since integer addition is exact the
-    // result does not depend on the order in which the splits arrive.  A
-    // partial outside the fixed-point range first sets the word's overflow
-    // flag (a rare second atomic on the same word, ordered before the add),
-    // and the row is written as NaN.
-    //
-    // With several batch rows, all NB atomics are issued before any result
-    // is examined, so that their round trips overlap instead of queueing one
-    // behind the other.
-    if (row_ok) {
-      uint64_t contrib[NB], old[NB];
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        const float scaled = part[b] * kFixScale;
-        const bool ovf = !(fabsf(scaled) < kFixLimit);  // NaN and inf overflow too
-        const int64_t q = ovf ? 0 : __float2ll_rn(scaled);  // an overflowing partial adds 0 (the row is NaN)
-        contrib[b] = (uint64_t)(q + kFixBias);
-        old[b] = 0;
-        if (b < a.batch) {
-          uint64_t *slot = a.acc + (int64_t)b * a.n_pad + row;
-          if (ovf) __hip_atomic_fetch_or(slot, kOverflow, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          old[b] = __hip_atomic_fetch_add(slot, contrib[b] + kOneArrival, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-      }
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        if (b < a.batch && (int)((old[b] >> kCountShift) & 0xffu) == a.splits - 1) {
-          const int64_t total = (int64_t)((old[b] & kValueMask) + contrib[b]) - (int64_t)a.splits * kFixBias;
-          a.y[(int64_t)b * a.n + row] = (old[b] & kOverflow) ? kHalfNaN : f2h(__ll2float_rn(total) * kFixInv);
-          __hip_atomic_store(a.acc + (int64_t)b * a.n_pad + row, (uint64_t)0, __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
-        }
-      }
-    }
+    finish_rows<NB>(a, row, row_ok, part);
   };
   if (sg < a.kb) {
     body(BoolTag<false>{});

@@ -295,7 +295,7 @@ def calibration_weights(k: int, outlier_frac: float = 0.0, seed: tuple = (0, 0, 
 def dyadic_layer(n: int, k: int, kb: int, ks: int, g: int, s: int, seed: int = 7) -> tuple:
     """A layer and activations whose every partial sum is exact in fp32.
 
-    x in {-2..2} * 2^-3, c in {2^-2, 2^-1, 1}, r in {2^-1, 1}.  Returns (Layer, x).
+    x in {-2..2} * 2^-3 (dyadic_x), c in {2^-2, 2^-1, 1}, r in {2^-1, 1}.  Returns the Layer.
     """
     rng = stream(99, seed)
     c_choices = np.array([0.25, 0.5, 1.0])

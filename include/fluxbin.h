@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define FLUXBIN_ABI_VERSION 5
+#define FLUXBIN_ABI_VERSION 6
 
 typedef enum {
   FLUXBIN_OK = 0,
@@ -167,6 +167,9 @@ typedef struct {
   int32_t total_chunks;     /* sum over segments of ceil(len/128) */
   int32_t lds_bytes;        /* LDS per workgroup at max_batch */
   int64_t grid;             /* workgroups per fluxbin_gemv launch (per group of batch rows) */
+  int32_t banked_tables;    /* 0: each sub-vector's table in consecutive dwords, one row per lane; 2 or 4
+                               (g = 8, one batch row, per-row scales, fp32 entries): bank-private tables,
+                               each a column of the LDS, over column ranges of up to that many chunks */
 } fluxbin_plan;
 
 int32_t fluxbin_abi_version(void);

@@ -332,6 +332,48 @@ def test_gemv_edge_cases(fb, orc, g, n, k, kb, ks, s, batch, cpb, waves):
     dl.close()
 
 
+# g = 8 bank-private tables (one batch row, per-row scales, fp32 entries): regions of 2 and 4 chunks
+# at 4 and 8 waves, column ranges shorter than the region (k = 1000: 8 chunks cut 3-3-2; k = 384: one
+# range of 3), rows that fill neither the last tile nor the last row block, a single row, salient
+# segments of 1 and 2 chunks, and the automatic plan.  Dyadic inputs must give RNE(exact) bitwise;
+# random inputs the rounding bound.
+BANKED = [
+    # n, k, kb, ks, s, cpb, waves, region
+    (4000, 1000, 3, 1, 200, 4, 8, 4),
+    (4000, 1000, 3, 1, 200, 3, 4, 4),
+    (4000, 1000, 3, 1, 200, 2, 8, 2),
+    (4000, 1000, 3, 1, 200, 2, 4, 2),
+    (4000, 1000, 3, 1, 200, 1, 8, 2),
+    (100, 11008, 3, 1, 220, 4, 8, 4),
+    (100, 11008, 3, 1, 220, 2, 4, 2),
+    (600, 384, 2, 2, 129, 4, 8, 4),
+    (600, 384, 2, 2, 129, 2, 8, 2),
+    (1, 4096, 1, 0, 0, 4, 8, 4),
+    (1, 4096, 1, 0, 0, 2, 4, 2),
+    (513, 4096, 4, 2, 82, 0, 0, None),
+    (300, 11008, 3, 1, 220, 0, 0, None),
+]
+
+
+@pytest.mark.parametrize("n,k,kb,ks,s,cpb,waves,region", BANKED)
+def test_g8_banked_tables(fb, orc, n, k, kb, ks, s, cpb, waves, region):
+    note(f"banked g=8 n={n} k={k} kb={kb} ks={ks} s={s} cpb={cpb} waves={waves}")
+    layer = I.dyadic_layer(n, k, kb, ks, 8, s, seed=n + 3 * k + cpb)
+    x = I.dyadic_x(k, 1, seed=k + cpb)
+    dl = fb.DeviceLayer(layer, chunks_per_block=cpb, waves_per_block=waves)
+    assert dl.plan["banked_tables"] == (region or (4 if dl.plan["chunks_per_block"] > 2 else 2))
+    y16 = gemv(fb, dl, x)
+    y_ref, _ = orc.gemv_dense(layer, x)
+    assert np.array_equal(y16, orc.double_to_half(y_ref)), "y differs from RNE(exact)"
+    dl.close()
+    layer = I.make_layer(n, k, kb, ks, 8, s=s if ks else None, outlier_frac=0.01, seed=(65, n, k))
+    x = I.make_x(layer, 1, seed=(65, n, k))
+    dl = fb.DeviceLayer(layer, chunks_per_block=cpb, waves_per_block=waves)
+    y16 = gemv(fb, dl, x)
+    check_y(orc, layer, x, y16, dl.plan)
+    dl.close()
+
+
 def test_batch_zero_is_a_no_op(fb):
     layer = I.workload_layer(1)
     dl = fb.DeviceLayer(layer)

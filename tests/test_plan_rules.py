@@ -77,16 +77,25 @@ def test_wide_layers_keep_four_waves(fb):
 
 def test_g8_layers_take_eight_waves_within_the_lds_budget(fb):
     # 7B layer, 3 global bases + 2 % salient, g = 8: 512 rows per workgroup; a chunk's g = 8
-    # tables are 16 sub-vectors x 256 entries, 16 KiB per batch row (fp32), so qkv and down take
-    # 2-chunk ranges and the gate+up projection 4 (64 KiB of tables plus the staged inputs)
-    expect = {0: (2, 49), 1: (2, 49), 2: (4, 25), 3: (2, 130)}
+    # tables are 16 sub-vectors x 256 entries, 16 KiB per batch row (fp32).  The bank-private layout
+    # takes 2-chunk ranges (four workgroups per CU), or 4 for the down projection, whose 86 chunks
+    # per basis would otherwise make 130 ranges
+    expect = {0: (2, 49), 1: (2, 49), 2: (2, 49), 3: (4, 67)}
     for shape, (cpb, splits) in expect.items():
         p = plan(fb, workload_desc(fb, 3, shape))
         assert (p["rows_per_block"], p["chunks_per_block"], p["splits"]) == (512, cpb, splits), shape
-    assert plan(fb, workload_desc(fb, 3, 2))["lds_bytes"] == 4 * (16 * 256 * 4 + 128 * 4) + 256
-    # fp16 entries halve the tables
-    assert plan(fb, workload_desc(fb, 3, 2, table_precision=fb.TABLE_F16, chunks_per_block=4))["lds_bytes"] == \
-        4 * (16 * 256 * 2 + 128 * 4) + 256
+        # one batch row, per-row scales, fp32 entries: bank-private tables over the range's chunks
+        assert p["banked_tables"] == (4 if cpb > 2 else 2), shape
+        assert p["lds_bytes"] == p["banked_tables"] * (16 * 256 * 4 + 128 * 4), shape
+    # fp16 entries halve the tables (and keep the one-table-per-sub-vector layout)
+    p = plan(fb, workload_desc(fb, 3, 2, table_precision=fb.TABLE_F16, chunks_per_block=4))
+    assert p["lds_bytes"] == 4 * (16 * 256 * 2 + 128 * 4) + 256 and p["banked_tables"] == 0
+    # the natural layout's own rule for a batched g = 8 layer
+    assert plan(fb, workload_desc(fb, 3, 2, max_batch=2))["chunks_per_block"] == 2
+    # so do batched and block-wise g = 8 layers, and every g = 4 layer
+    assert plan(fb, workload_desc(fb, 3, 2, max_batch=2))["banked_tables"] == 0
+    assert plan(fb, blockwise_desc(fb, 4096, 4096, g=8))["banked_tables"] == 0
+    assert plan(fb, workload_desc(fb, 5, 2))["banked_tables"] == 0
 
 
 def test_explicit_choices_override_the_rules(fb):
