@@ -35,7 +35,6 @@ Prints one JSON line.  --out FILE also writes the detail as JSON.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import math
 import os
@@ -48,20 +47,14 @@ import numpy as np
 ROOT = Path(__file__).resolve().parent
 sys.path.insert(0, str(ROOT))
 
+from binary_basis_lut_amd import rocprof_summary as RS  # noqa: E402  (host-only helpers: hashes, no GPU)
+
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, decimal GB/s
 HEADLINE = 5            # LLaMA-2-70B decode layers
 N_LAYERS = 80
 STREAM_7B = 3           # LLaMA-2-7B layers at g = 8
 N_LAYERS_7B = 32
 PAGES_A100_US = 41.0    # FluxBin summary, appendix E.4: isolated 4096x4096 2-bit GEMV on A100
-
-
-def kernel_source_hash() -> str:
-    h = hashlib.sha256()
-    for p in ["binary_basis_lut_amd/csrc/common.hpp", "binary_basis_lut_amd/csrc/gemv_kernel.hpp",
-              "binary_basis_lut_amd/csrc/fluxbin.hip"]:
-        h.update((ROOT / p).read_bytes())
-    return h.hexdigest()[:16]
 
 
 def measured_traffic(name: str):
@@ -73,7 +66,7 @@ def measured_traffic(name: str):
         d = json.loads(f.read_text())
     except Exception:
         return None, "unreadable counter summary"
-    if d.get("kernel_source_hash") != kernel_source_hash():
+    if d.get("kernel_source_hash") != RS.kernel_source_hash():
         return None, "counters were taken on another kernel source"
     return d.get("hbm_bytes_per_launch"), d.get("note")
 
@@ -244,6 +237,17 @@ def lookup_probe(torch, F, configs, iters=400, reps=3):
     return out
 
 
+def banked_lookup_rate(torch, F, region, iters=400, reps=3):
+    """Lookups per second of the g = 8 bank-private tables (the banked GEMV's lookup instructions)."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    wgs = cus * (4 if region == 2 else 2) * 2
+    sink = torch.zeros(wgs * 512, dtype=torch.float32, device="cuda")
+    F.fluxbin_probe_lds_lookup_banked(region, wgs, iters, -1.0, sink)
+    sec = timed(torch, torch.cuda.current_stream(),
+                lambda: [F.fluxbin_probe_lds_lookup_banked(region, wgs, iters, -1.0, sink) for _ in range(reps)])
+    return wgs * 512 * iters * 16 * region * reps / sec
+
+
 def cpu_baseline(O, model, ys_gpu, budget_s: float):
     """The fp64 oracle, as it is, on the host cores: layer 0's four GEMVs, repeated for ~budget_s.
 
@@ -377,14 +381,23 @@ def main() -> int:
         s7 = timed(torch, stream, lambda: [g7.replay() for _ in range(reps)])
         per7, _ = per_gemv_durations(torch, F, m7, stream)
         b7 = sum(m7.bytes)
+        plans7 = [F.fluxbin_get_plan(m7.handles[0][i]) for i in range(len(m7.wl.shapes))]
+        brates = {r: banked_lookup_rate(torch, F, r) for r in sorted({p["banked_tables"] for p in plans7}) if r}
+
+        def lookup_floor_us(i):
+            lay, r = m7.layer0[i], plans7[i]["banked_tables"]
+            return A.lookups(lay.n, lay.k, lay.s, lay.kb, lay.ks, lay.g, 1) / brates[r] * 1e6 if r else None
         extra["llama2_7b_g8_stream"] = {
             "workload": m7.wl.name, "layers": N_LAYERS_7B, "bytes_per_layer": b7,
             "us_per_layer": round(s7 * 1e6 / (reps * N_LAYERS_7B), 3),
             "gbs": round(b7 * reps * N_LAYERS_7B / s7 / 1e9, 1),
             "pct_hbm_peak": round(100 * b7 * reps * N_LAYERS_7B / s7 / 1e9 / HBM_PEAK_GBS, 2),
             "per_gemv": {s.name: {"us": round(per7[s.name], 3), "gbs": round(m7.bytes[i] / per7[s.name] / 1e3, 1),
-                                  "plan": F.fluxbin_get_plan(m7.handles[0][i])}
+                                  "lookup_roofline_us": round(lookup_floor_us(i), 3),
+                                  "frac_of_lookup_roofline": round(lookup_floor_us(i) / per7[s.name], 4),
+                                  "plan": plans7[i]}
                          for i, s in enumerate(m7.wl.shapes)},
+            "banked_lookup_rate_per_s": {f"region{r}": v for r, v in brates.items()},
         }
         m7.close(F)
         del m7, g7
@@ -476,7 +489,7 @@ def main() -> int:
     print(json.dumps(line), flush=True)
     detail.update(line)
     detail["traffic_note"] = traffic_note
-    detail["kernel_source_hash"] = kernel_source_hash()
+    detail["kernel_source_hash"] = RS.kernel_source_hash()
     if args.out:
         Path(args.out).parent.mkdir(parents=True, exist_ok=True)
         Path(args.out).write_text(json.dumps(detail, indent=1, default=str))

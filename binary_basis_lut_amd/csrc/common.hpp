@@ -19,8 +19,10 @@
 //
 // Mapping onto CDNA4 (not the pages' A100 tiling):
 //   * one wave = 64 output rows, lane l = row l of its tile; all 64 lanes read
-//     the SAME 2^g-entry table at each step, so table reads are broadcasts
-//     within 16 (g=4) or 256 (g=8) consecutive dwords;
+//     the SAME 2^g-entry table at each step: at g = 4 a read of 16
+//     consecutive dwords, conflict-free; at g = 8 (one batch row, per-row
+//     scales, fp32 entries) the tables are instead laid out one per LDS bank
+//     and the lanes spread over them (gemv_banked.hpp);
 //   * weights are streamed from the TILED layout: a wave's 16-byte-per-lane
 //     load of one 128-column chunk is 1 KiB of contiguous memory, loaded with
 //     non-temporal 128-bit loads (streamed once, kept out of L2);

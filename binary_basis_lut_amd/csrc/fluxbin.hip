@@ -1015,6 +1015,30 @@ fluxbin_status fluxbin_probe_lds_lookup(int32_t g, int32_t nb, int64_t workgroup
   return ok();
 }
 
+fluxbin_status fluxbin_probe_lds_lookup_banked(int32_t region, int64_t workgroups, int32_t iters, float never,
+                                               float *sink, void *stream) {
+  if (!sink) return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "sink is NULL");
+  if (workgroups < 1 || workgroups > 65536 || iters < 1)
+    return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "workgroups = %lld (1..65536), iters = %d (>= 1)", (long long)workgroups,
+                iters);
+  if (region != 2 && region != 4) return fail(FLUXBIN_ERR_UNSUPPORTED, "region = %d (2 or 4)", region);
+  const void *fn = region == 4 ? reinterpret_cast<const void *>(lds_lookup_banked_kernel<4>)
+                               : reinterpret_cast<const void *>(lds_lookup_banked_kernel<2>);
+  const int lds = region * 16 * 256 * 4;
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (e != hipSuccess) return hip_fail(e, "setting the probe's dynamic LDS size");
+  const uint32_t seed = 0x2545F491u;
+  if (region == 4)
+    hipLaunchKernelGGL(lds_lookup_banked_kernel<4>, dim3((unsigned)workgroups), dim3(512), lds, (hipStream_t)stream,
+                       iters, seed, never, sink);
+  else
+    hipLaunchKernelGGL(lds_lookup_banked_kernel<2>, dim3((unsigned)workgroups), dim3(512), lds, (hipStream_t)stream,
+                       iters, seed, never, sink);
+  e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "banked lookup probe launch");
+  return ok();
+}
+
 fluxbin_status fluxbin_dense_gemv_f16(const uint16_t *w, int64_t n, int64_t k, const uint16_t *x, uint16_t *y,
                                       int64_t batch, void *stream) {
   if (n < 1 || k < 1) return fail(FLUXBIN_ERR_INVALID_ARGUMENT, "n, k must be >= 1");

@@ -33,6 +33,52 @@
 
 namespace fluxbin {
 
+// One lane's view of a banked region of R chunks: lane (c, r) of chunk c
+// looks up, at step (q, kk) of a 16-byte group of sign words, sub-vector
+// t = (4 q + kk) XOR r, table T = 16 c + t.  slot[q] holds in byte kk the
+// byte SLOT * T, sel[kk] is the v_perm_b32 selector that puts that byte into
+// bits 0-7 of the address and byte kk XOR (r mod 4) of the reordered word
+// into bits 8-15 (the pattern p), giving p * 256 + 4 T (R = 4), or
+// p * 256 + 8 T, halved to p * 128 + 4 T (R = 2).
+template <int R>
+struct BankedLane {
+  static constexpr uint32_t SLOT = R == 4 ? 4 : 8;
+  uint32_t slot[4], sel[4];
+  bool b0, b1;
+
+  __device__ __forceinline__ BankedLane(int c, int r) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      uint32_t sv = 0;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) sv |= (SLOT * (uint32_t)(16 * c + ((4 * q + kk) ^ r))) << (8 * kk);
+      slot[q] = sv;
+    }
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) sel[kk] = 0x0c0c0000u | ((uint32_t)(kk ^ (r & 3)) << 8) | (uint32_t)(4 + kk);
+    b0 = (r >> 2) & 1;
+    b1 = (r >> 3) & 1;
+  }
+
+  // the lane's four words in step order: word q is word q XOR (r / 4)
+  __device__ __forceinline__ void order(const u32x4 w, uint32_t (&ew)[4]) const {
+    const uint32_t f0 = b0 ? w[1] : w[0], f1 = b0 ? w[0] : w[1];
+    const uint32_t f2 = b0 ? w[3] : w[2], f3 = b0 ? w[2] : w[3];
+    ew[0] = b1 ? f2 : f0;
+    ew[1] = b1 ? f3 : f1;
+    ew[2] = b1 ? f0 : f2;
+    ew[3] = b1 ? f1 : f3;
+  }
+
+  // the table entry of step (q, kk) for the reordered words ew (the region
+  // starts at LDS address 0)
+  __device__ __forceinline__ float entry(const uint32_t (&ew)[4], int q, int kk) const {
+    uint32_t ad = __builtin_amdgcn_perm(slot[q], ew[q], sel[kk]);
+    if constexpr (R == 2) ad >>= 1;
+    return lds_f32(ad);
+  }
+};
+
 // R = 2 layouts take 33 KiB: four workgroups of 8 waves fit a CU, and the
 // registers are held to 64 for 8 waves per SIMD.
 template <int R, int WAVES>
@@ -51,7 +97,6 @@ void lut_gemv_g8_banked_kernel(const GemvArgs a) {
   constexpr int VPT = ITEMS >= NT ? ITEMS / NT : 1;
   constexpr int GR = 64 / R;          // rows of one row group: 16 rows per chunk lane group x R chunks = 64 lanes
   constexpr int NG = R;               // row groups of the wave's 64-row tile
-  constexpr uint32_t SLOT = R == 4 ? 4 : 8;  // slot byte per table: 4 T (R = 4) or 8 T, halved after the merge
   static_assert(ITEMS % NT == 0 || NT % ITEMS == 0, "staging rounds");
   extern __shared__ __align__(1024) float smem[];
   float *s_tab = smem;
@@ -157,34 +202,10 @@ void lut_gemv_g8_banked_kernel(const GemvArgs a) {
     }
     __syncthreads();
 
-    // Per-lane constants of the lookups: slot[q] byte kk = SLOT * T for the
-    // table of step (q, kk); sel[kk] takes that byte into bits 0-7 and byte
-    // kk XOR (r mod 4) of the permuted word into bits 8-15.
-    const int s1 = r & 3, s2 = r >> 2;
-    uint32_t slot[4], sel[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      uint32_t sv = 0;
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) sv |= (SLOT * (uint32_t)(16 * c + ((4 * q + kk) ^ r))) << (8 * kk);
-      slot[q] = sv;
-    }
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) sel[kk] = 0x0c0c0000u | ((uint32_t)(kk ^ s1) << 8) | (uint32_t)(4 + kk);
-    const bool b0 = s2 & 1, b1 = (s2 >> 1) & 1;
-
-    // this lane's words in step order: word q is word q XOR s2 of the chunk
+    const BankedLane<R> L(c, r);
     uint32_t ew[NG][4];
 #pragma unroll
-    for (int g = 0; g < NG; ++g) {
-      const u32x4 w = wb[g];
-      const uint32_t f0 = b0 ? w[1] : w[0], f1 = b0 ? w[0] : w[1];
-      const uint32_t f2 = b0 ? w[3] : w[2], f3 = b0 ? w[2] : w[3];
-      ew[g][0] = b1 ? f2 : f0;
-      ew[g][1] = b1 ? f3 : f1;
-      ew[g][2] = b1 ? f0 : f2;
-      ew[g][3] = b1 ? f1 : f3;
-    }
+    for (int g = 0; g < NG; ++g) L.order(wb[g], ew[g]);
     // the row groups' lookups of one step go out together (independent reads)
     float acc[NG][2];
 #pragma unroll
@@ -194,11 +215,7 @@ void lut_gemv_g8_banked_kernel(const GemvArgs a) {
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
-        for (int g = 0; g < NG; ++g) {
-          uint32_t ad = __builtin_amdgcn_perm(slot[q], ew[g][q], sel[kk]);
-          if constexpr (R == 2) ad >>= 1;  // p * 128 + 4 T
-          acc[g][kk & 1] += lds_f32(ad);
-        }
+        for (int g = 0; g < NG; ++g) acc[g][kk & 1] += L.entry(ew[g], q, kk);
       }
     }
 

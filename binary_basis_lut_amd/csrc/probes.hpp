@@ -9,10 +9,12 @@
 //   * lds_lookup_kernel: the rate of the GEMV's table lookups alone (LDS
 //     reads plus their address and accumulate instructions) with weights held
 //     in registers, for a table width and batch width: the roofline of the
-//     batch path, which at several batch rows is bound by lookups, not HBM.
+//     batch path, which at several batch rows is bound by lookups, not HBM;
+//   * lds_lookup_banked_kernel: the same for the g = 8 bank-private tables.
 #pragma once
 
 #include "common.hpp"
+#include "gemv_banked.hpp"
 
 namespace fluxbin {
 
@@ -89,6 +91,58 @@ __global__ __launch_bounds__(256) void lds_lookup_kernel(int32_t iters, uint32_t
 #pragma unroll
   for (int b = 0; b < NB; ++b) s += acc0[b] + acc1[b];
   if (s == never) sink[blockIdx.x * 256 + tid] = s;
+}
+
+// The banked g = 8 lookups of lut_gemv_g8_banked_kernel (BankedLane) on a
+// region of R chunks, 8 waves per workgroup as in the GEMV: every lane holds
+// R groups of 16 bytes of sign words (per-lane hash) and looks them up
+// `iters` times, 16 R lookups per iteration.
+template <int R>
+__global__ __launch_bounds__(512) void lds_lookup_banked_kernel(int32_t iters, uint32_t seed, float never,
+                                                               float *sink) {
+  constexpr int NTAB = 16 * R;
+  extern __shared__ __align__(1024) float smem[];
+  const int tid = threadIdx.x;
+  if (lds_addr(smem) != 0) return;  // the banked addresses carry no base (no static LDS here)
+  for (int e = tid; e < NTAB * 256; e += blockDim.x) smem[e] = (float)(e & 1023) * 0.001f;
+  __syncthreads();
+  const int lane = tid & 63;
+  const BankedLane<R> L((lane >> 4) % R, lane & 15);
+  uint32_t h = seed ^ (uint32_t)(blockIdx.x * 512 + tid) * 0x9e3779b9u;
+  u32x4 w[R];
+#pragma unroll
+  for (int g = 0; g < R; ++g) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      h ^= h << 13;
+      h ^= h >> 17;
+      h ^= h << 5;
+      w[g][q] = h;
+    }
+  }
+  float acc[R][2];
+#pragma unroll
+  for (int g = 0; g < R; ++g) acc[g][0] = acc[g][1] = 0.0f;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int g = 0; g < R; ++g) asm volatile("" : "+v"(w[g]));
+    uint32_t ew[R][4];
+#pragma unroll
+    for (int g = 0; g < R; ++g) L.order(w[g], ew[g]);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+        for (int g = 0; g < R; ++g) acc[g][kk & 1] += L.entry(ew[g], q, kk);
+      }
+    }
+    asm volatile("" ::: "memory");
+  }
+  float s = 0.0f;
+#pragma unroll
+  for (int g = 0; g < R; ++g) s += acc[g][0] + acc[g][1];
+  if (s == never) sink[blockIdx.x * 512 + tid] = s;
 }
 
 }  // namespace fluxbin

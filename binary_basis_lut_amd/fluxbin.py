@@ -92,6 +92,7 @@ _decl("fluxbin_dense_gemv_f16", ctypes.c_int, [P, I64, I64, P, P, I64, P])
 _decl("fluxbin_probe_stream_read", ctypes.c_int, [P, I64, I32, I64, ctypes.c_uint32, P, P])
 _decl("fluxbin_probe_empty", ctypes.c_int, [I64, I32, P])
 _decl("fluxbin_probe_lds_lookup", ctypes.c_int, [I32, I32, I64, I32, ctypes.c_float, P, P])
+_decl("fluxbin_probe_lds_lookup_banked", ctypes.c_int, [I32, I64, I32, ctypes.c_float, P, P])
 _decl("fluxbin_decomp_workspace_size", ctypes.c_int, [I64, I64, I32, ctypes.POINTER(ctypes.c_size_t)])
 _decl("fluxbin_decompose", ctypes.c_int, [P, I64, I64, I32, I32, P, P, P, P, P, P, P, P, ctypes.c_size_t, P])
 _decl("fluxbin_decomp_row_scales", ctypes.c_int, [P, I64, I64, I32, I32, P, P, P, P, P, P, ctypes.c_size_t, P])
@@ -106,7 +107,8 @@ SYMBOLS = [
     "fluxbin_workspace_size", "fluxbin_create", "fluxbin_destroy", "fluxbin_get_plan", "fluxbin_plan_of",
     "fluxbin_lut_size",
     "fluxbin_build_lut", "fluxbin_gemv", "fluxbin_gemv_timed", "fluxbin_gemv_static", "fluxbin_reset_workspace", "fluxbin_dense_gemv_f16",
-    "fluxbin_probe_stream_read", "fluxbin_probe_empty", "fluxbin_probe_lds_lookup", "fluxbin_decomp_workspace_size",
+    "fluxbin_probe_stream_read", "fluxbin_probe_empty", "fluxbin_probe_lds_lookup", "fluxbin_probe_lds_lookup_banked",
+    "fluxbin_decomp_workspace_size",
     "fluxbin_decompose", "fluxbin_decomp_row_scales", "fluxbin_decomp_col_scales", "fluxbin_decomp_signs",
     "fluxbin_decomp_residual_signs", "fluxbin_decomp_error",
 ]
@@ -245,6 +247,11 @@ def fluxbin_probe_empty(workgroups, threads, stream=None):
 def fluxbin_probe_lds_lookup(g, nb, workgroups, iters, never, sink, stream=None):
     _check(_lib.fluxbin_probe_lds_lookup(g, nb, workgroups, iters, never, _ptr(sink), _stream(stream)),
            "fluxbin_probe_lds_lookup")
+
+
+def fluxbin_probe_lds_lookup_banked(region, workgroups, iters, never, sink, stream=None):
+    _check(_lib.fluxbin_probe_lds_lookup_banked(region, workgroups, iters, never, _ptr(sink), _stream(stream)),
+           "fluxbin_probe_lds_lookup_banked")
 
 
 def fluxbin_dense_gemv_f16(w, n, k, x, y, batch, stream=None):

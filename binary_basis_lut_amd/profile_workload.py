@@ -37,9 +37,11 @@ profiles/ (each summary names the exact command).  Two modes:
 
   python3 -m binary_basis_lut_amd.profile_workload lookup --iters 2000 --reps 5
       the table-lookup rate alone (fluxbin_probe_lds_lookup) for g = 4 at 1, 2,
-      4, 8, 16 batch rows and g = 8 at 1, 2, 4: lookups per second, per CU per
-      clock (2.4 GHz), and the packed-weight GB/s that rate would sustain at
-      b = 1 (one lookup per g bits).
+      4, 8, 16 batch rows and g = 8 at 1, 2, 4, and of the g = 8 bank-private
+      tables (fluxbin_probe_lds_lookup_banked) over 2- and 4-chunk regions:
+      lookups per second, per CU per clock (2.4 GHz), and the packed-weight
+      GB/s that rate would sustain (one lookup per g bits of one row's
+      weights, divided by the batch rows that share them).
 """
 from __future__ import annotations
 
@@ -285,6 +287,23 @@ def run_lookup(args) -> None:
         gbs = rate / nb * g / 8 / 1e9
         print(f"lookups g={g} batch rows={nb}: {rate / 1e12:.3f} T lookups/s, {per_cu_clk:.2f} per CU per clock, "
               f"weight stream it sustains {gbs:.0f} GB/s", flush=True)
+    # the g = 8 bank-private tables (one batch row), 8 waves per workgroup, as many workgroups per CU as
+    # the GEMV runs (4 with 2-chunk regions, 2 with 4-chunk ones)
+    for region, per_cu in ((2, 4), (4, 2)):
+        wgs_b = cus * per_cu * 2
+        sink_b = torch.zeros(wgs_b * 512, dtype=torch.float32, device="cuda")
+        F.fluxbin_probe_lds_lookup_banked(region, wgs_b, args.iters, -1.0, sink_b)
+        torch.cuda.synchronize()
+        e0, e1 = _events()
+        e0.record()
+        for _ in range(args.reps):
+            F.fluxbin_probe_lds_lookup_banked(region, wgs_b, args.iters, -1.0, sink_b)
+        e1.record()
+        torch.cuda.synchronize()
+        s = e0.elapsed_time(e1) * 1e-3 / args.reps
+        rate = wgs_b * 512 * args.iters * 16 * region / s
+        print(f"lookups g=8 banked tables, {region}-chunk regions: {rate / 1e12:.3f} T lookups/s, "
+              f"{rate / cus / 2.4e9:.2f} per CU per clock, weight stream it sustains {rate / 1e9:.0f} GB/s", flush=True)
 
 
 def main() -> int:

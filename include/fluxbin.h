@@ -349,6 +349,16 @@ fluxbin_status fluxbin_probe_empty(int64_t workgroups, int32_t threads, void *st
 fluxbin_status fluxbin_probe_lds_lookup(int32_t g, int32_t nb, int64_t workgroups, int32_t iters, float never,
                                         float *sink, void *stream);
 
+/* The same for the g = 8 bank-private tables of one batch row (the lookups of
+ * the banked GEMV kernel: each lane's sub-vector order rotated by its row, one
+ * v_perm_b32 per address, one fp32 add per lookup) over a region of `region`
+ * (2 or 4) chunks: `workgroups` workgroups of 512 threads with region * 16 KiB
+ * of LDS, each lane looking up region groups of 16 bytes `iters` times.
+ * sink: float [workgroups * 512], written only if a lane's sum equals `never`.
+ * FLUXBIN_ERR_UNSUPPORTED for another region. */
+fluxbin_status fluxbin_probe_lds_lookup_banked(int32_t region, int64_t workgroups, int32_t iters, float never,
+                                               float *sink, void *stream);
+
 /* ------------------------------------------------------------------------
  * Offline decomposition W ~ sum_{b<kb} diag(r_b) B_b diag(c_b), the step that
  * produces the bases the GEMV streams (FluxBin summary, section 3 bullets

@@ -366,7 +366,11 @@ static inline uint32_t pattern_at(const uint32_t *row_words, int32_t g, int64_t 
  * the precision the GPU kernel takes them -- the half-table entry
  * v_{g-1} + sum_{t<g-1} (+-v_t) summed in fp32 in that order (each v_t =
  * c_t x_t is exact in fp32), rounded to fp16 (nearest even); the other half
- * is its negation.  Returns 0 and writes lut (2^g entries). */
+ * is its negation.  Returns 0 and writes lut (2^g entries).
+ * table_fmt 1 mirrors the kernel's entry arithmetic on purpose, so it is a
+ * diagnostic (it localises a failure to the table build or to the
+ * accumulation), not a reference: the fp16-table contract is the bound
+ * against the exact product (format 0 / orc_gemv_dense). */
 static void quantised_table(int32_t g, const double *v, int32_t table_fmt, double *lut) {
   int64_t tsize = (int64_t)1 << g, half = tsize / 2;
   if (table_fmt == 0) {

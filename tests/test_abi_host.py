@@ -200,6 +200,9 @@ def test_reset_and_probes_reject_on_the_host(fb):
     assert s("fluxbin_probe_lds_lookup", I32(8), I32(8), I64(8), I32(1), ctypes.c_float(0), P, None) == 2
     assert s("fluxbin_probe_lds_lookup", I32(4), I32(1), I64(8), I32(0), ctypes.c_float(0), P, None) == 1
     assert s("fluxbin_probe_lds_lookup", I32(4), I32(1), I64(8), I32(1), ctypes.c_float(0), None, None) == 1
+    assert s("fluxbin_probe_lds_lookup_banked", I32(3), I64(8), I32(1), ctypes.c_float(0), P, None) == 2
+    assert s("fluxbin_probe_lds_lookup_banked", I32(4), I64(0), I32(1), ctypes.c_float(0), P, None) == 1
+    assert s("fluxbin_probe_lds_lookup_banked", I32(2), I64(8), I32(1), ctypes.c_float(0), None, None) == 1
 
 
 def test_launching_calls_reject_bad_arguments_on_the_host(fb):

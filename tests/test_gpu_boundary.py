@@ -182,5 +182,8 @@ def test_measurement_kernels_run(fb):
     fs = torch.zeros(64 * 256, dtype=torch.float32, device="cuda")
     for g, nb in ((4, 1), (4, 4), (4, 16), (8, 1), (8, 4)):
         fb.fluxbin_probe_lds_lookup(g, nb, 64, 4, -1.0, fs)  # table entries are >= 0 and sums finite: never -1
+    fb2 = torch.zeros(64 * 512, dtype=torch.float32, device="cuda")
+    for region in (2, 4):
+        fb.fluxbin_probe_lds_lookup_banked(region, 64, 4, -1.0, fb2)
     torch.cuda.synchronize()
-    assert int(sink.abs().sum()) == 0 and float(fs.abs().sum()) == 0.0
+    assert int(sink.abs().sum()) == 0 and float(fs.abs().sum()) == 0.0 and float(fb2.abs().sum()) == 0.0

@@ -1,14 +1,18 @@
 """GPU parity of the fp16-table GEMV (quantised tables, LUT Tensor Core notes, section 3.1.3).
 
-Reference: the oracle's LUT route with fp16 entries built in the kernel's precision (fp32 sum in
-the kernel's order, rounded to fp16 once), so that the kernel and the reference quantise every
-entry identically.  Bars:
-  * against that reference: the rigorous fp32 accumulation + fp16 output bound of test_gpu_parity
-    (the kernel differs from it only by fp32 accumulation and the output rounding);
-  * against the exact product: the quantisation tolerance (2^-11 + g 2^-24) M plus the same
-    accumulation bound, M = sum over segments of |r| * sum |c x| (this format's own tolerance:
-    it is looser than the 1e-3 * sum|W_hat x| contract of the fp32 tables);
-  * dyadic inputs (every entry exact in fp16): y equal to RNE(exact).
+The contract of this format (what the tests hold the kernel to):
+  * against the exact product (the oracle's fp64 dense route): |y - y_exact| <= (2^-11 + g 2^-24) M
+    plus the rigorous fp32 accumulation + fp16 output bound of test_gpu_parity, with
+    M = sum over segments of |r| * sum |c x|.  This is the format's own tolerance, looser than the
+    1e-3 * sum|W_hat x| contract of the fp32 tables: each entry is one fp16 rounding of a sum of g
+    terms;
+  * dyadic inputs (every entry exact in fp16): y equal to RNE(exact), bitwise.
+
+A diagnostic, not the contract: the oracle's LUT route with fp16 entries built the way the kernel
+builds them (fp32 sum in the kernel's order, rounded to fp16 once) quantises every entry like the
+kernel, so the kernel must also sit within the plain accumulation bound of that route.  That
+route mirrors the kernel's entry arithmetic, so it pins nothing by itself; it only localises a
+failure (table build versus accumulation) when the contract check fails.
 """
 import numpy as np
 import pytest
@@ -34,18 +38,21 @@ def check_fp16_tables(orc, layer, x, y16, plan, rows=None):
     rows = np.arange(layer.n) if rows is None else np.asarray(rows)
     y = orc.half_to_double(y16[:, rows])
     assert np.all(np.isfinite(y))
-    y_q = orc.gemv_lut_fp16_tables(layer, x, rows=rows)
     y_ex, mag = orc.gemv_dense(layer, x, rows=rows)
     M = magnitude(layer, x, rows)
     steps = layer.g + max(layer.k, layer.s) / layer.g + layer.kb + layer.ks + plan["splits"] + 3
     fp32 = 2.0 ** -24 * steps * M + plan["splits"] * 2.0 ** -30
+    # the contract: the exact product within the format's quantisation tolerance
+    tight_ex = 2.0 ** -11 * (np.abs(y_ex) + fp32) * (1 + 2.0 ** -23) + fp32 + 2.0 ** -25
+    quant = (2.0 ** -11 + layer.g * 2.0 ** -24) * M + tight_ex
+    err = np.abs(y - y_ex)
+    assert np.all(err <= quant), f"contract (vs exact product): worst ratio {float((err / quant).max()):.3g}"
+    # diagnostic: the kernel-order fp16 tables of the oracle's LUT route, accumulation bound only
+    y_q = orc.gemv_lut_fp16_tables(layer, x, rows=rows)
     tight = 2.0 ** -11 * (np.abs(y_q) + fp32) * (1 + 2.0 ** -23) + fp32 + 2.0 ** -25
     err_q = np.abs(y - y_q)
-    assert np.all(err_q <= tight), f"vs quantised reference: worst ratio {float((err_q / tight).max()):.3g}"
-    quant = (2.0 ** -11 + layer.g * 2.0 ** -24) * M + tight
-    err = np.abs(y - y_ex)
-    assert np.all(err <= quant), f"vs exact: worst ratio {float((err / quant).max()):.3g}"
-    return float((err_q / tight).max()), float((err / (1e-3 * mag)).max())
+    assert np.all(err_q <= tight), f"diagnostic (vs kernel-order fp16 tables): worst ratio {float((err_q / tight).max()):.3g}"
+    return float((err / quant).max()), float((err_q / tight).max())
 
 
 EXACT = [
@@ -103,7 +110,7 @@ def test_fp16_tables_workloads(fb, orc, name, cid, shape_idx, batch, sg):
     rows = None if n <= 4096 else np.unique(np.concatenate([np.arange(32), np.arange(n - 32, n),
                                                              I.stream(110, n).choice(n, 256, replace=False)]))
     r = check_fp16_tables(orc, layer, x, y16, dl.plan, rows)
-    print(name, "plan", dl.plan, "ratios (vs quantised ref / contract vs exact):", r)
+    print(name, "plan", dl.plan, "ratios (contract vs exact / diagnostic vs kernel-order tables):", r)
     dl.close()
 
 

@@ -2,10 +2,13 @@
 section 3.1.3: table entries stored in a lower, uniform precision).
 
 The entries are built as the kernel builds them: the half-table sum in fp32 in a fixed order,
-rounded to fp16 (nearest even), the other half negated.  Pins: the entries against numpy's own
-float32 arithmetic and float16 cast; the symmetry LUT[~p] = -LUT[p]; exactness when every
-entry is representable in fp16 (dyadic inputs: the quantised route equals the exact product);
-and the quantisation bound against the exact product on random inputs.
+rounded to fp16 (nearest even), the other half negated.  That route is a diagnostic for the GPU
+tests (it mirrors the kernel's entry arithmetic); the contract of the fp16-table format is the
+bound against the exact product.  Pins: the entries against numpy's own float32 arithmetic and
+float16 cast (which only restates the rounding rule); the symmetry LUT[~p] = -LUT[p]; exactness
+when every entry is representable in fp16 (dyadic inputs: the quantised route equals the exact
+product); and the quantisation bound against the exact product on random inputs, which is the
+pin that ties the route to the mathematics.
 """
 import numpy as np
 import pytest
