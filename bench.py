@@ -26,7 +26,8 @@ at each kernel's own start and end, over an eager pass of the 80 layers (the
 gate+up projection is the dominant kernel of the roofline object); the HBM read rate of the GEMV's access pattern
 (fluxbin_probe_stream_read, the measured peak); the table-lookup rate
 (fluxbin_probe_lds_lookup) that bounds the batch path; the LLaMA-2-7B q_proj
-call on 256 resident sets; the LLaMA-2-7B 32-layer g = 8 stream; the
+call on 256 resident sets; the LLaMA-2-7B 32-layer g = 8 stream, each GEMV
+against the banked lookup rate (fluxbin_probe_lds_lookup_banked); the
 4096->11008 / 11008->4096 batch sweep; the hand-written dense fp16 GEMV on the
 70B shapes; and the fp64 oracle on the host cores (cpu_baseline).
 
