@@ -420,9 +420,11 @@ __host__ __device__ constexpr int banked_lds_bytes(int r) { return r * (16 * 256
 
 __host__ __device__ constexpr int cmin(int a, int b) { return a < b ? a : b; }
 
-// Table-build inputs (c * x) each thread stages per round: 4 for one batch
-// row, 8 for several (the first round's loads are all in flight at once).
-__host__ __device__ constexpr int stage_items(int nb) { return nb == 1 ? 4 : 8; }
+// Table-build inputs (c * x) each thread stages per round (the first round's
+// loads are all in flight at once): with one batch row 4 (4 waves) or 2 (8
+// waves), so that one round covers an 8-chunk range; 8 for several rows.
+// Longer ranges stage in further rounds.
+__host__ __device__ constexpr int stage_items(int nb, int waves) { return nb == 1 ? (waves == 8 ? 2 : 4) : 8; }
 
 // Most chunks one workgroup may take for table width g, batch width nb and
 // eb-byte entries: its tables and inputs must fit the LDS budget.

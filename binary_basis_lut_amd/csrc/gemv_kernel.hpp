@@ -58,7 +58,7 @@ void lut_gemv_kernel(const GemvArgs a) {
   constexpr int WPL = kChunkCols / 32;     // words per lane per chunk (4)
   constexpr int EB = TQ ? 2 : 4;           // bytes per table entry
   constexpr int CTB = NB * SUB * TAB * EB; // table bytes of one chunk (all batch rows)
-  constexpr int VPT = stage_items(NB);
+  constexpr int VPT = stage_items(NB, WAVES);
   constexpr bool TWO = NB == 1;            // two add chains in the lookups of a single batch row
   static_assert(CTB % 256 == 0 && (G == 4 || CTB % 1024 == 0), "chunk table blocks must stay aligned");
   static_assert(PF >= 1 && PF <= 8, "prefetch depth");
