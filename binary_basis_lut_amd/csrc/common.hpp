@@ -28,7 +28,7 @@
 //     non-temporal 128-bit loads (streamed once, kept out of L2);
 //   * a workgroup of WAVES waves shares the tables of CPB consecutive chunks of
 //     the concatenated column space of all segments; a grid of
-//     row_blocks x splits workgroups covers the layer;
+//     row_blocks x splits workgroups (a 2D grid) covers the layer;
 //   * a workgroup's column range never leaves one segment, so its sign words
 //     are consecutive 1 KiB blocks and its partial sum takes one row scale;
 //   * splits > 1: each workgroup adds its fp32 partial of every row, as an
@@ -196,19 +196,20 @@ struct GemvArgs {
   int64_t k;              // input columns (x row stride)
   int64_t n_pad;          // row_tiles * 64
   int32_t kb, ks;
-  // Column ranges: every segment is cut into equal-as-possible ranges of
-  // consecutive chunks, rpg per global and rps per salient segment; split sp
-  // < kb * rpg is range sp % rpg of global segment sp / rpg, the rest follow
-  // the same rule over the salient segments.  No range is longer than cpb
-  // chunks (the dynamic LDS is sized for cpb).
-  int32_t rpg, rps;
-  int32_t cpb;
+  int32_t cpb;            // longest column range, in chunks (the dynamic LDS is sized for it)
   int32_t row_tiles;
-  int32_t row_blocks;
-  int32_t splits;         // kb * rpg + ks * rps
+  int32_t splits;         // column ranges (the grid's y dimension; x is the row block)
   int32_t batch;
   int32_t sal16;          // block-wise: 16 salient row-scale groups per chunk (8 columns each), else 8
+  // Column range of split sp, decoded on the host (range_word): segment in
+  // bits 0-2, chunk count in bits 3-8, first chunk in bits 9-31.  Every
+  // segment is cut into equal-as-possible ranges of consecutive chunks.
+  uint32_t range[kMaxSplits];
 };
+
+__host__ __device__ constexpr uint32_t range_word(int sg, int c_lo, int nch) {
+  return (uint32_t)sg | ((uint32_t)nch << 3) | ((uint32_t)c_lo << 9);
+}
 
 typedef void (*gemv_fn)(const GemvArgs);
 
@@ -437,25 +438,20 @@ __host__ __device__ constexpr int cpb_cap(int g, int nb, int eb) {
 // Chunks of weights in flight per wave for ranges of up to cpb chunks.
 __host__ __device__ constexpr int prefetch_depth(int cpb) { return cpb >= 4 ? 4 : 2; }
 
-// The column range of split sp: segment sg, chunks [c_lo, c_lo + nch) of it
-// (the balanced cut described at GemvArgs::rpg).
+// The column range of split sp (uniform): segment sg, chunks [c_lo, c_lo +
+// nch) of it, from the host-decoded table in the argument block.
 struct ColRange {
   SegRef S;
   int sg, c_lo, nch;
 };
 
 __device__ __forceinline__ ColRange column_range(const GemvArgs &a, int sp) {
-  const int gsp = a.kb * a.rpg;
-  const bool gpart = sp < gsp;
-  const int rel = gpart ? sp : sp - gsp;
-  const int nr = gpart ? a.rpg : a.rps;
-  const int sq = rel / nr;
-  const int rr = rel - sq * nr;
+  const uint32_t w = a.range[sp];
   ColRange c;
-  c.sg = (gpart ? 0 : a.kb) + sq;
+  c.sg = (int)(w & 7u);
+  c.nch = (int)((w >> 3) & 63u);
+  c.c_lo = (int)(w >> 9);
   c.S = gemv_segment(a.seg, a.kb, c.sg);
-  c.c_lo = (int)(((uint32_t)rr * (uint32_t)c.S.nchunks) / (uint32_t)nr);
-  c.nch = (int)(((uint32_t)(rr + 1) * (uint32_t)c.S.nchunks) / (uint32_t)nr) - c.c_lo;
   return c;
 }
 

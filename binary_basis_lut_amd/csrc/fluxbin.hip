@@ -63,6 +63,7 @@ struct Plan {
   int32_t splits;      // kb * rpg + ks * rps
   int32_t banked;      // g = 8 bank-private tables over ranges of this many chunks (2 or 4), else 0
   int32_t lds;         // dynamic LDS bytes of one workgroup
+  uint32_t range[kMaxSplits];  // range_word of every split: segment, first chunk, chunk count
   int64_t n_pad;
   size_t acc_bytes;    // workspace (splits > 1): packed reduction words
 };
@@ -199,6 +200,18 @@ fluxbin_status make_plan(const fluxbin_layer_desc *d, Plan *p) {
   // the longest range (balanced cut: ceil(chunks / ranges))
   p->cpb = (int32_t)std::max<int64_t>(cdiv(nc_g, p->rpg), d->ks > 0 ? cdiv(nc_s, p->rps) : 0);
   p->pf = prefetch_depth(p->cpb);
+  // split sp < kb * rpg is range sp % rpg of global segment sp / rpg, the rest
+  // follow the same rule over the salient segments; range rr of a segment of
+  // nc chunks is chunks [rr * nc / nr, (rr + 1) * nc / nr)
+  for (int32_t sp = 0; sp < p->splits; ++sp) {
+    const bool gpart = sp < d->kb * p->rpg;
+    const int32_t rel = gpart ? sp : sp - d->kb * p->rpg;
+    const int32_t nr = gpart ? p->rpg : p->rps;
+    const int32_t nc = gpart ? nc_g : nc_s;
+    const int32_t sg = (gpart ? 0 : d->kb) + rel / nr, rr = rel % nr;
+    const int32_t lo = (int32_t)((int64_t)rr * nc / nr), hi = (int32_t)((int64_t)(rr + 1) * nc / nr);
+    p->range[sp] = range_word(sg, lo, hi - lo);
+  }
   // banked tables: one region of 2 or 4 chunks holds every range (cpb_cap
   // keeps g = 8 fp32 ranges at <= 4 chunks)
   p->banked = bank_ok ? (p->cpb <= 2 ? 2 : 4) : 0;
@@ -856,15 +869,13 @@ fluxbin_status gemv_launch(fluxbin_handle h, const uint16_t *x, uint16_t *y, int
   a.n_pad = p.n_pad;
   a.kb = d.kb;
   a.ks = d.ks;
-  a.rpg = p.rpg;
-  a.rps = p.rps;
   a.cpb = p.cpb;
   a.row_tiles = p.row_tiles;
-  a.row_blocks = p.row_blocks;
   a.splits = p.splits;
   a.sal16 = d.row_group && d.ks > 0 && d.sal_group == 8 ? 1 : 0;
+  memcpy(a.range, p.range, sizeof(uint32_t) * (size_t)p.splits);
   uint64_t *acc = p.splits > 1 ? words : nullptr;
-  const int64_t grid = (int64_t)p.row_blocks * p.splits;
+  const dim3 grid((unsigned)p.row_blocks, (unsigned)p.splits);  // x: row block, y: column range
   // one launch per group of p.nb batch rows (a prefill batch runs as several groups,
   // each building its own tables and streaming the weights again)
   for (int64_t b0 = 0; b0 < batch; b0 += p.nb) {
@@ -874,12 +885,12 @@ fluxbin_status gemv_launch(fluxbin_handle h, const uint16_t *x, uint16_t *y, int
     a.acc = acc ? acc + b0 * p.n_pad : nullptr;
     if (start_event || stop_event) {
       void *args[] = {&a};
-      hipError_t e = hipExtLaunchKernel(reinterpret_cast<const void *>(h->fn), dim3((unsigned)grid),
+      hipError_t e = hipExtLaunchKernel(reinterpret_cast<const void *>(h->fn), grid,
                                         dim3(p.waves * 64), args, h->lds, (hipStream_t)stream,
                                         b0 == 0 ? start_event : nullptr, b0 + p.nb >= batch ? stop_event : nullptr, 0);
       if (e != hipSuccess) return hip_fail(e, "gemv launch");
     } else {
-      hipLaunchKernelGGL(h->fn, dim3((unsigned)grid), dim3(p.waves * 64), h->lds, (hipStream_t)stream, a);
+      hipLaunchKernelGGL(h->fn, grid, dim3(p.waves * 64), h->lds, (hipStream_t)stream, a);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "gemv launch");

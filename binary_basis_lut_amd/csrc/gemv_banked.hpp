@@ -109,8 +109,8 @@ void lut_gemv_g8_banked_kernel(const GemvArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int rb = blockIdx.x % a.row_blocks;
-  const int sp = blockIdx.x / a.row_blocks;
+  const int rb = blockIdx.x;  // row block
+  const int sp = blockIdx.y;  // column range
   const int tile = rb * WAVES + wave;
 
   // lane roles: r = row within a group of 16 (and the rotation of the lane's

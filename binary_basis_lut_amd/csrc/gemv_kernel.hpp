@@ -74,8 +74,8 @@ void lut_gemv_kernel(const GemvArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar address arithmetic
-  const int rb = blockIdx.x % a.row_blocks;
-  const int sp = blockIdx.x / a.row_blocks;
+  const int rb = blockIdx.x;  // row block
+  const int sp = blockIdx.y;  // column range
   const int tile = rb * WAVES + wave;
   const int ltile = min(tile, a.row_tiles - 1);  // waves past the last tile read the last one, store nothing
   const int row = tile * kTileRows + lane;
