@@ -196,7 +196,8 @@ struct GemvArgs {
   int64_t k;              // input columns (x row stride)
   int64_t n_pad;          // row_tiles * 64
   int32_t kb, ks;
-  int32_t cpb;            // longest column range, in chunks (the dynamic LDS is sized for it)
+  int32_t cpb;            // longest column range, in chunks
+  int32_t tb;             // chunks whose tables the dynamic LDS holds (>= cpb: the whole range at once)
   int32_t row_tiles;
   int32_t splits;         // column ranges (the grid's y dimension; x is the row block)
   int32_t batch;

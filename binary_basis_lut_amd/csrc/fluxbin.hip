@@ -54,7 +54,9 @@ constexpr int kTargetBlocks = 1024;  // about four workgroups per CU
 struct Plan {
   int32_t waves;       // waves per workgroup (64 rows each)
   int32_t nb;          // compiled batch width = batch rows per group (see batch_group)
-  int32_t cpb;         // most chunks in one column range (LDS is sized for it)
+  int32_t cpb;         // most chunks in one column range
+  int32_t tb;          // chunks whose tables LDS holds at once (LDS is sized for it): cpb, or for
+                       // several batch rows a multiple of pf below cpb (tables built in groups)
   int32_t pf;          // chunks of weights in flight per wave (2 or 4)
   int32_t row_tiles;
   int32_t row_blocks;
@@ -125,8 +127,12 @@ fluxbin_status validate_shape(const fluxbin_layer_desc *d) {
 
 // Target chunks per column range: about kTargetBlocks workgroups' worth of
 // work in all, a workgroup of nb batch rows counting nb times, at least 2, a
-// power of two, at most 8, and at most 4 for several batch rows, within the
-// LDS budget (cmax).  Every segment is then cut into ceil(chunks / target)
+// power of two, at most 8, and at most 4 for several batch rows, within cmax:
+// the LDS budget, or for several batch rows at g = 4 the grouped-table limit
+// (8 rows: 4-chunk ranges whose tables are built two chunks at a time, 24.3 /
+// 25.0 us on the 4096 -> 11008 / 11008 -> 4096 projections against 30.4 / 32.7
+// with 3-chunk ranges held whole; at g = 8 with 2 rows grouping lost, qkv
+// 22.5 -> 24.3 us).  Every segment is then cut into ceil(chunks / target)
 // ranges of equal length (within one chunk).  Measured on MI355X (graph of
 // distinct resident weight sets, 8 / 4 waves): the 70B gate+up projection
 // (8192 -> 57344, 8 waves) ran 31.2 / 29.1 / 27.2 / 28.8 / 31.5 us with 5 / 7 /
@@ -157,7 +163,7 @@ int32_t banked_cpb(const fluxbin_layer_desc *d) {
 // power of two of max_batch, at most 16 (g = 4) or 4 (g = 8); wider batches
 // run as several groups.
 int32_t batch_group(int32_t g, int64_t max_batch) {
-  const int64_t cap = g == 4 ? 16 : 4;
+  const int64_t cap = g == 4 ? 8 : 4;
   return pow2_at_least(max_batch < cap ? max_batch : cap);
 }
 
@@ -178,20 +184,24 @@ fluxbin_status make_plan(const fluxbin_layer_desc *d, Plan *p) {
     p->waves = (d->g == 8 || p->row_tiles >= 512) ? 8 : 4;
   }
   const int32_t cmax = cpb_cap(d->g, p->nb, entry_bytes(d));
-  if (d->chunks_per_block > cmax)
+  // several batch rows build their tables in groups of chunks, so their ranges
+  // may exceed what LDS holds at once (given room for two chunks)
+  const bool grouped_ok = p->nb > 1 && cmax >= 2;
+  if (d->chunks_per_block > (grouped_ok ? kMaxCpb : cmax))
     return fail(FLUXBIN_ERR_UNSUPPORTED, "chunks_per_block = %d exceeds %d for g = %d, max_batch = %lld, %d waves",
-                d->chunks_per_block, cmax, d->g, (long long)d->max_batch, p->waves);
+                d->chunks_per_block, grouped_ok ? kMaxCpb : cmax, d->g, (long long)d->max_batch, p->waves);
   // g = 8, one batch row, per-row scales, fp32 entries: bank-private tables
   const bool bank_ok = d->g == 8 && p->nb == 1 && !d->row_group && entry_bytes(d) == 4;
   int32_t target = d->chunks_per_block ? d->chunks_per_block
                    : bank_ok           ? banked_cpb(d)
-                                       : auto_cpb(p->nb, cmax, p->waves, p->row_tiles, p->total_chunks);
+                                       : auto_cpb(p->nb, grouped_ok && d->g == 4 ? kMaxCpb : cmax, p->waves, p->row_tiles,
+                                              p->total_chunks);
   const int32_t nc_g = (int32_t)cdiv(d->k, kChunkCols), nc_s = d->ks > 0 ? (int32_t)cdiv(d->s, kChunkCols) : 0;
   for (;;) {
     p->rpg = (int32_t)cdiv(nc_g, target);
     p->rps = d->ks > 0 ? (int32_t)cdiv(nc_s, target) : 0;
     p->splits = d->kb * p->rpg + d->ks * p->rps;
-    if (p->splits <= kMaxSplits || d->chunks_per_block || target >= cmax) break;
+    if (p->splits <= kMaxSplits || d->chunks_per_block || target >= (grouped_ok ? kMaxCpb : cmax)) break;
     ++target;  // automatic plan: longer ranges until the splits fit the reduction word
   }
   if (p->splits > kMaxSplits)
@@ -200,6 +210,11 @@ fluxbin_status make_plan(const fluxbin_layer_desc *d, Plan *p) {
   // the longest range (balanced cut: ceil(chunks / ranges))
   p->cpb = (int32_t)std::max<int64_t>(cdiv(nc_g, p->rpg), d->ks > 0 ? cdiv(nc_s, p->rps) : 0);
   p->pf = prefetch_depth(p->cpb);
+  p->tb = p->cpb;
+  if (p->cpb > cmax) {  // grouped tables: groups of tb chunks, tb a multiple of the prefetch depth
+    p->pf = cmax >= 4 ? 4 : 2;
+    p->tb = cmax - cmax % p->pf;
+  }
   // split sp < kb * rpg is range sp % rpg of global segment sp / rpg, the rest
   // follow the same rule over the salient segments; range rr of a segment of
   // nc chunks is chunks [rr * nc / nr, (rr + 1) * nc / nr)
@@ -216,7 +231,7 @@ fluxbin_status make_plan(const fluxbin_layer_desc *d, Plan *p) {
   // keeps g = 8 fp32 ranges at <= 4 chunks)
   p->banked = bank_ok ? (p->cpb <= 2 ? 2 : 4) : 0;
   p->row_blocks = (int32_t)cdiv(p->row_tiles, p->waves);
-  p->lds = p->banked ? banked_lds_bytes(p->banked) : lds_bytes(d->g, p->nb, p->cpb, entry_bytes(d));
+  p->lds = p->banked ? banked_lds_bytes(p->banked) : lds_bytes(d->g, p->nb, p->tb, entry_bytes(d));
   p->acc_bytes = p->splits > 1 ? (size_t)d->max_batch * p->n_pad * sizeof(uint64_t) : 0;
   return FLUXBIN_OK;
 }
@@ -787,6 +802,7 @@ void fill_plan(const fluxbin_layer_desc &d, const Plan &p, fluxbin_plan *plan) {
   plan->lds_bytes = p.lds;
   plan->grid = (int64_t)p.row_blocks * p.splits;
   plan->banked_tables = p.banked;
+  plan->table_chunks = p.tb;
 }
 
 }  // namespace
@@ -870,6 +886,7 @@ fluxbin_status gemv_launch(fluxbin_handle h, const uint16_t *x, uint16_t *y, int
   a.kb = d.kb;
   a.ks = d.ks;
   a.cpb = p.cpb;
+  a.tb = p.tb;
   a.row_tiles = p.row_tiles;
   a.splits = p.splits;
   a.sal16 = d.row_group && d.ks > 0 && d.sal_group == 8 ? 1 : 0;

@@ -65,11 +65,11 @@ void lut_gemv_kernel(const GemvArgs a) {
   static_assert(kChunkCols % 64 == 0 && NT % 64 == 0, "a wave's staged items must share chunk and batch row");
   extern __shared__ __align__(1024) float smem[];
 
-  const int cpb = a.cpb;
+  const int tbc = a.tb;  // chunks whose tables the LDS holds at once
   float *s_tab = smem;
   const uint32_t tab_base = lds_addr(s_tab);  // 1024-aligned (table addresses are merged bytewise)
-  float *s_v = smem + cpb * (CTB / 4);
-  float *s_sink = s_v + cpb * NB * kChunkCols;
+  float *s_v = smem + tbc * (CTB / 4);
+  float *s_sink = s_v + tbc * NB * kChunkCols;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -126,13 +126,20 @@ void lut_gemv_kernel(const GemvArgs a) {
       for (int u = 0; u < D; ++u) load_into(u);
     };
 
-    // Staged items (chunk, batch row, column) of the range: item e is handled
+    // Table groups: the tables of chunks [g0, g0 + gn) of the range are in LDS
+    // at a time.  One batch row: the whole range (the host sizes the LDS for
+    // it).  Several batch rows, whose tables are NB times larger: groups of
+    // a.tb chunks, a multiple of D, built in turn while the weight slots keep
+    // streaming, so that a range need not fit the LDS (fewer, longer ranges).
+    int g0 = 0;
+    int gn = min(nch, tbc);
+    // Staged items (chunk, batch row, column) of the group: item e is handled
     // by thread e % NT, VPT per thread per round (the first round's loads go
-    // out before the weights, longer ranges take further rounds after them);
+    // out before the weights, longer groups take further rounds after them);
     // a wave's 64 items share chunk and batch row.  Every item slot loads
-    // (slots past the range re-read a live item's inputs and store them to the
+    // (slots past the group re-read a live item's inputs and store them to the
     // sink).
-    const int items = nch * NB * kChunkCols;
+    int items = gn * NB * kChunkCols;
     bool live[VPT];
     const FB_GLOBAL uint16_t *xrow[VPT];
     uint32_t ccl[VPT], gi[VPT];
@@ -145,7 +152,7 @@ void lut_gemv_kernel(const GemvArgs a) {
         const int ch = eb / (NB * kChunkCols);
         const int b = (eb / kChunkCols) % NB;
         const bool brow = b < a.batch;  // uniform; batch rows past `batch` do not exist
-        const uint32_t cc = (uint32_t)((c_lo + ch) * kChunkCols + (eb & (kChunkCols - 1)) + lane);
+        const uint32_t cc = (uint32_t)((c_lo + g0 + ch) * kChunkCols + (eb & (kChunkCols - 1)) + lane);
         live[i] = (e0 < items) & brow & (cc < (uint32_t)S.len);  // non-short-circuit: selects, not branches
         ccl[i] = live[i] ? cc : 0u;
         xrow[i] = ux + (int64_t)(brow ? b : 0) * a.k;
@@ -186,13 +193,16 @@ void lut_gemv_kernel(const GemvArgs a) {
       __builtin_amdgcn_sched_barrier(0);
       load_x();
     }
+    auto stage_rounds = [&]() {  // the group's further rounds (long groups only)
+      for (int base = VPT * NT; base < items; base += VPT * NT) {  // uniform
+        prep(base);
+        if constexpr (SAL) load_idx();
+        load_x();
+        stage(base);
+      }
+    };
     stage(0);
-    for (int base = VPT * NT; base < items; base += VPT * NT) {  // uniform; long ranges only
-      prep(base);
-      if constexpr (SAL) load_idx();
-      load_x();
-      stage(base);
-    }
+    stage_rounds();
     __syncthreads();
 
     // Tables.  Entry p of a sub-vector is the sum, in this order, of
@@ -202,9 +212,9 @@ void lut_gemv_kernel(const GemvArgs a) {
     // entries round exactly like that sequence; the half with the top bit
     // clear is built from -v_{G-1} and is therefore the exact negation of
     // the other half (LUT[~p] = -LUT[p]).  The g = 8 unit is g8_unit_entries.
-    {
+    auto build_tables = [&]() {
       constexpr int UPS = G == 4 ? 2 : 16;  // build units per sub-vector
-      const int units = nch * NB * SUB * UPS;
+      const int units = gn * NB * SUB * UPS;
       for (int t = tid; t < units; t += NT) {
         const int sv = t / UPS;  // (chunk * NB + batch row) * SUB + sub-vector
         const int un = t - sv * UPS;
@@ -245,7 +255,8 @@ void lut_gemv_kernel(const GemvArgs a) {
           }
         }
       }
-    }
+    };
+    build_tables();
     __syncthreads();
 
     // Lookups, chunk by chunk, with D chunks of weights in flight: once a
@@ -299,20 +310,57 @@ void lut_gemv_kernel(const GemvArgs a) {
       // the next chunk's table reads stay behind this chunk's (registers)
       asm volatile("" ::: "memory");
     };
-    int ch0 = 0;
-    for (; ch0 + D < nch; ch0 += D) {
+    if constexpr (NB == 1) {
+      // one group: every chunk's tables are in LDS
+      int ch0 = 0;
+      for (; ch0 + D < nch; ch0 += D) {
 #pragma unroll
-      for (int u = 0; u < D; ++u) {
-        // consumed before the refill is issued into the same registers: with
-        // both alive the compiler would rotate registers with copies that wait
-        consume(wb[u], ch0 + u, u);
-        load_into(u);
-        __builtin_amdgcn_sched_barrier(0);  // issue the refill here, not later
+        for (int u = 0; u < D; ++u) {
+          // consumed before the refill is issued into the same registers: with
+          // both alive the compiler would rotate registers with copies that wait
+          consume(wb[u], ch0 + u, u);
+          load_into(u);
+          __builtin_amdgcn_sched_barrier(0);  // issue the refill here, not later
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < D; ++u)
+        if (ch0 + u < nch) consume(wb[u], ch0 + u, u);
+    } else {
+      for (;;) {  // uniform
+        // group [g0, g0 + gn): g0 and, but for the last group, gn are multiples
+        // of D, so chunk ch0 + u is in slot u; the loop is the one-group loop
+        // above with the group's end as a second bound
+        const int gend = g0 + gn;
+        int ch0 = g0;
+        for (; ch0 + D <= gend && ch0 + D < nch; ch0 += D) {
+#pragma unroll
+          for (int u = 0; u < D; ++u) {
+            consume(wb[u], ch0 + u - g0, u);
+            load_into(u);  // the chunk D ahead, across groups
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+        if (gend >= nch) {
+#pragma unroll
+          for (int u = 0; u < D; ++u)
+            if (ch0 + u < nch) consume(wb[u], ch0 + u - g0, u);
+          break;
+        }
+        g0 = gend;
+        gn = min(tbc, nch - g0);
+        items = gn * NB * kChunkCols;
+        __syncthreads();  // every wave is done with the group's tables
+        prep(0);
+        if constexpr (SAL) load_idx();
+        load_x();
+        stage(0);
+        stage_rounds();
+        __syncthreads();
+        build_tables();
+        __syncthreads();
       }
     }
-#pragma unroll
-    for (int u = 0; u < D; ++u)
-      if (ch0 + u < nch) consume(wb[u], ch0 + u, u);
     if constexpr (RS == 0) {
       // the row scale, once, after the range's accumulation
       const float rv = h2f(rr16);
@@ -352,10 +400,7 @@ gemv_fn gemv_pick(int nb, int waves, int pf) {
     case 4: return gemv_pick_waves<G, 4, RS, TQ>(waves, pf);
   }
   if constexpr (G == 4) {
-    switch (nb) {
-      case 8: return gemv_pick_waves<G, 8, RS, TQ>(waves, pf);
-      case 16: return gemv_pick_waves<G, 16, RS, TQ>(waves, pf);
-    }
+    if (nb == 8) return gemv_pick_waves<G, 8, RS, TQ>(waves, pf);
   }
   return nullptr;
 }

@@ -20,7 +20,7 @@ if not LIB_PATH.exists():
 
 _lib = ctypes.CDLL(str(LIB_PATH))
 
-ABI_VERSION = 6
+ABI_VERSION = 7
 
 OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
 LAYOUT_ROWMAJOR, LAYOUT_TILED = 0, 1
@@ -47,7 +47,7 @@ class LayerDesc(ctypes.Structure):
 class PlanInfo(ctypes.Structure):
     _fields_ = [
         ("rows_per_block", I32), ("chunks_per_block", I32), ("row_blocks", I32), ("splits", I32),
-        ("total_chunks", I32), ("lds_bytes", I32), ("grid", I64), ("banked_tables", I32),
+        ("total_chunks", I32), ("lds_bytes", I32), ("grid", I64), ("banked_tables", I32), ("table_chunks", I32),
     ]
 
     def as_dict(self):

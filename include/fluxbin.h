@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define FLUXBIN_ABI_VERSION 6
+#define FLUXBIN_ABI_VERSION 7
 
 typedef enum {
   FLUXBIN_OK = 0,
@@ -131,9 +131,9 @@ typedef struct {
   size_t workspace_bytes;
   int32_t chunks_per_block;    /* tuning: 0 = automatic, else 1..32: the longest column range of one
                                   workgroup, in 128-column chunks (each segment is cut into equal ranges no
-                                  longer than this); the limit for a given g, batch width and
-                                  waves_per_block follows from 80 KiB of tables per workgroup and the table
-                                  inputs one thread stages (FLUXBIN_ERR_UNSUPPORTED beyond it) */
+                                  longer than this).  With one batch row the range's tables must fit 80 KiB
+                                  of LDS (FLUXBIN_ERR_UNSUPPORTED beyond it); with several, ranges longer
+                                  than that build their tables in groups (table_chunks of the plan) */
   int32_t waves_per_block;     /* tuning: 0 = automatic, else 4 or 8 (64 output rows per wave) */
   int32_t row_group;           /* row-scale format.  0: one scale per row per basis, r_global fp16 [kb][n],
                                   r_sal fp16 [ks][n].  128: block-wise, one scale per row per basis per group
@@ -170,6 +170,9 @@ typedef struct {
   int32_t banked_tables;    /* 0: each sub-vector's table in consecutive dwords, one row per lane; 2 or 4
                                (g = 8, one batch row, per-row scales, fp32 entries): bank-private tables,
                                each a column of the LDS, over column ranges of up to that many chunks */
+  int32_t table_chunks;     /* chunks whose tables a workgroup holds in LDS at once: chunks_per_block, or
+                               with several batch rows fewer, the tables then built in groups of this many
+                               chunks in turn while the range's sign words stream */
 } fluxbin_plan;
 
 int32_t fluxbin_abi_version(void);

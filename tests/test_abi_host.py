@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported(fb):
 
 
 def test_abi_version_and_strings(fb):
-    assert fb.fluxbin_abi_version() == fb.ABI_VERSION == 6
+    assert fb.fluxbin_abi_version() == fb.ABI_VERSION == 7
     assert fb.fluxbin_status_string(fb.OK) == "ok"
     assert "invalid" in fb.fluxbin_status_string(fb.ERR_INVALID_ARGUMENT)
     assert fb.fluxbin_status_string(99) == "unknown status"
@@ -108,7 +108,18 @@ def test_g8_batch_limit_and_salient_flags(fb):
     assert st == fb.OK and ws == 128 * 4096 * 8
     assert ws_status(fb, good_desc(fb, ks=0, s=0))[0] == fb.OK
     assert ws_status(fb, good_desc(fb, ks=0, s=8))[0] == fb.ERR_INVALID_ARGUMENT
-    assert ws_status(fb, good_desc(fb, chunks_per_block=8, max_batch=8))[0] == fb.ERR_UNSUPPORTED
+    # several batch rows: ranges longer than the LDS holds build their tables in groups of chunks
+    # (8 rows at g = 4: 20.5 KiB per chunk, groups of 2) ...
+    assert ws_status(fb, good_desc(fb, chunks_per_block=8, max_batch=8))[0] == fb.OK
+    p = plan_of(fb, good_desc(fb, chunks_per_block=8, max_batch=8))
+    assert (p["chunks_per_block"], p["table_chunks"]) == (8, 2) and p["lds_bytes"] == 2 * (8 * 32 * 16 * 4 + 8 * 128 * 4) + 256
+    # 16 rows run as two groups of 8 at g = 4 ...
+    p = plan_of(fb, good_desc(fb, chunks_per_block=8, max_batch=16))
+    assert (p["chunks_per_block"], p["table_chunks"]) == (8, 2)
+    # ... but a g = 8 group of 4 rows: the LDS holds one chunk's tables, too few to group
+    assert ws_status(fb, good_desc(fb, g=8, chunks_per_block=2, max_batch=4))[0] == fb.ERR_UNSUPPORTED
+    # one batch row: the range's tables must fit
+    assert ws_status(fb, good_desc(fb, chunks_per_block=32, waves_per_block=8))[0] == fb.ERR_UNSUPPORTED
 
 
 def plan_of(fb, d):

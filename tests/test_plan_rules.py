@@ -90,8 +90,13 @@ def test_g8_layers_take_eight_waves_within_the_lds_budget(fb):
     # fp16 entries halve the tables (and keep the one-table-per-sub-vector layout)
     p = plan(fb, workload_desc(fb, 3, 2, table_precision=fb.TABLE_F16, chunks_per_block=4))
     assert p["lds_bytes"] == 4 * (16 * 256 * 2 + 128 * 4) + 256 and p["banked_tables"] == 0
-    # the natural layout's own rule for a batched g = 8 layer
-    assert plan(fb, workload_desc(fb, 3, 2, max_batch=2))["chunks_per_block"] == 2
+    # a batched g = 8 layer keeps the one-table-per-sub-vector layout, its ranges held whole (two rows
+    # of tables for two chunks fill the LDS)
+    p = plan(fb, workload_desc(fb, 3, 2, max_batch=2))
+    assert (p["chunks_per_block"], p["table_chunks"]) == (2, 2)
+    # g = 4 with 8 rows: 4-chunk ranges, tables built two chunks at a time
+    p = plan(fb, workload_desc(fb, 4, 0, max_batch=8))
+    assert (p["chunks_per_block"], p["table_chunks"]) == (4, 2)
     # so do batched and block-wise g = 8 layers, and every g = 4 layer
     assert plan(fb, workload_desc(fb, 3, 2, max_batch=2))["banked_tables"] == 0
     assert plan(fb, blockwise_desc(fb, 4096, 4096, g=8))["banked_tables"] == 0
