@@ -42,7 +42,7 @@
  *     thread-local message.  Device faults surface at the caller's next
  *     synchronisation.  No C++ exception crosses this boundary.
  *   - fluxbin_build_lut and fluxbin_reset_workspace launch one kernel and
- *     fluxbin_gemv one kernel per group of batch rows (16 at g = 4, 4 at
+ *     fluxbin_gemv one kernel per group of batch rows (8 at g = 4, 4 at
  *     g = 8; one launch up to that batch); none of them ever allocates,
  *     copies, sets memory or synchronises, so they may be captured in a HIP
  *     graph.  fluxbin_create does synchronise.
@@ -112,7 +112,7 @@ typedef struct {
   int64_t n;             /* output rows, >= 1 */
   int64_t k;             /* input columns, >= 1 */
   int64_t s;             /* salient columns |S|: 0 when ks == 0, else 1..k */
-  int64_t max_batch;     /* largest batch a call may pass: 1..128.  A workgroup serves up to 16 batch
+  int64_t max_batch;     /* largest batch a call may pass: 1..128.  A workgroup serves up to 8 batch
                             rows (g = 8: 4); wider batches run as groups of that many rows, each
                             building its own tables and streaming the weights again */
   const uint32_t *bits_global; /* kb blocks of sign words in `layout`: TILED, fluxbin_tiled_words(n, k)
