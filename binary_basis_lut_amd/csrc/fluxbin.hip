@@ -125,8 +125,10 @@ fluxbin_status validate_shape(const fluxbin_layer_desc *d) {
   return FLUXBIN_OK;
 }
 
-// Target chunks per column range: about kTargetBlocks workgroups' worth of
-// work in all, a workgroup of nb batch rows counting nb times, at least 2, a
+// Target chunks per column range: about target_blocks workgroups' worth of
+// work in all (kTargetBlocks; half as many, of 8 waves, for the very wide
+// single-row layers, so that the 70B down projection keeps 8-chunk ranges at 8
+// waves), a workgroup of nb batch rows counting nb times, at least 2, a
 // power of two, at most 8, and at most 4 for several batch rows, within cmax:
 // the LDS budget, or for several batch rows at g = 4 the grouped-table limit
 // (8 rows: 4-chunk ranges whose tables are built two chunks at a time, 24.3 /
@@ -140,8 +142,8 @@ fluxbin_status validate_shape(const fluxbin_layer_desc *d) {
 // 17.1 / 16.3 / 20.9 us with 4 / 8 / 16; the qkv projection 10.0 / 8.8 /
 // 10.4 us with 2 / 4 / 8; the 4096 -> 11008 projection at 4 batch rows 15.2
 // us with 4 chunks, 18.0 with 7.
-int32_t auto_cpb(int32_t nb, int32_t cmax, int32_t waves, int64_t row_tiles, int32_t total_chunks) {
-  int64_t c = (int64_t)row_tiles * total_chunks * nb / ((int64_t)waves * kTargetBlocks);
+int32_t auto_cpb(int32_t nb, int32_t cmax, int32_t waves, int64_t row_tiles, int32_t total_chunks, int32_t target_blocks) {
+  int64_t c = (int64_t)row_tiles * total_chunks * nb / ((int64_t)waves * target_blocks);
   c = std::min<int64_t>(std::max<int64_t>(c, 2), nb > 1 ? 4 : 8);
   int64_t p = 1;
   while (p * 2 <= c) p *= 2;
@@ -174,14 +176,21 @@ fluxbin_status make_plan(const fluxbin_layer_desc *d, Plan *p) {
   p->n_pad = (int64_t)p->row_tiles * kTileRows;
   p->total_chunks = (int32_t)(d->kb * cdiv(d->k, kChunkCols) + d->ks * cdiv(d->s, kChunkCols));
   p->nb = batch_group(d->g, d->max_batch);
+  // one batch row at g = 4, per-row scales, over very many chunks (the 70B
+  // down projection; its block-wise form is slower at 8 waves: 21.2 against
+  // 20.3 us)
+  const bool wide = d->g == 4 && p->nb == 1 && !d->row_group && p->total_chunks >= 256;
   if (d->waves_per_block) {
     p->waves = d->waves_per_block;
   } else {
     // eight waves (512 rows) halve the per-row share of the table build: for
-    // the large g = 8 tables and for very tall layers (the 70B gate+up
-    // projection, 896 row tiles: 27.2 us with 8 waves, 29.9 with 4); the 70B
-    // down, qkv and o shapes (128 - 160 row tiles) are faster with 4
-    p->waves = (d->g == 8 || p->row_tiles >= 512) ? 8 : 4;
+    // the large g = 8 tables, for very tall layers (the 70B gate+up
+    // projection, 896 row tiles: 27.2 us with 8 waves, 29.9 with 4) and, at
+    // g = 4 with one batch row and per-row scales, for very wide ones (the
+    // 70B down projection, 455 chunks: 15.5-15.8 us with 8 waves and 8-chunk
+    // ranges, 15.9-16.0 with 4); the 70B qkv and o shapes (130 chunks, 128 -
+    // 160 row tiles) are faster with 4 (qkv 8.74 against 8.91 us)
+    p->waves = (d->g == 8 || p->row_tiles >= 512 || wide) ? 8 : 4;
   }
   const int32_t cmax = cpb_cap(d->g, p->nb, entry_bytes(d));
   // several batch rows build their tables in groups of chunks, so their ranges
@@ -195,7 +204,7 @@ fluxbin_status make_plan(const fluxbin_layer_desc *d, Plan *p) {
   int32_t target = d->chunks_per_block ? d->chunks_per_block
                    : bank_ok           ? banked_cpb(d)
                                        : auto_cpb(p->nb, grouped_ok && d->g == 4 ? kMaxCpb : cmax, p->waves, p->row_tiles,
-                                              p->total_chunks);
+                                              p->total_chunks, wide ? kTargetBlocks / 2 : kTargetBlocks);
   const int32_t nc_g = (int32_t)cdiv(d->k, kChunkCols), nc_s = d->ks > 0 ? (int32_t)cdiv(d->s, kChunkCols) : 0;
   for (;;) {
     p->rpg = (int32_t)cdiv(nc_g, target);
@@ -209,7 +218,12 @@ fluxbin_status make_plan(const fluxbin_layer_desc *d, Plan *p) {
                 p->splits, kMaxSplits, target);
   // the longest range (balanced cut: ceil(chunks / ranges))
   p->cpb = (int32_t)std::max<int64_t>(cdiv(nc_g, p->rpg), d->ks > 0 ? cdiv(nc_s, p->rps) : 0);
-  p->pf = prefetch_depth(p->cpb);
+  // two chunks in flight per wave at g = 4 with one batch row, whatever the
+  // range length: with 8 waves per SIMD the HBM serves fewer, earlier requests
+  // better (70B gate+up 26.3 against 27.6 us with four, down at 8 waves 15.5-15.8
+  // against 16.4-16.7, qkv and o at 4 waves 8.74 / 7.86 against 8.84 / 7.91,
+  // the block-wise gate+up 32.5 against 33.2; interleaved on one MI355X)
+  p->pf = d->g == 4 && p->nb == 1 ? 2 : prefetch_depth(p->cpb);
   p->tb = p->cpb;
   if (p->cpb > cmax) {  // grouped tables: groups of tb chunks, tb a multiple of the prefetch depth
     p->pf = cmax >= 4 ? 4 : 2;

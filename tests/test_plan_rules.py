@@ -63,12 +63,15 @@ def test_tall_layer_takes_eight_waves_and_eight_chunk_ranges(fb):
     assert p["rows_per_block"] == 512 and p["chunks_per_block"] == 8
 
 
-def test_wide_layers_keep_four_waves(fb):
-    # 70B down 28672 -> 8192: 128 row tiles x 455 chunks: 4 waves, 8-chunk ranges (224 global
-    # chunks per basis in 28 ranges, the 7 salient chunks in one)
+def test_very_wide_single_row_layers_take_eight_waves(fb):
+    # 70B down 28672 -> 8192: 128 row tiles x 455 chunks, one batch row, per-row scales: 8 waves,
+    # 8-chunk ranges (224 global chunks per basis in 28 ranges, the 7 salient chunks in one),
+    # 16 row blocks x 57 ranges
     p = plan(fb, workload_desc(fb, 5, 3))
-    assert (p["rows_per_block"], p["chunks_per_block"], p["splits"]) == (256, 8, 57)
+    assert (p["rows_per_block"], p["chunks_per_block"], p["splits"], p["grid"]) == (512, 8, 57, 912)
+    # its block-wise form, and several batch rows, keep 4 waves
     assert plan(fb, blockwise_desc(fb, 8192, 28672))["rows_per_block"] == 256
+    assert plan(fb, workload_desc(fb, 5, 3, max_batch=2))["rows_per_block"] == 256
     # qkv and o (160 / 128 row tiles x 130 chunks) stay at 4 waves
     for shape in (0, 1):
         p = plan(fb, workload_desc(fb, 5, shape))
