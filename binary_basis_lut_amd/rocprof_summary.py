@@ -8,6 +8,11 @@ folders of the rocprofv3 runs each summary names:
       run: calls and average / min / max duration per kernel, as a markdown
       table;
 
+  python3 -m binary_basis_lut_amd.rocprof_summary trace DIR --by-grid
+      the same from the dispatch trace, one row per kernel and grid (so
+      that launches of one instance on different layer shapes stay apart),
+      with the median besides the average;
+
   python3 -m binary_basis_lut_amd.rocprof_summary pmc DIR --kernel REGEX
       the counters of a `--pmc ... --output-format csv` run for the dispatches
       of the kernels matching REGEX: each dispatch's value summed over the
@@ -83,7 +88,25 @@ def pmc_medians(d: str, kernel: str) -> tuple[dict, int, str]:
     return med, len(per), name
 
 
+def trace_by_grid(d: str):
+    """Dispatch durations of the kernel trace grouped by (kernel, grid, workgroup size)."""
+    groups = defaultdict(list)
+    with open(_one(d, "kernel_trace.csv")) as f:
+        for r in csv.DictReader(f):
+            key = (r["Kernel_Name"], int(r["Grid_Size_X"]), int(r["Grid_Size_Y"]), int(r["Workgroup_Size_X"]))
+            groups[key].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    return [(k, len(v), statistics.mean(v), statistics.median(v), min(v), max(v)) for k, v in groups.items()]
+
+
 def cmd_trace(a) -> None:
+    if a.by_grid:
+        print("| kernel | grid (workgroups) | calls | average ns | median ns | min ns | max ns |")
+        print("|---|---|---|---|---|---|---|")
+        for (name, gx, gy, wg), calls, avg, med, mn, mx in sorted(trace_by_grid(a.dir)):
+            if a.kernel and not re.search(a.kernel, name):
+                continue
+            print(f"| {name} | {gx // wg} x {gy} | {calls} | {avg:.0f} | {med:.0f} | {mn} | {mx} |")
+        return
     print("| kernel | calls | average ns | min ns | max ns |")
     print("|---|---|---|---|---|")
     for name, calls, avg, mn, mx in trace_rows(a.dir):
@@ -147,6 +170,7 @@ def main() -> int:
     t = sub.add_parser("trace")
     t.add_argument("dir")
     t.add_argument("--kernel", default="")
+    t.add_argument("--by-grid", action="store_true", help="one row per (kernel, grid) from the dispatch trace")
     p = sub.add_parser("pmc")
     p.add_argument("dir")
     p.add_argument("--kernel", required=True)

@@ -60,3 +60,23 @@ def test_trace_table_lists_the_kernels(tmp_path):
         '"copyBuffer",2,100,50.0,50.0,50,50,0.0\n')
     rows = RS.trace_rows(str(d))
     assert rows[0][1:] == (4, 25.0, 20.0, 30.0) and rows[1][0] == "copyBuffer"
+
+
+def test_trace_by_grid_keeps_the_shapes_apart(tmp_path, capsys, monkeypatch):
+    d = tmp_path / "g"
+    d.mkdir()
+    hdr = ('"Kind","Agent_Id","Queue_Id","Stream_Id","Thread_Id","Dispatch_Id","Kernel_Id","Kernel_Name",'
+           '"Correlation_Id","Start_Timestamp","End_Timestamp","LDS_Block_Size","Scratch_Size","VGPR_Count",'
+           '"Accum_VGPR_Count","SGPR_Count","Workgroup_Size_X","Workgroup_Size_Y","Workgroup_Size_Z","Grid_Size_X",'
+           '"Grid_Size_Y","Grid_Size_Z"\n')
+    k = "void fluxbin::lut_gemv_kernel<4, 1, 8, 2, 0, 0>(fluxbin::GemvArgs)"
+    rows = [(k, 100, 130, 112, 17), (k, 200, 220, 112, 17), (k, 300, 400, 112, 17), (k, 400, 410, 16, 57)]
+    lines = [hdr] + [f'"KERNEL_DISPATCH","Agent 1",1,0,1,{i},1,"{n}",{i},{s},{e},0,0,60,0,40,512,1,1,{gx * 512},{gy},1\n'
+                     for i, (n, s, e, gx, gy) in enumerate(rows)]
+    (d / "b_kernel_trace.csv").write_text("".join(lines))
+    out = {(key[1] // key[3], key[2]): (calls, avg, med) for key, calls, avg, med, mn, mx in RS.trace_by_grid(str(d))}
+    assert out == {(112, 17): (3, 50, 30), (16, 57): (1, 10, 10)}
+    monkeypatch.setattr(sys, "argv", ["x", "trace", str(d), "--by-grid", "--kernel", "lut_gemv"])
+    assert RS.main() == 0
+    text = capsys.readouterr().out
+    assert "| 112 x 17 | 3 | 50 | 30 | 20 | 100 |" in text and "| 16 x 57 | 1 | 10 | 10 | 10 | 10 |" in text
