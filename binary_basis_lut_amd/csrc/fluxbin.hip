@@ -218,12 +218,18 @@ fluxbin_status make_plan(const fluxbin_layer_desc *d, Plan *p) {
                 p->splits, kMaxSplits, target);
   // the longest range (balanced cut: ceil(chunks / ranges))
   p->cpb = (int32_t)std::max<int64_t>(cdiv(nc_g, p->rpg), d->ks > 0 ? cdiv(nc_s, p->rps) : 0);
-  // two chunks in flight per wave at g = 4 with one batch row, whatever the
-  // range length: with 8 waves per SIMD the HBM serves fewer, earlier requests
-  // better (70B gate+up 26.3 against 27.6 us with four, down at 8 waves 15.5-15.8
-  // against 16.4-16.7, qkv and o at 4 waves 8.74 / 7.86 against 8.84 / 7.91,
-  // the block-wise gate+up 32.5 against 33.2; interleaved on one MI355X)
-  p->pf = d->g == 4 && p->nb == 1 ? 2 : prefetch_depth(p->cpb);
+  // at g = 4 with one batch row, two chunks in flight per wave, three for
+  // 4-wave workgroups over 4-chunk or longer ranges with per-row scales: with
+  // 8 waves per SIMD the HBM serves fewer, earlier requests better (70B
+  // gate+up 26.3 against 27.6 us with four, down at 8 waves 15.5-15.8 against
+  // 16.4-16.7, the block-wise gate+up 32.5 against 33.2; one chunk is slower
+  // everywhere, gate+up 27.9 against 26.4), while the 4-wave qkv and o take
+  // three (8.59 / 7.78 us against 8.69 / 8.03 with two and 8.76 / 7.97 with
+  // four; interleaved on one MI355X, the same order on another)
+  if (d->g == 4 && p->nb == 1)
+    p->pf = (p->waves == 4 && p->cpb >= 4 && !d->row_group) ? 3 : 2;
+  else
+    p->pf = prefetch_depth(p->cpb);
   p->tb = p->cpb;
   if (p->cpb > cmax) {  // grouped tables: groups of tb chunks, tb a multiple of the prefetch depth
     p->pf = cmax >= 4 ? 4 : 2;

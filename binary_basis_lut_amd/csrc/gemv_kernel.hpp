@@ -381,6 +381,9 @@ void lut_gemv_kernel(const GemvArgs a) {
 // row-scale format RS and table entry type TQ, or nullptr.
 template <int G, int NB, int W, int RS, int TQ>
 gemv_fn gemv_pick_pf(int pf) {
+  if constexpr (G == 4 && NB == 1 && RS == 0) {
+    if (pf == 3) return lut_gemv_kernel<G, NB, W, 3, RS, TQ>;
+  }
   return pf == 8 ? lut_gemv_kernel<G, NB, W, 8, RS, TQ>
          : pf == 4 ? lut_gemv_kernel<G, NB, W, 4, RS, TQ>
          : pf == 2 ? lut_gemv_kernel<G, NB, W, 2, RS, TQ>
