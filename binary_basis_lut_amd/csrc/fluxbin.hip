@@ -250,6 +250,11 @@ fluxbin_status make_plan(const fluxbin_layer_desc *d, Plan *p) {
   // banked tables: one region of 2 or 4 chunks holds every range (cpb_cap
   // keeps g = 8 fp32 ranges at <= 4 chunks)
   p->banked = bank_ok ? (p->cpb <= 2 ? 2 : 4) : 0;
+  // 4-chunk regions (66 KiB of LDS, two workgroups per CU) take 16 waves, so
+  // that the CU still holds 32: the 7B g = 8 down projection 10.29 -> 9.00 us
+  // (2-chunk regions stay at 8 waves, four workgroups per CU: qkv / o /
+  // gate+up 9.07 / 5.65 / 13.04 us against 9.78 / 5.81 / 13.64 at 16)
+  if (p->banked == 4 && !d->waves_per_block) p->waves = 16;
   p->row_blocks = (int32_t)cdiv(p->row_tiles, p->waves);
   p->lds = p->banked ? banked_lds_bytes(p->banked) : lds_bytes(d->g, p->nb, p->tb, entry_bytes(d));
   p->acc_bytes = p->splits > 1 ? (size_t)d->max_batch * p->n_pad * sizeof(uint64_t) : 0;

@@ -80,10 +80,11 @@ struct BankedLane {
 };
 
 // R = 2 layouts take 33 KiB: four workgroups of 8 waves fit a CU, and the
-// registers are held to 64 for 8 waves per SIMD.
+// registers are held to 64 for 8 waves per SIMD.  R = 4 layouts take 66 KiB:
+// two workgroups per CU, so they run 16 waves (1024 rows) to fill it.
 template <int R, int WAVES>
 constexpr int banked_waves_per_eu() {
-  return R == 2 ? 8 : 1;
+  return (R == 2 || WAVES == 16) ? 8 : 1;
 }
 
 template <int R, int WAVES>
@@ -252,7 +253,10 @@ void lut_gemv_g8_banked_kernel(const GemvArgs a) {
 
 template <int R>
 gemv_fn gemv_pick_banked_waves(int waves) {
-  return waves == 8 ? lut_gemv_g8_banked_kernel<R, 8> : waves == 4 ? lut_gemv_g8_banked_kernel<R, 4> : nullptr;
+  return waves == 16  ? lut_gemv_g8_banked_kernel<R, 16>
+         : waves == 8 ? lut_gemv_g8_banked_kernel<R, 8>
+         : waves == 4 ? lut_gemv_g8_banked_kernel<R, 4>
+                      : nullptr;
 }
 
 }  // namespace fluxbin

@@ -83,10 +83,11 @@ def test_g8_layers_take_eight_waves_within_the_lds_budget(fb):
     # tables are 16 sub-vectors x 256 entries, 16 KiB per batch row (fp32).  The bank-private layout
     # takes 2-chunk ranges (four workgroups per CU), or 4 for the down projection, whose 86 chunks
     # per basis would otherwise make 130 ranges
-    expect = {0: (2, 49), 1: (2, 49), 2: (2, 49), 3: (4, 67)}
-    for shape, (cpb, splits) in expect.items():
+    # (4-chunk regions take two workgroups per CU and therefore 16 waves, 1024 rows)
+    expect = {0: (512, 2, 49), 1: (512, 2, 49), 2: (512, 2, 49), 3: (1024, 4, 67)}
+    for shape, (rows, cpb, splits) in expect.items():
         p = plan(fb, workload_desc(fb, 3, shape))
-        assert (p["rows_per_block"], p["chunks_per_block"], p["splits"]) == (512, cpb, splits), shape
+        assert (p["rows_per_block"], p["chunks_per_block"], p["splits"]) == (rows, cpb, splits), shape
         # one batch row, per-row scales, fp32 entries: bank-private tables over the range's chunks
         assert p["banked_tables"] == (4 if cpb > 2 else 2), shape
         assert p["lds_bytes"] == p["banked_tables"] * (16 * 256 * 4 + 128 * 4), shape
