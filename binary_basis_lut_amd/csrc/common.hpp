@@ -227,8 +227,9 @@ gemv_fn gemv_pick_g4_rs1_t16(int nb, int waves, int pf);
 gemv_fn gemv_pick_g8_rs0_t16(int nb, int waves, int pf);
 gemv_fn gemv_pick_g8_rs1_t16(int nb, int waves, int pf);
 // The g = 8 kernel with bank-private tables (one batch row, per-row scales,
-// fp32 entries) for column ranges of up to `region` (2 or 4) chunks.
-gemv_fn gemv_pick_g8_banked(int region, int waves);
+// fp32 entries) for column ranges of up to `regions` (1, or 2 for region 2)
+// regions of `region` (2 or 4) chunks.
+gemv_fn gemv_pick_g8_banked(int region, int regions, int waves);
 
 __device__ __forceinline__ float h2f(uint16_t h) { return __half2float(__ushort_as_half(h)); }
 __device__ __forceinline__ uint16_t f2h(float f) { return __half_as_ushort(__float2half_rn(f)); }
@@ -416,9 +417,12 @@ __host__ __device__ constexpr int lds_bytes(int g, int nb, int cpb, int eb) {
   return cpb * lds_per_chunk(g, nb, eb) + kLdsSink;
 }
 
-// LDS of the g = 8 bank-private-table kernel over a region of r chunks: the
-// tables (16 r x 256 fp32), then the r * 128 fp32 scale-fused inputs.
-__host__ __device__ constexpr int banked_lds_bytes(int r) { return r * (16 * 256 * 4 + kChunkCols * 4); }
+// LDS of the g = 8 bank-private-table kernel over ranges of nreg regions of r
+// chunks: one region's tables (16 r x 256 fp32), then the scale-fused inputs
+// of all the range's chunks (nreg r x 128 fp32).
+__host__ __device__ constexpr int banked_lds_bytes(int r, int nreg) {
+  return r * 16 * 256 * 4 + nreg * r * kChunkCols * 4;
+}
 
 __host__ __device__ constexpr int cmin(int a, int b) { return a < b ? a : b; }
 

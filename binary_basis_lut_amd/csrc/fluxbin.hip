@@ -63,7 +63,8 @@ struct Plan {
   int32_t total_chunks;
   int32_t rpg, rps;    // column ranges per global / salient segment
   int32_t splits;      // kb * rpg + ks * rps
-  int32_t banked;      // g = 8 bank-private tables over ranges of this many chunks (2 or 4), else 0
+  int32_t banked;      // g = 8 bank-private tables over regions of this many chunks (2 or 4), else 0
+  int32_t bregions;    // regions per column range of the banked kernel (1, or 2 with 2-chunk regions)
   int32_t lds;         // dynamic LDS bytes of one workgroup
   uint32_t range[kMaxSplits];  // range_word of every split: segment, first chunk, chunk count
   int64_t n_pad;
@@ -150,15 +151,19 @@ int32_t auto_cpb(int32_t nb, int32_t cmax, int32_t waves, int64_t row_tiles, int
   return (int32_t)std::max<int64_t>(1, std::min<int64_t>(p, cmax));
 }
 
-// Ranges of the banked g = 8 kernel: 2 chunks (33 KiB of LDS, four
-// workgroups per CU), or 4 (two per CU) where 2-chunk ranges would cut the
-// layer into more than 64 column ranges.  Measured on MI355X (graph of 32
-// distinct resident weight sets of the LLaMA-2-7B g = 8 layer, 8 waves), 2 /
-// 4-chunk ranges: qkv 9.4 / 10.6 us, o 6.0 / 6.2, gate+up 13.7 / 15.2, down
-// (130 / 67 ranges) 11.8 / 11.1.
-int32_t banked_cpb(const fluxbin_layer_desc *d) {
+// Ranges of the banked g = 8 kernel (automatic plan): 2 chunks (one 2-chunk
+// region, 33 KiB of LDS, four 8-wave workgroups per CU), or 4 chunks as two
+// 2-chunk regions in turn (the same LDS and occupancy, half the split
+// atomics) where 2-chunk ranges would make more than 64 column ranges or
+// more than 1536 workgroups.  Measured on MI355X (graph of 32 distinct
+// resident weight sets of the LLaMA-2-7B g = 8 layer, 8 waves, interleaved),
+// one / two regions per range: gate+up (2107 workgroups) 13.09 / 12.44 us,
+// down (130 ranges) 9.19 (4-chunk regions at 16 waves) / 8.81, qkv (1176)
+// 9.14 / 9.21, o (392) 5.64 / 6.04.
+int32_t banked_cpb(const fluxbin_layer_desc *d, int64_t row_tiles) {
   const int64_t ranges2 = d->kb * cdiv(cdiv(d->k, kChunkCols), 2) + d->ks * cdiv(cdiv(d->s, kChunkCols), 2);
-  return ranges2 > 64 ? 4 : 2;
+  const int64_t blocks2 = cdiv(row_tiles, 8) * ranges2;
+  return (ranges2 > 64 || blocks2 > 1536) ? 4 : 2;
 }
 
 // Batch rows one workgroup serves (the kernel's compiled width): the next
@@ -202,7 +207,7 @@ fluxbin_status make_plan(const fluxbin_layer_desc *d, Plan *p) {
   // g = 8, one batch row, per-row scales, fp32 entries: bank-private tables
   const bool bank_ok = d->g == 8 && p->nb == 1 && !d->row_group && entry_bytes(d) == 4;
   int32_t target = d->chunks_per_block ? d->chunks_per_block
-                   : bank_ok           ? banked_cpb(d)
+                   : bank_ok           ? banked_cpb(d, p->row_tiles)
                                        : auto_cpb(p->nb, grouped_ok && d->g == 4 ? kMaxCpb : cmax, p->waves, p->row_tiles,
                                               p->total_chunks, wide ? kTargetBlocks / 2 : kTargetBlocks);
   const int32_t nc_g = (int32_t)cdiv(d->k, kChunkCols), nc_s = d->ks > 0 ? (int32_t)cdiv(d->s, kChunkCols) : 0;
@@ -247,16 +252,20 @@ fluxbin_status make_plan(const fluxbin_layer_desc *d, Plan *p) {
     const int32_t lo = (int32_t)((int64_t)rr * nc / nr), hi = (int32_t)((int64_t)(rr + 1) * nc / nr);
     p->range[sp] = range_word(sg, lo, hi - lo);
   }
-  // banked tables: one region of 2 or 4 chunks holds every range (cpb_cap
-  // keeps g = 8 fp32 ranges at <= 4 chunks)
-  p->banked = bank_ok ? (p->cpb <= 2 ? 2 : 4) : 0;
+  // banked tables (cpb_cap keeps g = 8 fp32 ranges at <= 4 chunks): the
+  // automatic plan takes 2-chunk regions, one per range or, for 3- or 4-chunk
+  // ranges, two in turn; a given chunks_per_block takes one region of 2 or 4
+  // chunks that holds the whole range
+  p->banked = bank_ok ? (p->cpb <= 2 || !d->chunks_per_block ? 2 : 4) : 0;
+  p->bregions = p->banked && p->cpb > p->banked ? 2 : 1;
+  if (p->banked) p->tb = p->banked;
   // 4-chunk regions (66 KiB of LDS, two workgroups per CU) take 16 waves, so
   // that the CU still holds 32: the 7B g = 8 down projection 10.29 -> 9.00 us
   // (2-chunk regions stay at 8 waves, four workgroups per CU: qkv / o /
   // gate+up 9.07 / 5.65 / 13.04 us against 9.78 / 5.81 / 13.64 at 16)
   if (p->banked == 4 && !d->waves_per_block) p->waves = 16;
   p->row_blocks = (int32_t)cdiv(p->row_tiles, p->waves);
-  p->lds = p->banked ? banked_lds_bytes(p->banked) : lds_bytes(d->g, p->nb, p->tb, entry_bytes(d));
+  p->lds = p->banked ? banked_lds_bytes(p->banked, p->bregions) : lds_bytes(d->g, p->nb, p->tb, entry_bytes(d));
   p->acc_bytes = p->splits > 1 ? (size_t)d->max_batch * p->n_pad * sizeof(uint64_t) : 0;
   return FLUXBIN_OK;
 }
@@ -783,7 +792,7 @@ fluxbin_status fluxbin_create(const fluxbin_layer_desc *d, fluxbin_handle *out) 
     hipError_t e = hipDeviceSynchronize();
     if (e != hipSuccess) return hip_fail(e, "synchronising after create");
   }
-  gemv_fn fn = p.banked ? gemv_pick_g8_banked(p.banked, p.waves)
+  gemv_fn fn = p.banked ? gemv_pick_g8_banked(p.banked, p.bregions, p.waves)
                         : pick_gemv(d->g, d->row_group ? 1 : 0, d->table_precision, p.nb, p.waves, p.pf);
   if (!fn) return fail(FLUXBIN_ERR_UNSUPPORTED, "no kernel for g = %d, batch width %d, %d waves", d->g, p.nb, p.waves);
   const size_t lds = (size_t)p.lds;

@@ -87,14 +87,18 @@ constexpr int banked_waves_per_eu() {
   return (R == 2 || WAVES == 16) ? 8 : 1;
 }
 
-template <int R, int WAVES>
+// A column range of up to NREG regions of R chunks: the inputs of all of
+// them are staged and all of their sign words requested at once; the regions'
+// tables are then built and looked up one after the other in the same LDS.
+template <int R, int WAVES, int NREG>
 __global__ __launch_bounds__(WAVES * 64)
 __attribute__((amdgpu_waves_per_eu(banked_waves_per_eu<R, WAVES>())))
 void lut_gemv_g8_banked_kernel(const GemvArgs a) {
   static_assert(R == 2 || R == 4, "region of 2 or 4 chunks");
+  static_assert(NREG == 1 || NREG == 2, "one or two regions per range");
   constexpr int NT = WAVES * 64;
   constexpr int NTAB = 16 * R;        // tables of the region
-  constexpr int ITEMS = R * kChunkCols;
+  constexpr int ITEMS = R * kChunkCols * NREG;
   constexpr int VPT = ITEMS >= NT ? ITEMS / NT : 1;
   constexpr int GR = 64 / R;          // rows of one row group: 16 rows per chunk lane group x R chunks = 64 lanes
   constexpr int NG = R;               // row groups of the wave's 64-row tile
@@ -129,12 +133,12 @@ void lut_gemv_g8_banked_kernel(const GemvArgs a) {
   const ColRange cr = column_range(a, sp);
   const SegRef S = cr.S;
   const int c_lo = cr.c_lo, nch = cr.nch;
-  const bool cl = c < nch;  // this lane's chunk exists (ranges may be shorter than R)
-  // this lane's 16 bytes of row group g: element
-  // ((tile * nchunks + chunk) * 64 + g * GR + h * 16 + r); waves past the last
-  // tile read the last one and store nothing
+  // this lane's 16 bytes of row group g of region q: element
+  // ((tile * nchunks + c_lo + q R + c) * 64 + g * GR + h * 16 + r); waves past
+  // the last tile read the last one and store nothing; lanes whose chunk does
+  // not exist (ranges may be shorter than NREG R) load nothing
   const int ltile = min(tile, a.row_tiles - 1);
-  const FB_GLOBAL u32x4 *wp = S.bits + ((int64_t)ltile * S.nchunks + c_lo + (cl ? c : 0)) * kTileRows + h * 16 + r;
+  const FB_GLOBAL u32x4 *wp = S.bits + ((int64_t)ltile * S.nchunks + c_lo) * kTileRows + h * 16 + r;
 
   auto body = [&](auto sal_tag) {
     constexpr bool SAL = decltype(sal_tag)::value;
@@ -157,12 +161,17 @@ void lut_gemv_g8_banked_kernel(const GemvArgs a) {
       ccl[i] = live[i] ? cc : 0u;
       cvl[i] = S.c[ccl[i]];
     }
-    u32x4 wb[NG];
+    u32x4 wb[NREG][NG];
     auto issue_weights = [&]() {
 #pragma unroll
-      for (int g = 0; g < NG; ++g) {
-        wb[g] = u32x4{0u, 0u, 0u, 0u};
-        if (cl) wb[g] = __builtin_nontemporal_load(wp + g * GR);
+      for (int q = 0; q < NREG; ++q) {
+        const int ch = q * R + c;
+        const bool cl = ch < nch;
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+          wb[q][g] = u32x4{0u, 0u, 0u, 0u};
+          if (cl) wb[q][g] = __builtin_nontemporal_load(wp + (cl ? ch : 0) * kTileRows + g * GR);
+        }
       }
     };
     if constexpr (!SAL) {
@@ -189,34 +198,39 @@ void lut_gemv_g8_banked_kernel(const GemvArgs a) {
     }
     __syncthreads();
 
-    // Tables: unit u = (combo, T), T fastest, so that the 64 lanes of a
-    // store write 64 consecutive dwords (one row p of the layout, or two).
-    for (int u = tid; u < NTAB * 16; u += NT) {
-      const int T = u & (NTAB - 1);
-      const int un = u / NTAB;
-      float e[16];
-      g8_unit_entries(s_v + 8 * T, un, e);
-      const int p0 = ((un >> 3) << 7) | (un & 7);
-      float *tb = s_tab + p0 * NTAB + T;
-#pragma unroll
-      for (int m = 0; m < 16; ++m) tb[m * 8 * NTAB] = e[m];
-    }
-    __syncthreads();
-
     const BankedLane<R> L(c, r);
-    uint32_t ew[NG][4];
-#pragma unroll
-    for (int g = 0; g < NG; ++g) L.order(wb[g], ew[g]);
-    // the row groups' lookups of one step go out together (independent reads)
     float acc[NG][2];
 #pragma unroll
     for (int g = 0; g < NG; ++g) acc[g][0] = acc[g][1] = 0.0f;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int rq = 0; rq < NREG; ++rq) {
+      if (rq * R >= nch) break;  // uniform: the range ends before this region
+      if (rq > 0) __syncthreads();  // every wave is done with the previous region's tables
+      // Tables: unit u = (combo, T), T fastest, so that the 64 lanes of a
+      // store write 64 consecutive dwords (one row p of the layout, or two).
+      for (int u = tid; u < NTAB * 16; u += NT) {
+        const int T = u & (NTAB - 1);
+        const int un = u / NTAB;
+        float e[16];
+        g8_unit_entries(s_v + rq * R * kChunkCols + 8 * T, un, e);
+        const int p0 = ((un >> 3) << 7) | (un & 7);
+        float *tb = s_tab + p0 * NTAB + T;
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
+        for (int m = 0; m < 16; ++m) tb[m * 8 * NTAB] = e[m];
+      }
+      __syncthreads();
+
+      uint32_t ew[NG][4];
 #pragma unroll
-        for (int g = 0; g < NG; ++g) acc[g][kk & 1] += L.entry(ew[g], q, kk);
+      for (int g = 0; g < NG; ++g) L.order(wb[rq][g], ew[g]);
+      // the row groups' lookups of one step go out together (independent reads)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+          for (int g = 0; g < NG; ++g) acc[g][kk & 1] += L.entry(ew[g], q, kk);
+        }
       }
     }
 
@@ -251,11 +265,11 @@ void lut_gemv_g8_banked_kernel(const GemvArgs a) {
   }
 }
 
-template <int R>
+template <int R, int NREG>
 gemv_fn gemv_pick_banked_waves(int waves) {
-  return waves == 16  ? lut_gemv_g8_banked_kernel<R, 16>
-         : waves == 8 ? lut_gemv_g8_banked_kernel<R, 8>
-         : waves == 4 ? lut_gemv_g8_banked_kernel<R, 4>
+  return waves == 16  ? lut_gemv_g8_banked_kernel<R, 16, NREG>
+         : waves == 8 ? lut_gemv_g8_banked_kernel<R, 8, NREG>
+         : waves == 4 ? lut_gemv_g8_banked_kernel<R, 4, NREG>
                       : nullptr;
 }
 

@@ -169,10 +169,12 @@ typedef struct {
   int64_t grid;             /* workgroups per fluxbin_gemv launch (per group of batch rows) */
   int32_t banked_tables;    /* 0: each sub-vector's table in consecutive dwords, one row per lane; 2 or 4
                                (g = 8, one batch row, per-row scales, fp32 entries): bank-private tables,
-                               each a column of the LDS, over column ranges of up to that many chunks */
+                               each a column of the LDS, over regions of that many chunks (a column
+                               range of up to chunks_per_block chunks is one region, or two 2-chunk
+                               regions in turn) */
   int32_t table_chunks;     /* chunks whose tables a workgroup holds in LDS at once: chunks_per_block, or
-                               with several batch rows fewer, the tables then built in groups of this many
-                               chunks in turn while the range's sign words stream */
+                               fewer (several batch rows; two-region banked ranges), the tables then built
+                               in groups of this many chunks in turn while the range's sign words stream */
 } fluxbin_plan;
 
 int32_t fluxbin_abi_version(void);

@@ -335,9 +335,11 @@ def test_gemv_edge_cases(fb, orc, g, n, k, kb, ks, s, batch, cpb, waves):
 # g = 8 bank-private tables (one batch row, per-row scales, fp32 entries): regions of 2 and 4 chunks
 # at 4 and 8 waves, column ranges shorter than the region (k = 1000: 8 chunks cut 3-3-2; k = 384: one
 # range of 3), rows that fill neither the last tile nor the last row block, a single row, salient
-# segments of 1 and 2 chunks, and the automatic plan (which runs 4-chunk regions as 16-wave
-# workgroups of 1024 rows: k = 11008 with 300 rows fills five of a block's sixteen tiles, with
-# 1100 rows one block and two tiles of the next, the last tile partly).  Dyadic inputs must give
+# segments of 1 and 2 chunks, a given 4-chunk range at the automatic wave count (one 4-chunk region,
+# 16-wave workgroups of 1024 rows: 1100 rows fill one block and two tiles of the next, the last
+# tile partly), and the automatic plan (2-chunk regions, two in turn per range for the wide
+# layers: k = 11008 cuts 86 chunks into ranges of 3 and 4, so some ranges end inside their second
+# region, and its 2-chunk salient ranges have no second region).  Dyadic inputs must give
 # RNE(exact) bitwise; random inputs the rounding bound.
 BANKED = [
     # n, k, kb, ks, s, cpb, waves, region
@@ -353,6 +355,7 @@ BANKED = [
     (1, 4096, 1, 0, 0, 4, 8, 4),
     (1, 4096, 1, 0, 0, 2, 4, 2),
     (513, 4096, 4, 2, 82, 0, 0, None),
+    (1100, 11008, 3, 1, 220, 4, 0, 4),
     (300, 11008, 3, 1, 220, 0, 0, None),
     (1100, 11008, 3, 1, 220, 0, 0, None),
 ]
@@ -364,8 +367,10 @@ def test_g8_banked_tables(fb, orc, n, k, kb, ks, s, cpb, waves, region):
     layer = I.dyadic_layer(n, k, kb, ks, 8, s, seed=n + 3 * k + cpb)
     x = I.dyadic_x(k, 1, seed=k + cpb)
     dl = fb.DeviceLayer(layer, chunks_per_block=cpb, waves_per_block=waves)
-    assert dl.plan["banked_tables"] == (region or (4 if dl.plan["chunks_per_block"] > 2 else 2))
-    if not waves:  # automatic: 16 waves for 4-chunk regions, 8 for 2-chunk ones
+    # automatic plan: 2-chunk regions, one or two per range
+    assert dl.plan["banked_tables"] == (region or 2)
+    assert dl.plan["table_chunks"] == dl.plan["banked_tables"]
+    if not waves:  # automatic wave count: 16 for 4-chunk regions, 8 for 2-chunk ones
         assert dl.plan["rows_per_block"] == (1024 if dl.plan["banked_tables"] == 4 else 512)
     y16 = gemv(fb, dl, x)
     y_ref, _ = orc.gemv_dense(layer, x)

@@ -81,16 +81,20 @@ def test_very_wide_single_row_layers_take_eight_waves(fb):
 def test_g8_layers_take_eight_waves_within_the_lds_budget(fb):
     # 7B layer, 3 global bases + 2 % salient, g = 8: 512 rows per workgroup; a chunk's g = 8
     # tables are 16 sub-vectors x 256 entries, 16 KiB per batch row (fp32).  The bank-private layout
-    # takes 2-chunk ranges (four workgroups per CU), or 4 for the down projection, whose 86 chunks
-    # per basis would otherwise make 130 ranges
-    # (4-chunk regions take two workgroups per CU and therefore 16 waves, 1024 rows)
-    expect = {0: (512, 2, 49), 1: (512, 2, 49), 2: (512, 2, 49), 3: (1024, 4, 67)}
-    for shape, (rows, cpb, splits) in expect.items():
+    # takes 2-chunk regions (four workgroups per CU): one per range, or two in turn per 4-chunk
+    # range where 2-chunk ranges would make more than 1536 workgroups (gate+up: 43 row blocks x 49)
+    # or more than 64 ranges (down: 86 chunks per basis)
+    expect = {0: (2, 49, 1176), 1: (2, 49, 392), 2: (4, 25, 1075), 3: (4, 67, 536)}
+    for shape, (cpb, splits, grid) in expect.items():
         p = plan(fb, workload_desc(fb, 3, shape))
-        assert (p["rows_per_block"], p["chunks_per_block"], p["splits"]) == (rows, cpb, splits), shape
-        # one batch row, per-row scales, fp32 entries: bank-private tables over the range's chunks
-        assert p["banked_tables"] == (4 if cpb > 2 else 2), shape
-        assert p["lds_bytes"] == p["banked_tables"] * (16 * 256 * 4 + 128 * 4), shape
+        assert (p["rows_per_block"], p["chunks_per_block"], p["splits"], p["grid"]) == (512, cpb, splits, grid), shape
+        # one batch row, per-row scales, fp32 entries: bank-private tables, one 2-chunk region at a time
+        assert (p["banked_tables"], p["table_chunks"]) == (2, 2), shape
+        assert p["lds_bytes"] == 2 * 16 * 256 * 4 + cpb * 128 * 4, shape
+    # a given chunks_per_block of 3 or 4 takes one 4-chunk region, 16 waves (two workgroups per CU)
+    p = plan(fb, workload_desc(fb, 3, 3, chunks_per_block=4))
+    assert (p["rows_per_block"], p["banked_tables"], p["table_chunks"]) == (1024, 4, 4)
+    assert p["lds_bytes"] == 4 * (16 * 256 * 4 + 128 * 4)
     # fp16 entries halve the tables (and keep the one-table-per-sub-vector layout)
     p = plan(fb, workload_desc(fb, 3, 2, table_precision=fb.TABLE_F16, chunks_per_block=4))
     assert p["lds_bytes"] == 4 * (16 * 256 * 2 + 128 * 4) + 256 and p["banked_tables"] == 0
