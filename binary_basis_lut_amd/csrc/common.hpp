@@ -440,7 +440,9 @@ __host__ __device__ constexpr int cpb_cap(int g, int nb, int eb) {
              : cmin(kMaxCpb, (kLdsBudget - kLdsSink) / lds_per_chunk(g, nb, eb));
 }
 
-// Chunks of weights in flight per wave for ranges of up to cpb chunks.
+// Chunks of weights in flight per wave for ranges of up to cpb chunks, for
+// several batch rows and for g = 8 outside the bank-private kernel (one batch
+// row at g = 4 takes two or three whatever the range length: make_plan).
 __host__ __device__ constexpr int prefetch_depth(int cpb) { return cpb >= 4 ? 4 : 2; }
 
 // The column range of split sp (uniform): segment sg, chunks [c_lo, c_lo +

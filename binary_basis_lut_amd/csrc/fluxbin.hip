@@ -57,7 +57,7 @@ struct Plan {
   int32_t cpb;         // most chunks in one column range
   int32_t tb;          // chunks whose tables LDS holds at once (LDS is sized for it): cpb, or for
                        // several batch rows a multiple of pf below cpb (tables built in groups)
-  int32_t pf;          // chunks of weights in flight per wave (2 or 4)
+  int32_t pf;          // chunks of weights in flight per wave (2, 3 or 4)
   int32_t row_tiles;
   int32_t row_blocks;
   int32_t total_chunks;

@@ -64,6 +64,19 @@ def test_static_scratch_matches_the_workspace_call_on_consecutive_calls(fb):
     dl_small.close()
 
 
+def test_static_scratch_with_the_banked_g8_kernel(fb):
+    note("static scratch: g = 8 banked plans, two 2-chunk regions per range and one")
+    for n, k in ((300, 11008), (700, 1024)):
+        layer = I.make_layer(n, k, 3, 1, 8, s=224 if k > 4096 else 32, outlier_frac=0.0, seed=(78, n, k))
+        dl = fb.DeviceLayer(layer)
+        assert dl.plan["banked_tables"] == 2 and dl.plan["splits"] > 1
+        assert dl.plan["chunks_per_block"] == (4 if k > 4096 else 2)
+        x = dev(I.make_x(layer, 1, seed=(78, n, k)))
+        y0, y1 = both(fb, dl, x, 1)
+        assert torch.equal(y0, y1)
+        dl.close()
+
+
 def test_handle_without_workspace(fb):
     note("static scratch: q_proj handle created without a workspace")
     layer = I.workload_layer(2)
