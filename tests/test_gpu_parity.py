@@ -384,6 +384,37 @@ def test_g8_banked_tables(fb, orc, n, k, kb, ks, s, cpb, waves, region):
     dl.close()
 
 
+# The split reduction at its limit: one-chunk column ranges cut these rows into exactly 255
+# ranges, the most the 8-bit arrival count of a reduction word takes (the last arriver finds 254
+# arrivals before its own); g = 4 with and without a salient basis (ragged k and s), and the
+# bank-private g = 8 kernel.  Dyadic inputs must give RNE(exact) bitwise; random inputs the bound.
+SPLIT_LIMIT = [
+    # n, k, kb, ks, s, g
+    (300, 10800, 3, 0, 0, 4),
+    (257, 16100, 2, 1, 384, 4),
+    (300, 10800, 3, 0, 0, 8),
+]
+
+
+@pytest.mark.parametrize("n,k,kb,ks,s,g", SPLIT_LIMIT)
+def test_split_count_at_its_limit(fb, orc, n, k, kb, ks, s, g):
+    note(f"255 splits: n={n} k={k} kb={kb} ks={ks} s={s} g={g}")
+    layer = I.dyadic_layer(n, k, kb, ks, g, s, seed=n + k + g)
+    x = I.dyadic_x(k, 1, seed=k + g)
+    dl = fb.DeviceLayer(layer, chunks_per_block=1)
+    assert dl.plan["splits"] == 255 and dl.plan["chunks_per_block"] == 1
+    y16 = gemv(fb, dl, x)
+    y_ref, _ = orc.gemv_dense(layer, x)
+    assert np.array_equal(y16, orc.double_to_half(y_ref)), "y differs from RNE(exact)"
+    dl.close()
+    layer = I.make_layer(n, k, kb, ks, g, s=s if ks else None, outlier_frac=0.01, seed=(66, n, k))
+    x = I.make_x(layer, 1, seed=(66, n, k))
+    dl = fb.DeviceLayer(layer, chunks_per_block=1)
+    y16 = gemv(fb, dl, x)
+    check_y(orc, layer, x, y16, dl.plan)
+    dl.close()
+
+
 def test_batch_zero_is_a_no_op(fb):
     layer = I.workload_layer(1)
     dl = fb.DeviceLayer(layer)
