@@ -9,9 +9,11 @@
 // the LLaMA-2-7B g = 8 gate+up shape such stalls were two thirds of the
 // LDS-active cycles.
 //
-// The layout.  A workgroup's column range of up to R chunks (R = 2 or 4) has
-// 16 R tables, table T = 16 c + t for sub-vector t (8 columns) of chunk c of
-// the range.  Entry p of table T is the dword p * 16R + T: each table is a
+// The layout.  A region of R chunks (R = 2 or 4) of a workgroup's column
+// range has 16 R tables, table T = 16 c + t for sub-vector t (8 columns) of
+// chunk c of the region; a range is one region, or two 2-chunk regions whose
+// tables are built and looked up in turn in the same LDS.  Entry p of table
+// T is the dword p * 16R + T: each table is a
 // column of the LDS, one bank (dword address mod 32, or mod 64 for R = 4)
 // holding all of it.  A lane is a (chunk c, row) pair, 16 rows per chunk:
 // at step i (0..15) the lane with row index r (0..15 in its group of 16)
@@ -24,9 +26,11 @@
 // at step group q (the 4 words permuted once per load, 8 selects) and byte
 // kk XOR (r mod 4) of it; one v_perm_b32 with a per-lane selector picks that
 // byte and merges it with the table's column, which makes the LDS address.
-// After the range, the partial sums of one row are spread over the R chunk
-// lanes that share it and are added with R = 4: two, R = 2: one cross-lane
-// exchange, after which each lane owns one row of the 64-row tile.
+// A lane keeps its chunk position c in every region, so its sums run on
+// across regions.  After the range, the partial sums of one row are spread
+// over the R chunk lanes that share it and are added with R = 4: two, R = 2:
+// one cross-lane exchange, after which each lane owns one row of the 64-row
+// tile.
 #pragma once
 
 #include "common.hpp"
