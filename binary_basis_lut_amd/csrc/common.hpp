@@ -226,6 +226,9 @@ gemv_fn gemv_pick_g4_rs0_t16(int nb, int waves, int pf);
 gemv_fn gemv_pick_g4_rs1_t16(int nb, int waves, int pf);
 gemv_fn gemv_pick_g8_rs0_t16(int nb, int waves, int pf);
 gemv_fn gemv_pick_g8_rs1_t16(int nb, int waves, int pf);
+// g = 4, one batch row, per-row scales, fp32 entries, two waves per row tile
+// (KS = 2): the instance for waves per workgroup and prefetch depth pf.
+gemv_fn gemv_pick_g4_ks2(int waves, int pf);
 // The g = 8 kernel with bank-private tables (one batch row, per-row scales,
 // fp32 entries) for column ranges of up to `regions` (1, or 2 for region 2)
 // regions of `region` (2 or 4) chunks.
@@ -430,7 +433,7 @@ __host__ __device__ constexpr int cmin(int a, int b) { return a < b ? a : b; }
 // loads are all in flight at once): with one batch row 4 (4 waves) or 2 (8
 // waves), so that one round covers an 8-chunk range; 8 for several rows.
 // Longer ranges stage in further rounds.
-__host__ __device__ constexpr int stage_items(int nb, int waves) { return nb == 1 ? (waves == 8 ? 2 : 4) : 8; }
+__host__ __device__ constexpr int stage_items(int nb, int waves) { return nb == 1 ? (waves >= 8 ? 2 : 4) : 8; }
 
 // Most chunks one workgroup may take for table width g, batch width nb and
 // eb-byte entries: its tables and inputs must fit the LDS budget.

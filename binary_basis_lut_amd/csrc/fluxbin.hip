@@ -50,6 +50,7 @@ bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 constexpr int kTargetBlocks = 1024;  // about four workgroups per CU
+constexpr int kCus = 256;            // compute units of an MI355X (8 XCDs of 32)
 
 struct Plan {
   int32_t waves;       // waves per workgroup (64 rows each)
@@ -58,6 +59,7 @@ struct Plan {
   int32_t tb;          // chunks whose tables LDS holds at once (LDS is sized for it): cpb, or for
                        // several batch rows a multiple of pf below cpb (tables built in groups)
   int32_t pf;          // chunks of weights in flight per wave (2, 3 or 4)
+  int32_t ks;          // waves per row tile (g = 4, one batch row: 1, or 2 over the two halves of a range)
   int32_t row_tiles;
   int32_t row_blocks;
   int32_t total_chunks;
@@ -181,6 +183,7 @@ fluxbin_status make_plan(const fluxbin_layer_desc *d, Plan *p) {
   p->n_pad = (int64_t)p->row_tiles * kTileRows;
   p->total_chunks = (int32_t)(d->kb * cdiv(d->k, kChunkCols) + d->ks * cdiv(d->s, kChunkCols));
   p->nb = batch_group(d->g, d->max_batch);
+  p->ks = 1;
   // one batch row at g = 4, per-row scales, over very many chunks (the 70B
   // down projection; its block-wise form is slower at 8 waves: 21.2 against
   // 20.3 us)
@@ -210,6 +213,23 @@ fluxbin_status make_plan(const fluxbin_layer_desc *d, Plan *p) {
                    : bank_ok           ? banked_cpb(d, p->row_tiles)
                                        : auto_cpb(p->nb, grouped_ok && d->g == 4 ? kMaxCpb : cmax, p->waves, p->row_tiles,
                                               p->total_chunks, wide ? kTargetBlocks / 2 : kTargetBlocks);
+  // Two waves per row tile where one wave per tile would take 2-chunk ranges
+  // over more workgroups than the chip has CUs (g = 4, one batch row, per-row
+  // scales, fp32 entries, 4-wave layers, automatic plan): 8-wave workgroups of
+  // 256 rows over 4-chunk ranges, each wave over two of their chunks, half the
+  // ranges and so half the split atomics for the same waves.  Measured on
+  // MI355X (256 resident weight sets, one graph, interleaved), one / two
+  // waves per tile: q_proj 5.13 / 5.01 us, the 7B 11008 -> 4096 projection at
+  // one batch row 7.65 / 6.55, 4096 -> 11008 6.53 / 6.50; slower where the
+  // one-wave plan has few workgroups (512 x 512: 3.50 / 3.86, 8 workgroups)
+  // or longer ranges (the 70B qkv 8.67 / 9.45, gate+up 26.3 / 29.4).
+  if (!d->chunks_per_block && !d->waves_per_block && d->g == 4 && p->nb == 1 && !d->row_group &&
+      entry_bytes(d) == 4 && p->waves == 4 && target == 2 && cmax >= 4 &&
+      cdiv(p->row_tiles, 4) * cdiv(p->total_chunks, 2) > kCus) {
+    p->ks = 2;
+    p->waves = 8;
+    target = 4;
+  }
   const int32_t nc_g = (int32_t)cdiv(d->k, kChunkCols), nc_s = d->ks > 0 ? (int32_t)cdiv(d->s, kChunkCols) : 0;
   for (;;) {
     p->rpg = (int32_t)cdiv(nc_g, target);
@@ -230,9 +250,10 @@ fluxbin_status make_plan(const fluxbin_layer_desc *d, Plan *p) {
   // 16.4-16.7, the block-wise gate+up 32.5 against 33.2; one chunk is slower
   // everywhere, gate+up 27.9 against 26.4), while the 4-wave qkv and o take
   // three (8.59 / 7.78 us against 8.69 / 8.03 with two and 8.76 / 7.97 with
-  // four; interleaved on one MI355X, the same order on another)
+  // four; interleaved on one MI355X, the same order on another); two waves
+  // per row tile take two at any range length
   if (d->g == 4 && p->nb == 1)
-    p->pf = (p->waves == 4 && p->cpb >= 4 && !d->row_group) ? 3 : 2;
+    p->pf = (p->ks == 1 && p->waves == 4 && p->cpb >= 4 && !d->row_group) ? 3 : 2;
   else
     p->pf = prefetch_depth(p->cpb);
   p->tb = p->cpb;
@@ -264,8 +285,9 @@ fluxbin_status make_plan(const fluxbin_layer_desc *d, Plan *p) {
   // (2-chunk regions stay at 8 waves, four workgroups per CU: qkv / o /
   // gate+up 9.07 / 5.65 / 13.04 us against 9.78 / 5.81 / 13.64 at 16)
   if (p->banked == 4 && !d->waves_per_block) p->waves = 16;
-  p->row_blocks = (int32_t)cdiv(p->row_tiles, p->waves);
+  p->row_blocks = (int32_t)cdiv(p->row_tiles, p->waves / p->ks);
   p->lds = p->banked ? banked_lds_bytes(p->banked, p->bregions) : lds_bytes(d->g, p->nb, p->tb, entry_bytes(d));
+  if (p->ks == 2) p->lds += (p->waves / 2) * kTileRows * 4;  // the second waves' partials
   p->acc_bytes = p->splits > 1 ? (size_t)d->max_batch * p->n_pad * sizeof(uint64_t) : 0;
   return FLUXBIN_OK;
 }
@@ -792,7 +814,8 @@ fluxbin_status fluxbin_create(const fluxbin_layer_desc *d, fluxbin_handle *out) 
     hipError_t e = hipDeviceSynchronize();
     if (e != hipSuccess) return hip_fail(e, "synchronising after create");
   }
-  gemv_fn fn = p.banked ? gemv_pick_g8_banked(p.banked, p.bregions, p.waves)
+  gemv_fn fn = p.ks == 2 ? gemv_pick_g4_ks2(p.waves, p.pf)
+               : p.banked ? gemv_pick_g8_banked(p.banked, p.bregions, p.waves)
                         : pick_gemv(d->g, d->row_group ? 1 : 0, d->table_precision, p.nb, p.waves, p.pf);
   if (!fn) return fail(FLUXBIN_ERR_UNSUPPORTED, "no kernel for g = %d, batch width %d, %d waves", d->g, p.nb, p.waves);
   const size_t lds = (size_t)p.lds;
@@ -828,7 +851,7 @@ fluxbin_status fluxbin_destroy(fluxbin_handle h) {
 namespace {
 
 void fill_plan(const fluxbin_layer_desc &d, const Plan &p, fluxbin_plan *plan) {
-  plan->rows_per_block = p.waves * kTileRows;
+  plan->rows_per_block = p.waves / p.ks * kTileRows;
   plan->chunks_per_block = p.cpb;
   plan->row_blocks = p.row_blocks;
   plan->splits = p.splits;
@@ -837,6 +860,7 @@ void fill_plan(const fluxbin_layer_desc &d, const Plan &p, fluxbin_plan *plan) {
   plan->grid = (int64_t)p.row_blocks * p.splits;
   plan->banked_tables = p.banked;
   plan->table_chunks = p.tb;
+  plan->threads_per_block = p.waves * 64;
 }
 
 }  // namespace

@@ -48,11 +48,16 @@ constexpr int lut_waves_per_eu() {
 //     again, which keeps the compiler's load counters exact);
 //  5. row scale, then a direct fp16 store (one range per row) or the packed
 //     fixed-point atomic (several ranges).
-template <int G, int NB, int WAVES, int PF, int RS, int TQ>
-__global__ __launch_bounds__(WAVES * 64)
-__attribute__((amdgpu_waves_per_eu(lut_waves_per_eu<G, NB, WAVES, PF, RS, TQ>())))
-void lut_gemv_kernel(const GemvArgs a) {
+//
+// KS = 2 (one batch row): the WAVES waves cover WAVES / 2 row tiles, two waves
+// per tile, each over one half of the range's chunks; the second wave's
+// row-scaled partial reaches the first through LDS, which adds it and makes
+// the row's one atomic: half the split atomics for the same waves.
+template <int G, int NB, int WAVES, int PF, int RS, int TQ, int KS>
+__device__ __forceinline__ void lut_gemv_body(const GemvArgs &a) {
+  static_assert(KS == 1 || (KS == 2 && NB == 1), "two waves per row tile with one batch row only");
   constexpr int NT = WAVES * 64;
+  constexpr int TW = WAVES / KS;           // row tiles of the workgroup
   constexpr int SUB = kChunkCols / G;      // sub-vectors per chunk
   constexpr int TAB = 1 << G;              // full table entries
   constexpr int WPL = kChunkCols / 32;     // words per lane per chunk (4)
@@ -70,24 +75,29 @@ void lut_gemv_kernel(const GemvArgs a) {
   const uint32_t tab_base = lds_addr(s_tab);  // 1024-aligned (table addresses are merged bytewise)
   float *s_v = smem + tbc * (CTB / 4);
   float *s_sink = s_v + tbc * NB * kChunkCols;
+  float *s_red = s_sink + 64;  // KS = 2: the second waves' partials, TW * 64 floats
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar address arithmetic
   const int rb = blockIdx.x;  // row block
   const int sp = blockIdx.y;  // column range
-  const int tile = rb * WAVES + wave;
+  const int wt = KS == 1 ? wave : wave % TW;  // the wave's row tile within the workgroup (uniform)
+  const int kh = KS == 1 ? 0 : wave / TW;     // and which part of the range it looks up (uniform)
+  const int tile = rb * TW + wt;
   const int ltile = min(tile, a.row_tiles - 1);  // waves past the last tile read the last one, store nothing
   const int row = tile * kTileRows + lane;
   const bool row_ok = tile < a.row_tiles && row < a.n;
   const int rrow = row_ok ? row : 0;
 
-  // The column range: segment sg, chunks [c_lo, c_lo + nch) of it.
+  // The column range: segment sg, chunks [c_lo, c_lo + nch) of it; this
+  // wave's part of it: chunks [k0, k0 + nk) of the range (all of it when KS = 1)
   const ColRange cr = column_range(a, sp);
   const SegRef S = cr.S;
   const int sg = cr.sg, c_lo = cr.c_lo, nch = cr.nch;
-  // element of this lane's 16 bytes in the range's first chunk; chunk u is 64 elements further
-  const int64_t te0 = ((int64_t)ltile * S.nchunks + c_lo) * kTileRows + lane;
+  const int k0 = KS == 1 ? 0 : kh * nch / KS, nk = KS == 1 ? nch : (kh + 1) * nch / KS - k0;
+  // element of this lane's 16 bytes in the part's first chunk; chunk u is 64 elements further
+  const int64_t te0 = ((int64_t)ltile * S.nchunks + c_lo + k0) * kTileRows + lane;
   const FB_GLOBAL u32x4 *wp = S.bits + te0;
 
   auto body = [&](auto sal_tag) {
@@ -110,7 +120,9 @@ void lut_gemv_kernel(const GemvArgs a) {
     const int sal_hi = a.sal16 ? 1 : 0;  // uniform
     int pidx = 0;                        // next chunk of the range to load
     auto load_into = [&](int u) {
-      const int ci = min(pidx, nch - 1);
+      // past the part's end its last chunk is read again (a part without
+      // chunks, KS = 2 over a 1-chunk range, reads the range's first)
+      const int ci = KS == 1 ? min(pidx, nch - 1) : min(pidx, max(nk, 1) - 1);
       wb[u] = __builtin_nontemporal_load(wp + ci * kTileRows);
       if constexpr (RS == 1 && !SAL) rg[u] = __builtin_nontemporal_load(S.r + te0 + ci * kTileRows);
       if constexpr (RS == 1 && SAL) {
@@ -311,21 +323,22 @@ void lut_gemv_kernel(const GemvArgs a) {
       asm volatile("" ::: "memory");
     };
     if constexpr (NB == 1) {
-      // one group: every chunk's tables are in LDS
+      // one group: every chunk's tables are in LDS; this wave's part is
+      // chunks [k0, k0 + nk) of the range
       int ch0 = 0;
-      for (; ch0 + D < nch; ch0 += D) {
+      for (; ch0 + D < nk; ch0 += D) {
 #pragma unroll
         for (int u = 0; u < D; ++u) {
           // consumed before the refill is issued into the same registers: with
           // both alive the compiler would rotate registers with copies that wait
-          consume(wb[u], ch0 + u, u);
+          consume(wb[u], k0 + ch0 + u, u);
           load_into(u);
           __builtin_amdgcn_sched_barrier(0);  // issue the refill here, not later
         }
       }
 #pragma unroll
       for (int u = 0; u < D; ++u)
-        if (ch0 + u < nch) consume(wb[u], ch0 + u, u);
+        if (ch0 + u < nk) consume(wb[u], k0 + ch0 + u, u);
     } else {
       for (;;) {  // uniform
         // group [g0, g0 + gn): g0 and, but for the last group, gn are multiples
@@ -368,6 +381,13 @@ void lut_gemv_kernel(const GemvArgs a) {
       for (int b = 0; b < NB; ++b) part[b] = rv * (TWO ? acc0[b] + acc1[b] : acc0[b]);
     }
 
+    if constexpr (KS == 2) {
+      // the second waves hand their row-scaled partials to the first ones
+      if (kh == 1) s_red[wt * 64 + lane] = part[0];
+      __syncthreads();
+      if (kh == 1) return;
+      part[0] += s_red[wt * 64 + lane];
+    }
     finish_rows<NB>(a, row, row_ok, part);
   };
   if (sg < a.kb) {
@@ -375,6 +395,21 @@ void lut_gemv_kernel(const GemvArgs a) {
   } else {
     body(BoolTag<true>{});
   }
+}
+
+template <int G, int NB, int WAVES, int PF, int RS, int TQ>
+__global__ __launch_bounds__(WAVES * 64)
+__attribute__((amdgpu_waves_per_eu(lut_waves_per_eu<G, NB, WAVES, PF, RS, TQ>())))
+void lut_gemv_kernel(const GemvArgs a) {
+  lut_gemv_body<G, NB, WAVES, PF, RS, TQ, 1>(a);
+}
+
+// Two waves per row tile (one batch row): WAVES / 2 row tiles.
+template <int G, int WAVES, int PF, int RS, int TQ>
+__global__ __launch_bounds__(WAVES * 64)
+__attribute__((amdgpu_waves_per_eu(lut_waves_per_eu<G, 1, WAVES, PF, RS, TQ>())))
+void lut_gemv_ks2_kernel(const GemvArgs a) {
+  lut_gemv_body<G, 1, WAVES, PF, RS, TQ, 2>(a);
 }
 
 // Instance for (batch width, waves, prefetch depth) at table width G,

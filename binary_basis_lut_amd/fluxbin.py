@@ -20,7 +20,7 @@ if not LIB_PATH.exists():
 
 _lib = ctypes.CDLL(str(LIB_PATH))
 
-ABI_VERSION = 7
+ABI_VERSION = 8
 
 OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
 LAYOUT_ROWMAJOR, LAYOUT_TILED = 0, 1
@@ -48,6 +48,7 @@ class PlanInfo(ctypes.Structure):
     _fields_ = [
         ("rows_per_block", I32), ("chunks_per_block", I32), ("row_blocks", I32), ("splits", I32),
         ("total_chunks", I32), ("lds_bytes", I32), ("grid", I64), ("banked_tables", I32), ("table_chunks", I32),
+        ("threads_per_block", I32),
     ]
 
     def as_dict(self):

@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported(fb):
 
 
 def test_abi_version_and_strings(fb):
-    assert fb.fluxbin_abi_version() == fb.ABI_VERSION == 7
+    assert fb.fluxbin_abi_version() == fb.ABI_VERSION == 8
     assert fb.fluxbin_status_string(fb.OK) == "ok"
     assert "invalid" in fb.fluxbin_status_string(fb.ERR_INVALID_ARGUMENT)
     assert fb.fluxbin_status_string(99) == "unknown status"

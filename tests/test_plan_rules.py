@@ -48,10 +48,42 @@ def plan(fb, d):
 
 
 def test_q_proj_decode_plan(fb):
-    # the measured workload: 4 waves (256 rows), 2-chunk ranges, 33 splits over 16 row blocks
+    # the measured workload: 256 rows per workgroup, two waves per row tile (512 threads), each
+    # over 2 chunks of a 4-chunk range: 17 splits over 16 row blocks
     p = plan(fb, workload_desc(fb, 2, 0))
-    assert (p["rows_per_block"], p["chunks_per_block"], p["row_blocks"], p["splits"]) == (256, 2, 16, 33)
-    assert p["total_chunks"] == 66 and p["grid"] == 528
+    assert (p["rows_per_block"], p["chunks_per_block"], p["row_blocks"], p["splits"]) == (256, 4, 16, 17)
+    assert p["total_chunks"] == 66 and p["grid"] == 272 and p["threads_per_block"] == 512
+    # an explicit range length or wave count keeps one wave per row tile
+    p = plan(fb, workload_desc(fb, 2, 0, chunks_per_block=2))
+    assert (p["rows_per_block"], p["chunks_per_block"], p["threads_per_block"]) == (256, 2, 256)
+    p = plan(fb, workload_desc(fb, 2, 0, waves_per_block=4))
+    assert (p["rows_per_block"], p["chunks_per_block"], p["threads_per_block"]) == (256, 2, 256)
+
+
+def test_two_waves_per_row_tile_only_where_ranges_would_be_two_chunks(fb):
+    # 7B up 4096 -> 11008 and down 11008 -> 4096 at one batch row take them; the 70B layers
+    # (longer ranges or 8-wave workgroups), several batch rows, fp16 entries and block-wise
+    # scales do not
+    for shape in (0, 1):
+        p = plan(fb, workload_desc(fb, 4, shape))
+        assert p["threads_per_block"] == 2 * p["rows_per_block"] == 512, shape
+        assert p["chunks_per_block"] == 4, shape
+    for shape in range(4):
+        p = plan(fb, workload_desc(fb, 5, shape))
+        assert p["threads_per_block"] == p["rows_per_block"], shape
+    assert plan(fb, workload_desc(fb, 4, 0, max_batch=2))["threads_per_block"] == 256
+    p = plan(fb, workload_desc(fb, 2, 0, table_precision=fb.TABLE_F16))
+    assert p["threads_per_block"] == p["rows_per_block"]
+    p = plan(fb, blockwise_desc(fb, 4096, 4096))
+    assert p["threads_per_block"] == p["rows_per_block"]
+    # nor layers whose one-wave plan has fewer workgroups than the chip has CUs: 512 x 512 keeps
+    # 2 x 4 workgroups of 256 threads, 1100 x 4096 its 5 x 33 (a 2100-row layer, 9 x 33, does not)
+    p = plan(fb, workload_desc(fb, 1, 0))
+    assert (p["grid"], p["threads_per_block"], p["chunks_per_block"]) == (8, 256, 2)
+    p = plan(fb, desc_for(fb, 1100, 4096, 2, 1, 100))
+    assert (p["grid"], p["threads_per_block"]) == (165, 256)
+    p = plan(fb, desc_for(fb, 2100, 4096, 2, 1, 100))
+    assert (p["grid"], p["threads_per_block"]) == (153, 512)
 
 
 def test_tall_layer_takes_eight_waves_and_eight_chunk_ranges(fb):
@@ -117,9 +149,10 @@ def test_explicit_choices_override_the_rules(fb):
 
 
 def test_range_length_counts_batch_rows(fb):
-    # up 4096 -> 11008: 2 chunks at one batch row, 4 at two and four (a group of nb rows
-    # counts nb times); the LDS caps four-row ranges at 4 chunks
-    assert plan(fb, workload_desc(fb, 4, 0))["chunks_per_block"] == 2
+    # up 4096 -> 11008: 2 chunks per wave at one batch row (two waves over each 4-chunk range),
+    # 4 at two and four (a group of nb rows counts nb times); the LDS caps four-row ranges at 4
+    p = plan(fb, workload_desc(fb, 4, 0))
+    assert p["chunks_per_block"] == 4 and p["threads_per_block"] == 2 * p["rows_per_block"]
     assert plan(fb, workload_desc(fb, 4, 0, max_batch=2))["chunks_per_block"] == 4
     p = plan(fb, workload_desc(fb, 4, 0, max_batch=4))
     assert p["chunks_per_block"] == 4 and p["splits"] == 17
