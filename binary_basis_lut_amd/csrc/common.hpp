@@ -226,9 +226,9 @@ gemv_fn gemv_pick_g4_rs0_t16(int nb, int waves, int pf);
 gemv_fn gemv_pick_g4_rs1_t16(int nb, int waves, int pf);
 gemv_fn gemv_pick_g8_rs0_t16(int nb, int waves, int pf);
 gemv_fn gemv_pick_g8_rs1_t16(int nb, int waves, int pf);
-// g = 4, one batch row, per-row scales, fp32 entries, two waves per row tile
-// (KS = 2): the instance for waves per workgroup and prefetch depth pf.
-gemv_fn gemv_pick_g4_ks2(int waves, int pf);
+// g = 4, one batch row, per-row scales, fp32 entries, ks (2 or 4) waves per
+// row tile: the instance for waves per workgroup and prefetch depth pf.
+gemv_fn gemv_pick_g4_ks(int ks, int waves, int pf);
 // The g = 8 kernel with bank-private tables (one batch row, per-row scales,
 // fp32 entries) for column ranges of up to `regions` (1, or 2 for region 2)
 // regions of `region` (2 or 4) chunks.

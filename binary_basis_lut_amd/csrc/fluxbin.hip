@@ -213,22 +213,28 @@ fluxbin_status make_plan(const fluxbin_layer_desc *d, Plan *p) {
                    : bank_ok           ? banked_cpb(d, p->row_tiles)
                                        : auto_cpb(p->nb, grouped_ok && d->g == 4 ? kMaxCpb : cmax, p->waves, p->row_tiles,
                                               p->total_chunks, wide ? kTargetBlocks / 2 : kTargetBlocks);
-  // Two waves per row tile where one wave per tile would take 2-chunk ranges
-  // over more workgroups than the chip has CUs (g = 4, one batch row, per-row
-  // scales, fp32 entries, 4-wave layers, automatic plan): 8-wave workgroups of
-  // 256 rows over 4-chunk ranges, each wave over two of their chunks, half the
-  // ranges and so half the split atomics for the same waves.  Measured on
-  // MI355X (256 resident weight sets, one graph, interleaved), one / two
-  // waves per tile: q_proj 5.13 / 5.01 us, the 7B 11008 -> 4096 projection at
-  // one batch row 7.65 / 6.55, 4096 -> 11008 6.53 / 6.50; slower where the
-  // one-wave plan has few workgroups (512 x 512: 3.50 / 3.86, 8 workgroups)
-  // or longer ranges (the 70B qkv 8.67 / 9.45, gate+up 26.3 / 29.4).
+  // Several waves per row tile where one wave per tile would take 2-chunk
+  // ranges over more workgroups than the chip has CUs (g = 4, one batch row,
+  // per-row scales, fp32 entries, 4-wave layers, automatic plan): 8-wave
+  // workgroups whose ks waves per tile each look up 2 chunks of a 2 ks-chunk
+  // range, so 1 / ks of the ranges, and so of the split atomics, for the same
+  // waves.  Two waves per tile (256 rows, 4-chunk ranges); four (128 rows,
+  // 8-chunk ranges) where the two-wave grid is a single round (at most two
+  // workgroups per CU) and the four-wave one still has a workgroup for every
+  // CU.  Measured on MI355X (256 resident weight sets, one graph, the
+  // libraries interleaved), one / two / four waves per tile: q_proj 5.13 /
+  // 5.02 / 4.92 us, the 7B 11008 -> 4096 projection at one batch row 7.65 /
+  // 6.47 / 6.50, 4096 -> 11008 6.53 / 6.45 / 6.54; slower where the one-wave
+  // plan has few workgroups (512 x 512: 3.50 / 3.86 with two, 8 workgroups)
+  // or longer ranges (with two: the 70B qkv 8.67 / 9.45, gate+up 26.3 / 29.4).
   if (!d->chunks_per_block && !d->waves_per_block && d->g == 4 && p->nb == 1 && !d->row_group &&
-      entry_bytes(d) == 4 && p->waves == 4 && target == 2 && cmax >= 4 &&
+      entry_bytes(d) == 4 && p->waves == 4 && target == 2 && cmax >= 8 &&
       cdiv(p->row_tiles, 4) * cdiv(p->total_chunks, 2) > kCus) {
-    p->ks = 2;
+    const bool four = cdiv(p->row_tiles, 4) * cdiv(p->total_chunks, 4) <= 2 * kCus &&
+                      cdiv(p->row_tiles, 2) * cdiv(p->total_chunks, 8) >= kCus;
+    p->ks = four ? 4 : 2;
     p->waves = 8;
-    target = 4;
+    target = 2 * p->ks;
   }
   const int32_t nc_g = (int32_t)cdiv(d->k, kChunkCols), nc_s = d->ks > 0 ? (int32_t)cdiv(d->s, kChunkCols) : 0;
   for (;;) {
@@ -287,7 +293,7 @@ fluxbin_status make_plan(const fluxbin_layer_desc *d, Plan *p) {
   if (p->banked == 4 && !d->waves_per_block) p->waves = 16;
   p->row_blocks = (int32_t)cdiv(p->row_tiles, p->waves / p->ks);
   p->lds = p->banked ? banked_lds_bytes(p->banked, p->bregions) : lds_bytes(d->g, p->nb, p->tb, entry_bytes(d));
-  if (p->ks == 2) p->lds += (p->waves / 2) * kTileRows * 4;  // the second waves' partials
+  if (p->ks > 1) p->lds += (p->ks - 1) * (p->waves / p->ks) * kTileRows * 4;  // the other waves' partials
   p->acc_bytes = p->splits > 1 ? (size_t)d->max_batch * p->n_pad * sizeof(uint64_t) : 0;
   return FLUXBIN_OK;
 }
@@ -814,7 +820,7 @@ fluxbin_status fluxbin_create(const fluxbin_layer_desc *d, fluxbin_handle *out) 
     hipError_t e = hipDeviceSynchronize();
     if (e != hipSuccess) return hip_fail(e, "synchronising after create");
   }
-  gemv_fn fn = p.ks == 2 ? gemv_pick_g4_ks2(p.waves, p.pf)
+  gemv_fn fn = p.ks > 1 ? gemv_pick_g4_ks(p.ks, p.waves, p.pf)
                : p.banked ? gemv_pick_g8_banked(p.banked, p.bregions, p.waves)
                         : pick_gemv(d->g, d->row_group ? 1 : 0, d->table_precision, p.nb, p.waves, p.pf);
   if (!fn) return fail(FLUXBIN_ERR_UNSUPPORTED, "no kernel for g = %d, batch width %d, %d waves", d->g, p.nb, p.waves);

@@ -49,13 +49,14 @@ constexpr int lut_waves_per_eu() {
 //  5. row scale, then a direct fp16 store (one range per row) or the packed
 //     fixed-point atomic (several ranges).
 //
-// KS = 2 (one batch row): the WAVES waves cover WAVES / 2 row tiles, two waves
-// per tile, each over one half of the range's chunks; the second wave's
-// row-scaled partial reaches the first through LDS, which adds it and makes
-// the row's one atomic: half the split atomics for the same waves.
+// KS = 2 or 4 (one batch row): the WAVES waves cover WAVES / KS row tiles, KS
+// waves per tile, each over one KS-th of the range's chunks; the other waves'
+// row-scaled partials reach the first through LDS, which adds them in wave
+// order and makes the row's one atomic: 1 / KS of the split atomics for the
+// same waves.
 template <int G, int NB, int WAVES, int PF, int RS, int TQ, int KS>
 __device__ __forceinline__ void lut_gemv_body(const GemvArgs &a) {
-  static_assert(KS == 1 || (KS == 2 && NB == 1), "two waves per row tile with one batch row only");
+  static_assert(KS == 1 || ((KS == 2 || KS == 4) && NB == 1), "several waves per row tile with one batch row only");
   constexpr int NT = WAVES * 64;
   constexpr int TW = WAVES / KS;           // row tiles of the workgroup
   constexpr int SUB = kChunkCols / G;      // sub-vectors per chunk
@@ -75,7 +76,7 @@ __device__ __forceinline__ void lut_gemv_body(const GemvArgs &a) {
   const uint32_t tab_base = lds_addr(s_tab);  // 1024-aligned (table addresses are merged bytewise)
   float *s_v = smem + tbc * (CTB / 4);
   float *s_sink = s_v + tbc * NB * kChunkCols;
-  float *s_red = s_sink + 64;  // KS = 2: the second waves' partials, TW * 64 floats
+  float *s_red = s_sink + 64;  // KS > 1: the other waves' partials, (KS - 1) * TW * 64 floats
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -121,7 +122,7 @@ __device__ __forceinline__ void lut_gemv_body(const GemvArgs &a) {
     int pidx = 0;                        // next chunk of the range to load
     auto load_into = [&](int u) {
       // past the part's end its last chunk is read again (a part without
-      // chunks, KS = 2 over a 1-chunk range, reads the range's first)
+      // chunks, KS > 1 over a range shorter than KS chunks, reads the range's first)
       const int ci = KS == 1 ? min(pidx, nch - 1) : min(pidx, max(nk, 1) - 1);
       wb[u] = __builtin_nontemporal_load(wp + ci * kTileRows);
       if constexpr (RS == 1 && !SAL) rg[u] = __builtin_nontemporal_load(S.r + te0 + ci * kTileRows);
@@ -381,12 +382,13 @@ __device__ __forceinline__ void lut_gemv_body(const GemvArgs &a) {
       for (int b = 0; b < NB; ++b) part[b] = rv * (TWO ? acc0[b] + acc1[b] : acc0[b]);
     }
 
-    if constexpr (KS == 2) {
-      // the second waves hand their row-scaled partials to the first ones
-      if (kh == 1) s_red[wt * 64 + lane] = part[0];
+    if constexpr (KS > 1) {
+      // the other waves of the tile hand their row-scaled partials to the first
+      if (kh > 0) s_red[((kh - 1) * TW + wt) * 64 + lane] = part[0];
       __syncthreads();
-      if (kh == 1) return;
-      part[0] += s_red[wt * 64 + lane];
+      if (kh > 0) return;
+#pragma unroll
+      for (int h = 1; h < KS; ++h) part[0] += s_red[((h - 1) * TW + wt) * 64 + lane];
     }
     finish_rows<NB>(a, row, row_ok, part);
   };
@@ -410,6 +412,14 @@ __global__ __launch_bounds__(WAVES * 64)
 __attribute__((amdgpu_waves_per_eu(lut_waves_per_eu<G, 1, WAVES, PF, RS, TQ>())))
 void lut_gemv_ks2_kernel(const GemvArgs a) {
   lut_gemv_body<G, 1, WAVES, PF, RS, TQ, 2>(a);
+}
+
+// Four waves per row tile (one batch row): WAVES / 4 row tiles.
+template <int G, int WAVES, int PF, int RS, int TQ>
+__global__ __launch_bounds__(WAVES * 64)
+__attribute__((amdgpu_waves_per_eu(lut_waves_per_eu<G, 1, WAVES, PF, RS, TQ>())))
+void lut_gemv_ks4_kernel(const GemvArgs a) {
+  lut_gemv_body<G, 1, WAVES, PF, RS, TQ, 4>(a);
 }
 
 // Instance for (batch width, waves, prefetch depth) at table width G,

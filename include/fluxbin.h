@@ -175,9 +175,9 @@ typedef struct {
   int32_t table_chunks;     /* chunks whose tables a workgroup holds in LDS at once: chunks_per_block, or
                                fewer (several batch rows; two-region banked ranges), the tables then built
                                in groups of this many chunks in turn while the range's sign words stream */
-  int32_t threads_per_block; /* threads of one workgroup: 64 per row tile of rows_per_block, or 128 where two
-                               waves share each row tile, each over one half of the column range (g = 4, one
-                               batch row, layers whose ranges would otherwise be 2 chunks long) */
+  int32_t threads_per_block; /* threads of one workgroup: 64 per row tile of rows_per_block, or 128 / 256 where
+                               two / four waves share each row tile, each over one part of the column range
+                               (g = 4, one batch row, layers whose ranges would otherwise be 2 chunks long) */
 } fluxbin_plan;
 
 int32_t fluxbin_abi_version(void);

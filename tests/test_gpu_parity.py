@@ -332,35 +332,38 @@ def test_gemv_edge_cases(fb, orc, g, n, k, kb, ks, s, batch, cpb, waves):
     dl.close()
 
 
-# Two waves per row tile (g = 4, one batch row, automatic plan of a layer whose ranges would be 2
-# chunks long over more than 256 workgroups): each wave of a pair takes one half of a 4-chunk range
-# and the second hands its partial to the first through LDS.  q_proj and the 7B up and down shapes;
-# rows that fill neither the last tile nor the last row block (2100: one tile of the last block,
-# 4097: one row of it); 1-chunk salient ranges (the first wave of each pair looks up nothing), 2-
-# and 3-chunk ones (1 + 1, 1 + 2); global segments cut into ranges of 3 and 4, a last chunk of 104
-# columns (k = 1000) or of one (k = 129, whose 2-chunk segments make 1 + 1 ranges throughout);
-# three and four global and two salient bases.  Dyadic inputs must give RNE(exact) bitwise; random
-# ones the rounding bound.
-TWO_WAVE = [
-    # n, k, kb, ks, s
-    (4096, 4096, 2, 1, 256),
-    (2100, 4096, 2, 1, 100),
-    (9000, 1000, 2, 1, 300),
-    (4096, 11008, 2, 1, 224),
-    (11008, 4096, 2, 1, 96),
-    (4097, 11008, 2, 1, 224),
-    (3000, 4096, 3, 2, 300),
-    (16000, 129, 4, 2, 100),
+# Two or four waves per row tile (g = 4, one batch row, automatic plan of a layer whose ranges
+# would be 2 chunks long over more than 256 workgroups): each wave of a tile takes one part of a
+# 4- or 8-chunk range and the others hand their partials to the first through LDS.  q_proj and
+# the 7B up and down shapes; rows that fill neither the last tile nor the last row block (2100:
+# one tile of the last block, 4097: one row of it); 1-chunk salient ranges (all but one wave of a
+# tile look up nothing), 2- and 3-chunk ones (1 + 1, 1 + 2; at four waves 0 + 1 + 1 + 1); global
+# segments cut into ranges of 3 and 4, a last chunk of 104 columns (k = 1000), of 32 (k = 4000) or
+# of one (k = 129, whose 2-chunk segments make 1 + 1 ranges throughout); three and four global and
+# two salient bases.  Dyadic inputs must give RNE(exact) bitwise; random ones the rounding bound.
+SEVERAL_WAVES = [
+    # n, k, kb, ks, s, waves per row tile
+    (4096, 4096, 2, 1, 256, 4),
+    (4097, 4096, 2, 1, 256, 4),
+    (4000, 4000, 2, 1, 100, 4),
+    (3000, 4096, 3, 2, 300, 4),
+    (5000, 3000, 3, 2, 300, 4),
+    (2100, 4096, 2, 1, 100, 2),
+    (9000, 1000, 2, 1, 300, 2),
+    (4096, 11008, 2, 1, 224, 2),
+    (11008, 4096, 2, 1, 96, 2),
+    (4097, 11008, 2, 1, 224, 2),
+    (16000, 129, 4, 2, 100, 2),
 ]
 
 
-@pytest.mark.parametrize("n,k,kb,ks,s", TWO_WAVE)
-def test_two_waves_per_row_tile(fb, orc, n, k, kb, ks, s):
-    note(f"two waves per tile n={n} k={k} kb={kb} ks={ks} s={s}")
+@pytest.mark.parametrize("n,k,kb,ks,s,wpt", SEVERAL_WAVES)
+def test_several_waves_per_row_tile(fb, orc, n, k, kb, ks, s, wpt):
+    note(f"{wpt} waves per tile n={n} k={k} kb={kb} ks={ks} s={s}")
     layer = I.dyadic_layer(n, k, kb, ks, 4, s, seed=n + k + 7)
     x = I.dyadic_x(k, 1, seed=k + 7)
     dl = fb.DeviceLayer(layer, max_batch=1)
-    assert dl.plan["threads_per_block"] == 2 * dl.plan["rows_per_block"] == 512, dl.plan
+    assert dl.plan["threads_per_block"] == wpt * dl.plan["rows_per_block"] == 512, dl.plan
     y16 = gemv(fb, dl, x)
     y_ref, _ = orc.gemv_dense(layer, x)
     assert np.array_equal(y16, orc.double_to_half(y_ref)), "y differs from RNE(exact)"
@@ -368,7 +371,7 @@ def test_two_waves_per_row_tile(fb, orc, n, k, kb, ks, s):
     layer = I.make_layer(n, k, kb, ks, 4, s=s if ks else None, outlier_frac=0.01, seed=(65, n, k))
     x = I.make_x(layer, 1, seed=(65, n, k))
     dl = fb.DeviceLayer(layer, max_batch=1)
-    assert dl.plan["threads_per_block"] == 512
+    assert dl.plan["threads_per_block"] == wpt * dl.plan["rows_per_block"]
     y16 = gemv(fb, dl, x)
     rows = None if n <= 4096 else I.stream(65, n).choice(n, 1024, replace=False)
     check_y(orc, layer, x, y16, dl.plan, rows=rows)

@@ -48,11 +48,11 @@ def plan(fb, d):
 
 
 def test_q_proj_decode_plan(fb):
-    # the measured workload: 256 rows per workgroup, two waves per row tile (512 threads), each
-    # over 2 chunks of a 4-chunk range: 17 splits over 16 row blocks
+    # the measured workload: 128 rows per workgroup, four waves per row tile (512 threads), each
+    # over 2 chunks of an 8-chunk range: 9 splits over 32 row blocks
     p = plan(fb, workload_desc(fb, 2, 0))
-    assert (p["rows_per_block"], p["chunks_per_block"], p["row_blocks"], p["splits"]) == (256, 4, 16, 17)
-    assert p["total_chunks"] == 66 and p["grid"] == 272 and p["threads_per_block"] == 512
+    assert (p["rows_per_block"], p["chunks_per_block"], p["row_blocks"], p["splits"]) == (128, 8, 32, 9)
+    assert p["total_chunks"] == 66 and p["grid"] == 288 and p["threads_per_block"] == 512
     # an explicit range length or wave count keeps one wave per row tile
     p = plan(fb, workload_desc(fb, 2, 0, chunks_per_block=2))
     assert (p["rows_per_block"], p["chunks_per_block"], p["threads_per_block"]) == (256, 2, 256)
@@ -60,7 +60,7 @@ def test_q_proj_decode_plan(fb):
     assert (p["rows_per_block"], p["chunks_per_block"], p["threads_per_block"]) == (256, 2, 256)
 
 
-def test_two_waves_per_row_tile_only_where_ranges_would_be_two_chunks(fb):
+def test_several_waves_per_row_tile_only_where_ranges_would_be_two_chunks(fb):
     # 7B up 4096 -> 11008 and down 11008 -> 4096 at one batch row take them; the 70B layers
     # (longer ranges or 8-wave workgroups), several batch rows, fp16 entries and block-wise
     # scales do not
@@ -84,6 +84,21 @@ def test_two_waves_per_row_tile_only_where_ranges_would_be_two_chunks(fb):
     assert (p["grid"], p["threads_per_block"]) == (165, 256)
     p = plan(fb, desc_for(fb, 2100, 4096, 2, 1, 100))
     assert (p["grid"], p["threads_per_block"]) == (153, 512)
+
+
+def test_four_waves_per_row_tile_where_two_would_be_one_round(fb):
+    # four waves per tile where the two-wave grid has at most 512 workgroups and the four-wave one
+    # at least 256: q_proj (272 -> 288), 4000 x 4000; the 7B up and down shapes (731, 720
+    # workgroups at two) and 2100 x 4096 (153 at four) keep two
+    for d, four in ((workload_desc(fb, 2, 0), True), (desc_for(fb, 4000, 4000, 2, 1, 100), True),
+                    (workload_desc(fb, 4, 0), False), (workload_desc(fb, 4, 1), False),
+                    (desc_for(fb, 2100, 4096, 2, 1, 100), False)):
+        p = plan(fb, d)
+        assert p["threads_per_block"] == (4 if four else 2) * p["rows_per_block"], (d.n, d.k)
+        assert p["chunks_per_block"] <= (8 if four else 4)
+    # the LDS holds the partials of the three other waves of each of the two tiles
+    p = plan(fb, workload_desc(fb, 2, 0))
+    assert p["lds_bytes"] == 8 * (32 * 16 * 4 + 128 * 4) + 256 + 3 * 2 * 64 * 4
 
 
 def test_tall_layer_takes_eight_waves_and_eight_chunk_ranges(fb):
