@@ -249,6 +249,17 @@ def banked_lookup_rate(torch, F, region, iters=400, reps=3):
     return wgs * 512 * iters * 16 * region * reps / sec
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(O, model, ys_gpu, budget_s: float):
     """The fp64 oracle, as it is, on the host cores: layer 0's four GEMVs, repeated for ~budget_s.
 
@@ -271,6 +282,12 @@ def cpu_baseline(O, model, ys_gpu, budget_s: float):
             break
     per_layer = el / calls
     wb = sum(model.bytes)
+    # one thread, for the scaling: one call of the smallest shape (the o projection)
+    so = min(range(len(model.layer0)), key=lambda i: model.bytes[i])
+    t1 = time.perf_counter()
+    O.gemv_dense(model.layer0[so], model.x0[so], nthreads=1)
+    t1 = time.perf_counter() - t1
+    lo = model.layer0[so]
     return {
         "value": round(wb / per_layer / 1e9, 4),
         "unit": "GB/s",
@@ -280,6 +297,9 @@ def cpu_baseline(O, model, ys_gpu, budget_s: float):
                   f"1 salient bases; fp64 dense reconstruction row by row, OpenMP over rows), {el:.1f} s: "
                   f"{per_layer * 1e3:.0f} ms per layer; the 80-layer stream would take {80 * per_layer:.0f} s "
                   f"(x80 extrapolated)",
+        "cpu_model": cpu_model(),
+        "single_thread": {"value": round(model.bytes[so] / t1 / 1e9, 4), "unit": "GB/s", "cores": 1,
+                          "sample": f"one {lo.k}->{lo.n} GEMV of layer 0 on one thread, {t1 * 1e3:.0f} ms"},
     }, {"parity_layer0_ok": ok, "parity_layer0_worst_err_over_tol": worst, "rows": "every 7th row of each shape"}
 
 

@@ -11,7 +11,7 @@ folders of the rocprofv3 runs each summary names:
   python3 -m binary_basis_lut_amd.rocprof_summary trace DIR --by-grid
       the same from the dispatch trace, one row per kernel and grid (so
       that launches of one instance on different layer shapes stay apart),
-      with the median besides the average;
+      with the median, 10th and 90th percentiles besides the average;
 
   python3 -m binary_basis_lut_amd.rocprof_summary pmc DIR --kernel REGEX
       the counters of a `--pmc ... --output-format csv` run for the dispatches
@@ -95,17 +95,27 @@ def trace_by_grid(d: str):
         for r in csv.DictReader(f):
             key = (r["Kernel_Name"], int(r["Grid_Size_X"]), int(r["Grid_Size_Y"]), int(r["Workgroup_Size_X"]))
             groups[key].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
-    return [(k, len(v), statistics.mean(v), statistics.median(v), min(v), max(v)) for k, v in groups.items()]
+    return [(k, len(v), statistics.mean(v), statistics.median(v), percentile(v, 10), percentile(v, 90), min(v), max(v))
+            for k, v in groups.items()]
+
+
+def percentile(v, q: float) -> float:
+    """The q-th percentile of v, linear between the closest ranks (numpy's default)."""
+    s = sorted(v)
+    pos = (len(s) - 1) * q / 100.0
+    lo = int(pos)
+    hi = min(lo + 1, len(s) - 1)
+    return s[lo] + (s[hi] - s[lo]) * (pos - lo)
 
 
 def cmd_trace(a) -> None:
     if a.by_grid:
-        print("| kernel | grid (workgroups) | calls | average ns | median ns | min ns | max ns |")
-        print("|---|---|---|---|---|---|---|")
-        for (name, gx, gy, wg), calls, avg, med, mn, mx in sorted(trace_by_grid(a.dir)):
+        print("| kernel | grid (workgroups) | calls | average ns | median ns | p10 ns | p90 ns | min ns | max ns |")
+        print("|---|---|---|---|---|---|---|---|---|")
+        for (name, gx, gy, wg), calls, avg, med, p10, p90, mn, mx in sorted(trace_by_grid(a.dir)):
             if a.kernel and not re.search(a.kernel, name):
                 continue
-            print(f"| {name} | {gx // wg} x {gy} | {calls} | {avg:.0f} | {med:.0f} | {mn} | {mx} |")
+            print(f"| {name} | {gx // wg} x {gy} | {calls} | {avg:.0f} | {med:.0f} | {p10:.0f} | {p90:.0f} | {mn} | {mx} |")
         return
     print("| kernel | calls | average ns | min ns | max ns |")
     print("|---|---|---|---|---|")

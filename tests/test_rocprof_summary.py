@@ -74,9 +74,13 @@ def test_trace_by_grid_keeps_the_shapes_apart(tmp_path, capsys, monkeypatch):
     lines = [hdr] + [f'"KERNEL_DISPATCH","Agent 1",1,0,1,{i},1,"{n}",{i},{s},{e},0,0,60,0,40,512,1,1,{gx * 512},{gy},1\n'
                      for i, (n, s, e, gx, gy) in enumerate(rows)]
     (d / "b_kernel_trace.csv").write_text("".join(lines))
-    out = {(key[1] // key[3], key[2]): (calls, avg, med) for key, calls, avg, med, mn, mx in RS.trace_by_grid(str(d))}
-    assert out == {(112, 17): (3, 50, 30), (16, 57): (1, 10, 10)}
+    out = {(key[1] // key[3], key[2]): (calls, avg, med, p10, p90)
+           for key, calls, avg, med, p10, p90, mn, mx in RS.trace_by_grid(str(d))}
+    # durations 30, 20, 100: percentiles linear between closest ranks (numpy's default): 22 and 86
+    assert out == {(112, 17): (3, 50, 30, 22, 86), (16, 57): (1, 10, 10, 10, 10)}
+    assert [RS.percentile([20, 30, 100], q) for q in (0, 10, 50, 90, 100)] == [20, 22, 30, 86, 100]
     monkeypatch.setattr(sys, "argv", ["x", "trace", str(d), "--by-grid", "--kernel", "lut_gemv"])
     assert RS.main() == 0
     text = capsys.readouterr().out
-    assert "| 112 x 17 | 3 | 50 | 30 | 20 | 100 |" in text and "| 16 x 57 | 1 | 10 | 10 | 10 | 10 |" in text
+    assert "| 112 x 17 | 3 | 50 | 30 | 22 | 86 | 20 | 100 |" in text
+    assert "| 16 x 57 | 1 | 10 | 10 | 10 | 10 | 10 | 10 |" in text
