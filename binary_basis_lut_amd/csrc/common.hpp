@@ -278,6 +278,18 @@ __device__ __forceinline__ float add_f16_bits(float acc, uint32_t h) {
   return r;
 }
 
+// acc + (the fp16 value in the high half of h): the same instruction reading
+// the upper half (op_sel).
+__device__ __forceinline__ float add_f16_hi_bits(float acc, uint32_t h) {
+  float r;
+  asm("v_fma_mix_f32 %0, %1, 1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(h), "v"(acc));
+  return r;
+}
+
+__device__ __forceinline__ uint32_t lds_u32(uint32_t addr) {
+  return *reinterpret_cast<const FB_LDS uint32_t *>((uintptr_t)addr);
+}
+
 // Table entries of EB bytes: 4 = fp32, 2 = fp16 (quantised tables).
 template <int EB>
 __device__ __forceinline__ float add_entry(float acc, uint32_t addr) {
@@ -318,6 +330,12 @@ __device__ __forceinline__ uint32_t byte_pattern(uint32_t w) {
   }
 }
 
+// fp16 tables of several batch rows at g = 4, in batch-row pairs: in a
+// chunk's table block, dword ((q * 32 + j) * 16 + p) holds entry p of
+// sub-vector j for batch row 2q (low half) and row 2q + 1 (high half); the
+// block has the size of the unpaired fp16 tables.
+__host__ __device__ constexpr int pair_table_dword(int q, int j, int p) { return (q * 32 + j) * 16 + p; }
+
 // Accumulate the lookups of one 32-bit word (32 columns) of one row.  `base`
 // is the LDS byte address of the chunk's table block (a multiple of 256, or of
 // 1024 for 256-entry tables, below 2^24); j0 is the first sub-vector of the
@@ -326,12 +344,36 @@ __device__ __forceinline__ uint32_t byte_pattern(uint32_t w) {
 // and 2) go to acc0, odd ones to acc1: two independent chains of fp32 adds,
 // or one when the caller passes the same array twice (wide batches, whose NB
 // rows already give independent chains).
-template <int G, int NB, int EB>
+template <int G, int NB, int EB, bool PAIRS = false>
 __device__ __forceinline__ void lookup_word(uint32_t w, uint32_t base, float (&acc0)[NB], float (&acc1)[NB],
                                             int j0) {
   constexpr int SUB = kChunkCols / G;
   constexpr int TAB = 1 << G;
-  if constexpr (G == 4) {
+  if constexpr (PAIRS) {
+    // fp16 tables in batch-row pairs (pair_table_dword): one dword read gives
+    // the entries of rows 2q (low half) and 2q + 1 (high half), so a lookup
+    // returns 2 bytes of LDS data per batch row instead of 4.  Each row still
+    // adds its even sub-vector's entry, then its odd one's, as above.
+    static_assert(G == 4 && EB == 2 && NB % 2 == 0, "pairs: g = 4, fp16 entries, an even batch width");
+    const uint32_t A = nibbles_even<4>(w);
+    const uint32_t B = nibbles_odd<4>(w);
+    const uint32_t ia[4] = {addr_of<0>(A, base), addr_of<1>(A, base), addr_of<2>(A, base), addr_of<3>(A, base)};
+    const uint32_t ib[4] = {addr_of<0>(B, base), addr_of<1>(B, base), addr_of<2>(B, base), addr_of<3>(B, base)};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+      for (int q = 0; q < NB / 2; ++q) {
+        const int off0 = ((q * SUB + j0 + 2 * kk) * TAB) * 4;
+        const uint32_t e = lds_u32(ia[kk] + off0);
+        const uint32_t f = lds_u32(ib[kk] + off0 + TAB * 4);
+        acc0[2 * q] = add_f16_bits(acc0[2 * q], e);
+        acc0[2 * q + 1] = add_f16_hi_bits(acc0[2 * q + 1], e);
+        acc1[2 * q] = add_f16_bits(acc1[2 * q], f);
+        acc1[2 * q + 1] = add_f16_hi_bits(acc1[2 * q + 1], f);
+      }
+      if constexpr (NB >= 8) asm volatile("" ::: "memory");
+    }
+  } else if constexpr (G == 4) {
     const uint32_t A = nibbles_even<EB>(w);
     const uint32_t B = nibbles_odd<EB>(w);
     const uint32_t ia[4] = {addr_of<0>(A, base), addr_of<1>(A, base), addr_of<2>(A, base), addr_of<3>(A, base)};

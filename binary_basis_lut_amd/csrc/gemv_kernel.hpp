@@ -66,6 +66,9 @@ __device__ __forceinline__ void lut_gemv_body(const GemvArgs &a) {
   constexpr int CTB = NB * SUB * TAB * EB; // table bytes of one chunk (all batch rows)
   constexpr int VPT = stage_items(NB, WAVES);
   constexpr bool TWO = NB == 1;            // two add chains in the lookups of a single batch row
+  // fp16 tables of several batch rows at g = 4 (per-row scales): batch-row
+  // pairs share each table dword (pair_table_dword), one LDS read per pair
+  constexpr bool PAIRS = G == 4 && TQ == 1 && NB % 2 == 0 && RS == 0;
   static_assert(CTB % 256 == 0 && (G == 4 || CTB % 1024 == 0), "chunk table blocks must stay aligned");
   static_assert(PF >= 1 && PF <= 8, "prefetch depth");
   static_assert(kChunkCols % 64 == 0 && NT % 64 == 0, "a wave's staged items must share chunk and batch row");
@@ -225,22 +228,55 @@ __device__ __forceinline__ void lut_gemv_body(const GemvArgs &a) {
     // entries round exactly like that sequence; the half with the top bit
     // clear is built from -v_{G-1} and is therefore the exact negation of
     // the other half (LUT[~p] = -LUT[p]).  The g = 8 unit is g8_unit_entries.
+    // g = 4 build unit un of the sub-vector whose products start at v: unit
+    // 1 gives entries 8..15, unit 0 entries 0..7
+    auto g4_unit = [](const float *v, int un, float (&e)[8]) {
+      const float4 vv = *reinterpret_cast<const float4 *>(v);
+      const float top = un ? vv.w : -vv.w;
+      const float l1[2] = {top - vv.x, top + vv.x};
+      float l2[4];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) l2[i] = l1[i] - vv.y, l2[i + 2] = l1[i] + vv.y;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) e[i] = l2[i] - vv.z, e[i + 4] = l2[i] + vv.z;
+    };
     auto build_tables = [&]() {
       constexpr int UPS = G == 4 ? 2 : 16;  // build units per sub-vector
+      if constexpr (PAIRS) {
+        // a unit builds one half of one sub-vector's entries for both rows of
+        // a batch-row pair and stores them as 8 shared dwords
+        const int units = gn * (NB / 2) * SUB * UPS;
+        for (int t = tid; t < units; t += NT) {
+          const int pu = t / UPS;  // (chunk * NB / 2 + pair) * SUB + sub-vector
+          const int un = t - pu * UPS;
+          const int j = pu % SUB;
+          const int q = (pu / SUB) % (NB / 2);
+          const int ch = pu / (SUB * (NB / 2));
+          const int sv0 = (ch * NB + 2 * q) * SUB + j;
+          float e0[8], e1[8];
+          g4_unit(s_v + sv0 * G, un, e0);
+          g4_unit(s_v + (sv0 + SUB) * G, un, e1);
+          u32x4 h0, h1;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            h0[i] = (uint32_t)f2h(e0[i]) | ((uint32_t)f2h(e1[i]) << 16);
+            h1[i] = (uint32_t)f2h(e0[i + 4]) | ((uint32_t)f2h(e1[i + 4]) << 16);
+          }
+          u32x4 *tb = reinterpret_cast<u32x4 *>(reinterpret_cast<uint32_t *>(s_tab) + ch * (CTB / 4) +
+                                                pair_table_dword(q, j, un * 8));
+          tb[0] = h0;
+          tb[1] = h1;
+        }
+        return;
+      }
       const int units = gn * NB * SUB * UPS;
       for (int t = tid; t < units; t += NT) {
         const int sv = t / UPS;  // (chunk * NB + batch row) * SUB + sub-vector
         const int un = t - sv * UPS;
         const float *v = s_v + sv * G;
         if constexpr (G == 4) {
-          const float4 vv = *reinterpret_cast<const float4 *>(v);
-          const float top = un ? vv.w : -vv.w;  // unit 1: entries 8..15, unit 0: entries 0..7
-          const float l1[2] = {top - vv.x, top + vv.x};
-          float l2[4], e[8];
-#pragma unroll
-          for (int i = 0; i < 2; ++i) l2[i] = l1[i] - vv.y, l2[i + 2] = l1[i] + vv.y;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) e[i] = l2[i] - vv.z, e[i + 4] = l2[i] + vv.z;
+          float e[8];
+          g4_unit(v, un, e);
           if constexpr (TQ == 0) {
             float4 *tb = reinterpret_cast<float4 *>(s_tab + sv * TAB + un * 8);
             tb[0] = make_float4(e[0], e[1], e[2], e[3]);
@@ -306,7 +342,7 @@ __device__ __forceinline__ void lut_gemv_body(const GemvArgs &a) {
       } else {
 #pragma unroll
         for (int q = 0; q < WPL; ++q) {
-          lookup_word<G, NB, EB>(w[q], base, acc0, accb, q * (32 / G));
+          lookup_word<G, NB, EB, PAIRS>(w[q], base, acc0, accb, q * (32 / G));
           // wider batches: one word's table reads at a time
           if constexpr (NB >= 4) asm volatile("" ::: "memory");
         }
