@@ -59,6 +59,10 @@ EXACT = [
     # g, n, k, kb, ks, s, batch, blockwise sal_group (0: per-row)
     (4, 300, 1000, 2, 1, 77, 1, 0),
     (4, 130, 4096, 2, 1, 256, 16, 0),
+    # batch-row pairs of fp16 tables: one pair (2 rows), and 3 rows in a 4-row workgroup (the
+    # second pair's high half belongs to no row)
+    (4, 200, 1000, 2, 1, 77, 2, 0),
+    (4, 150, 777, 2, 1, 40, 3, 0),
     (8, 200, 4096, 3, 1, 96, 1, 0),
     (8, 64, 257, 1, 2, 31, 4, 0),
     (4, 130, 4096, 2, 2, 0, 3, 8),
