@@ -28,8 +28,9 @@ gate+up projection is the dominant kernel of the roofline object); the HBM read 
 (fluxbin_probe_lds_lookup) that bounds the batch path; the LLaMA-2-7B q_proj
 call on 256 resident sets; the LLaMA-2-7B 32-layer g = 8 stream, each GEMV
 against the banked lookup rate (fluxbin_probe_lds_lookup_banked); the
-4096->11008 / 11008->4096 batch sweep; the hand-written dense fp16 GEMV on the
-70B shapes; and the fp64 oracle on the host cores (cpu_baseline).
+4096->11008 / 11008->4096 batch sweep (fp32 tables, and fp16 tables from 4
+batch rows); the hand-written dense fp16 GEMV on the 70B shapes; and the fp64
+oracle on the host cores (cpu_baseline).
 
 Prints one JSON line.  --out FILE also writes the detail as JSON.
 """
@@ -75,12 +76,14 @@ def measured_traffic(name: str):
 class Model:
     """Handles of a streamed model: n_layers x the workload's shapes, every (layer, shape) its own weights."""
 
-    def __init__(self, wid: int, n_layers: int, torch, F, I, A, gen, max_batch: int = 1, shapes=None):
+    def __init__(self, wid: int, n_layers: int, torch, F, I, A, gen, max_batch: int = 1, shapes=None,
+                 table_precision: int = 0):
         self.wl = I.WORKLOADS[wid]
         self.wid = wid
         self.n_layers = n_layers
         self.shape_ids = list(range(len(self.wl.shapes))) if shapes is None else list(shapes)
         self.max_batch = max_batch
+        self.table_precision = table_precision
         self.layer0 = [I.workload_layer(wid, si, 0) for si in self.shape_ids]
         self.x0 = [I.workload_x(wid, lay, max_batch, si, 0) for si, lay in zip(self.shape_ids, self.layer0)]
         self.bytes = [A.weight_bytes(l.n, l.k, l.s, l.kb, l.ks) for l in self.layer0]
@@ -92,7 +95,7 @@ class Model:
             row = []
             for si, lay in enumerate(self.layer0):
                 if li == 0:
-                    dl = F.DeviceLayer(lay, max_batch=max_batch)
+                    dl = F.DeviceLayer(lay, max_batch=max_batch, table_precision=table_precision)
                     self.keep.append(dl)
                     row.append(dl.handle)
                 else:
@@ -120,6 +123,7 @@ class Model:
         d.g, d.kb, d.ks = lay.g, lay.kb, lay.ks
         d.n, d.k, d.s, d.max_batch = lay.n, lay.k, lay.s, self.max_batch
         d.layout = F.LAYOUT_TILED
+        d.table_precision = self.table_precision
         d.bits_global, d.r_global, d.c_global = (t["bits_g"].data_ptr(), t["r_g"].data_ptr(), t["c_g"].data_ptr())
         if lay.ks:
             d.bits_sal, d.r_sal, d.c_sal, d.sal_idx = (t["bits_s"].data_ptr(), t["r_s"].data_ptr(),
@@ -458,8 +462,22 @@ def main() -> int:
                                             "plan": F.fluxbin_get_plan(mb.handles[0][0])}
                 mb.close(F)
                 del mb, g
+        # the same calls with fp16 tables (quantised entries, two batch rows per table dword)
+        sweep16 = {}
+        for si, sh in enumerate(I.WORKLOADS[4].shapes):
+            for b in (4, 8, 16):
+                mb = Model(4, 48, torch, F, I, A, gen, max_batch=b, shapes=[si], table_precision=F.TABLE_F16)
+                g = mb.capture(torch, F, stream, 48)
+                with torch.cuda.stream(stream):
+                    g.replay()
+                s_ = timed(torch, stream, lambda: [g.replay() for _ in range(4)])
+                us = s_ * 1e6 / (4 * 48)
+                sweep16[f"{sh.name}_b{b}"] = {"us": round(us, 3),
+                                              "vs_fp32_tables": round(sweep[f"{sh.name}_b{b}"]["us"] / us, 3)}
+                mb.close(F)
+                del mb, g
         extra["batch_sweep_4096_11008"] = {"lookup_rate_per_s": {f"g{g}_b{nb}": r for (g, nb), r in rates.items()},
-                                          "calls": sweep, "sets": 48}
+                                          "calls": sweep, "sets": 48, "fp16_tables": sweep16}
 
     cpu = None
     if not args.no_cpu:
